@@ -1,0 +1,327 @@
+"""Pins for the oracle's GEMM definitions (CPU only).
+
+The oracle is checked against things other than itself: exact rational brute
+force written independently here, closed-form identities that hold exactly in
+any summation order, hand-worked rounding cases under tests/golden/, and a
+pure-Python IEEE-single emulation of the order-preserving recurrence.
+"""
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import read_golden
+import oracle
+import synthetic
+
+
+# ---------------------------------------------------------------------------
+# independent helpers (exact rationals, pure-Python single precision)
+# ---------------------------------------------------------------------------
+
+def bf16_exact(bits: int) -> Fraction:
+    """Exact value of a BF16 bit pattern from its fields (finite only)."""
+    s, e, m = bits >> 15, (bits >> 7) & 0xFF, bits & 0x7F
+    assert e != 0xFF
+    v = Fraction(m, 128) * Fraction(2) ** -126 if e == 0 else Fraction(128 + m, 128) * Fraction(2) ** (e - 127)
+    return -v if s else v
+
+
+def f32r(x: float) -> float:
+    """Round a Python float (binary64) to binary32, nearest-even.
+
+    Correct for one +, -, * of binary32 operands computed in binary64, since
+    53 >= 2*24 + 2 (double rounding is then innocuous).
+    """
+    return struct.unpack("<f", struct.pack("<f", x))[0]
+
+
+def f32_bits(x: float) -> int:
+    return struct.unpack("<I", struct.pack("<f", x))[0]
+
+
+def torch_bf16_bits(x_f32: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.asarray(x_f32, np.float32).copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def rand_bf16(shape, seed, std=1.0):
+    return synthetic.normal_bf16(shape, std, seed, 0)
+
+
+# ---------------------------------------------------------------------------
+# dense GEMM
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("m,n,k", [(3, 5, 7), (1, 1, 1), (4, 2, 19), (2, 6, 33)])
+def test_dense_brute_force_exact_rationals(m, n, k):
+    a = rand_bf16((m, k), 10 + k)
+    b = synthetic.normal_bf16((n, k), 0.5, 20 + k, 1)
+    got = oracle.gemm_bf16_ref(a, b)
+    assert got.shape == (m, n)
+    for i in range(m):
+        for j in range(n):
+            exact = sum(bf16_exact(int(a[i, kk])) * bf16_exact(int(b[j, kk])) for kk in range(k))
+            absum = sum(abs(bf16_exact(int(a[i, kk])) * bf16_exact(int(b[j, kk]))) for kk in range(k))
+            assert abs(Fraction(got[i, j]) - exact) <= Fraction(k) * Fraction(2) ** -52 * absum
+
+
+def test_dense_exactly_summable_is_exact():
+    a = synthetic.grid_bf16((9, 40), -8, 8, -5, 1, 0)
+    b = synthetic.grid_bf16((11, 40), -8, 8, -5, 1, 1)
+    got = oracle.gemm_bf16_ref(a, b)
+    for i in range(9):
+        for j in range(11):
+            exact = sum(bf16_exact(int(a[i, kk])) * bf16_exact(int(b[j, kk])) for kk in range(40))
+            assert Fraction(got[i, j]) == exact
+
+
+def test_dense_identity_and_permutation():
+    k = 24
+    a = rand_bf16((5, k), 3)
+    eye = torch_bf16_bits(np.eye(k, dtype=np.float32))
+    assert np.array_equal(oracle.gemm_bf16_ref(a, eye), oracle.bf16_to_f64(a))
+    perm = np.random.default_rng(5).permutation(k)
+    p = np.zeros((k, k), np.float32)
+    p[np.arange(k), perm] = 1.0          # row j of B selects column perm[j] of A
+    got = oracle.gemm_bf16_ref(a, torch_bf16_bits(p))
+    assert np.array_equal(got, oracle.bf16_to_f64(a)[:, perm])
+    # power-of-two diagonal scales columns exactly
+    d = np.diag(np.exp2(np.arange(k) % 5 - 2).astype(np.float32))
+    got = oracle.gemm_bf16_ref(a, torch_bf16_bits(d))
+    assert np.array_equal(got, oracle.bf16_to_f64(a) * np.exp2(np.arange(k) % 5 - 2)[None, :])
+
+
+def test_dense_transpose_symmetry_and_zero_k_padding():
+    a = synthetic.grid_bf16((7, 29), -6, 6, -4, 2, 0)
+    b = synthetic.grid_bf16((13, 29), -6, 6, -4, 2, 1)
+    c = oracle.gemm_bf16_ref(a, b)
+    assert np.array_equal(c, oracle.gemm_bf16_ref(b, a).T)
+    pad = np.zeros((7, 35), np.uint16)
+    pad[:, :29] = a
+    padb = np.zeros((13, 35), np.uint16)
+    padb[:, :29] = b
+    assert np.array_equal(c, oracle.gemm_bf16_ref(pad, padb))
+
+
+def test_dense_empty_k_is_zero():
+    a = np.zeros((3, 0), np.uint16)
+    b = np.zeros((4, 0), np.uint16)
+    assert np.array_equal(oracle.gemm_bf16_ref(a, b), np.zeros((3, 4)))
+
+
+def test_tolerance_closed_form():
+    ref = np.array([0.0, 1.0, -2.0])
+    t = oracle.tolerance(ref, 400, 1.0, 0.02)
+    assert np.allclose(t, 8e-3 * np.abs(ref) + 4e-3 * 20.0 * 0.02)
+
+
+# ---------------------------------------------------------------------------
+# order-preserving mode
+# ---------------------------------------------------------------------------
+
+def _parse_row(s):
+    return np.array([float(t) for t in s.split()], dtype=np.float32)
+
+
+def test_ordered_worked_cases():
+    for ln in read_golden("ordered_worked.txt"):
+        fields = [f.strip() for f in ln.split(";")]
+        name, arow, brow, want = fields[0], _parse_row(fields[1]), _parse_row(fields[2]), int(fields[3], 16)
+        a = torch_bf16_bits(arow[None, :])
+        b = torch_bf16_bits(brow[None, :])
+        assert np.array_equal(oracle.bf16_to_f32(a)[0], arow), name     # inputs exact in BF16
+        got = oracle.gemm_ordered_f32(a, b)
+        assert f32_bits(float(got[0, 0])) == want, name
+        if name == "cancel":
+            # reversed order differs, so the test pins the direction
+            rev = oracle.gemm_ordered_f32(a[:, ::-1].copy(), b[:, ::-1].copy())
+            assert f32_bits(float(rev[0, 0])) == 0x3F800000
+
+
+def _ordered_pure_python(a_bits, b_bits):
+    m, k = a_bits.shape
+    n = b_bits.shape[0]
+    a = [[float(bf16_exact(int(v))) for v in row] for row in a_bits]
+    b = [[float(bf16_exact(int(v))) for v in row] for row in b_bits]
+    out = np.zeros((m, n), np.float32)
+    for i in range(m):
+        for j in range(n):
+            acc = 0.0
+            for kk in range(k):
+                acc = f32r(acc + f32r(a[i][kk] * b[j][kk]))
+            out[i, j] = acc
+    return out
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_ordered_matches_pure_python_ieee_single(seed):
+    a = rand_bf16((4, 37), 100 + seed, 3.0)
+    b = synthetic.normal_bf16((5, 37), 7.0, 200 + seed, 1)
+    got = oracle.gemm_ordered_f32(a, b)
+    want = _ordered_pure_python(a, b)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    assert np.array_equal(oracle.gemm_ordered(a, b), torch_bf16_bits(want))
+
+
+def test_ordered_empty_k_is_positive_zero():
+    got = oracle.gemm_ordered_f32(np.zeros((2, 0), np.uint16), np.zeros((3, 0), np.uint16))
+    assert np.array_equal(got.view(np.uint32), np.zeros((2, 3), np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# fused LoRA fold
+# ---------------------------------------------------------------------------
+
+def test_scaled_acc_worked_cases():
+    for ln in read_golden("scaled_acc_worked.txt"):
+        f = [t.strip() for t in ln.split(";")]
+        name = f[0]
+        out = np.array([[int(f[1], 16)]], np.uint16)
+        x = torch_bf16_bits(_parse_row(f[2])[None, :])
+        b = torch_bf16_bits(_parse_row(f[3])[None, :])
+        scale = struct.unpack("<f", struct.pack("<I", int(f[4], 16)))[0]
+        want = int(f[5], 16)
+        got = int(oracle.gemm_scaled_acc_exact(out, x, b, scale)[0, 0])
+        assert got == want, (name, hex(got))
+
+
+def _unfused_pure_python(out_bits, delta_f32, scale):
+    """BF16 scratch of delta (torch RNE), then a scaled add in IEEE single."""
+    scratch = torch_bf16_bits(delta_f32)
+    res = np.zeros(out_bits.shape, np.float32)
+    for idx in np.ndindex(out_bits.shape):
+        d = float(bf16_exact(int(scratch[idx])))
+        o = float(bf16_exact(int(out_bits[idx])))
+        res[idx] = f32r(o + f32r(f32r(scale) * d))
+    return torch_bf16_bits(res)
+
+
+@pytest.mark.parametrize("scale", [2.0, 0.7, -1.3])
+def test_scaled_acc_equals_unfused_pair(scale):
+    out = rand_bf16((6, 9), 40)
+    x = synthetic.grid_bf16((6, 16), -8, 8, -5, 41, 0)
+    b = synthetic.grid_bf16((9, 16), -8, 8, -5, 41, 1)
+    delta = oracle.gemm_bf16_ref(x, b).astype(np.float32)      # exact for grid inputs
+    got = oracle.gemm_scaled_acc_exact(out, x, b, scale)
+    assert np.array_equal(got, _unfused_pure_python(out, delta, scale))
+
+
+def test_scaled_acc_scale_zero_keeps_values_and_unit_rows_add():
+    out = rand_bf16((5, 8), 50)
+    x = rand_bf16((5, 8), 51)
+    b = rand_bf16((8, 8), 52)
+    kept = oracle.gemm_scaled_acc_exact(out, x, b, 0.0)
+    assert np.array_equal(oracle.bf16_to_f32(kept), oracle.bf16_to_f32(out))
+    # X = identity rows, scale 1: out + B^T as a BF16 add (exact sum rounded once via FP32)
+    eye = torch_bf16_bits(np.eye(8, dtype=np.float32)[:5])
+    got = oracle.gemm_scaled_acc_exact(out, eye, b, 1.0)
+    for i in range(5):
+        for j in range(8):
+            s = bf16_exact(int(out[i, j])) + bf16_exact(int(b[j, i]))
+            want = torch_bf16_bits(np.array([f32r(float(s))], np.float32))[0]
+            assert got[i, j] == want
+
+
+def test_scaled_acc_candidates_bracket_exact_result():
+    out = rand_bf16((8, 32), 60)
+    x = synthetic.normal_bf16((8, 64), 0.1, 61, 0)
+    b = synthetic.normal_bf16((32, 64), 0.1, 61, 1)
+    lo, hi, n = oracle.scaled_acc_candidates(out, x, b, 2.0)
+    exact = oracle.scaled_acc_epilogue(out, oracle.f32_to_bf16(oracle.gemm_bf16_ref(x, b).astype(np.float32)), 2.0)
+    assert oracle.bf16_in_closed_range(exact, lo, hi).all()
+    # near-zero deltas may admit several BF16 values; most admit exactly one
+    assert (n >= 1).all() and (n == 1).mean() > 0.8
+
+
+# ---------------------------------------------------------------------------
+# split-K
+# ---------------------------------------------------------------------------
+
+def test_splitk_chunk_table():
+    assert oracle.splitk_chunk(2048, 1) == 2048
+    assert oracle.splitk_chunk(2048, 8) == 256
+    assert oracle.splitk_chunk(11008, 2) == 5504
+    assert oracle.splitk_chunk(11008, 4) == 2752
+    assert oracle.splitk_chunk(11008, 8) == 1408
+    assert oracle.splitk_chunk(100, 8) == 64
+    assert oracle.splitk_chunk(0, 3) == 0
+
+
+@pytest.mark.parametrize("k,ks", [(200, 3), (130, 8), (64, 2), (1, 4)])
+def test_splitk_planes_brute_force_and_distributivity(k, ks):
+    a = synthetic.grid_bf16((3, k), -8, 8, -5, 70, 0)
+    b = synthetic.grid_bf16((4, k), -8, 8, -5, 70, 1)
+    planes = oracle.gemm_splitk_planes_ref(a, b, ks)
+    kc = oracle.splitk_chunk(k, ks)
+    for s in range(ks):
+        lo, hi = min(k, s * kc), min(k, (s + 1) * kc)
+        for i in range(3):
+            for j in range(4):
+                exact = sum((bf16_exact(int(a[i, kk])) * bf16_exact(int(b[j, kk])) for kk in range(lo, hi)), Fraction(0))
+                assert Fraction(planes[s, i, j]) == exact
+    assert np.array_equal(planes.sum(axis=0), oracle.gemm_bf16_ref(a, b))
+
+
+def test_splitk_reduce_is_ascending_fp32():
+    planes = np.array([[[2.0 ** 24]], [[1.0]], [[-(2.0 ** 24)]]], np.float32)
+    assert int(oracle.splitk_reduce(planes)[0, 0]) == 0x0000
+    assert int(oracle.splitk_reduce(planes[::-1])[0, 0]) == 0x3F80
+    # one plane: the value itself (sign of zero kept)
+    neg0 = np.array([[[-0.0]]], np.float32)
+    assert int(oracle.splitk_reduce(neg0)[0, 0]) == 0x8000
+
+
+# ---------------------------------------------------------------------------
+# block-scaled FP4
+# ---------------------------------------------------------------------------
+
+def _e2m1_table():
+    return {int(r.split()[0]): Fraction(r.split()[1]) for r in read_golden("e2m1_table.txt")}
+
+
+def test_fp4_brute_force_exact():
+    tab = _e2m1_table()
+    m, n, k = 3, 4, 48
+    a = synthetic.fp4_packed(m, k, 80, 0)
+    b = synthetic.fp4_packed(n, k, 80, 1)
+    sfa = synthetic.e4m3_uniform(m, k // 16, 2 ** -4, 2 ** 4, 80, 4)
+    sfb = synthetic.e4m3_uniform(n, k // 16, 2 ** -4, 2 ** 4, 80, 5)
+    sa = torch.from_numpy(sfa).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    sb = torch.from_numpy(sfb).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+    def elem(packed, scales, r, kk):
+        byte = int(packed[r, kk // 2])
+        code = byte & 0xF if kk % 2 == 0 else byte >> 4
+        return tab[code] * Fraction(scales[r, kk // 16])
+
+    got = oracle.gemm_fp4_ref(a, sfa, b, sfb)
+    for i in range(m):
+        for j in range(n):
+            exact = sum(elem(a, sa, i, kk) * elem(b, sb, j, kk) for kk in range(k))
+            assert Fraction(got[i, j]) == exact
+
+
+def test_fp4_unit_scales_reduce_to_dense_on_dequantized_operands():
+    m, n, k = 5, 6, 64
+    a = synthetic.fp4_packed(m, k, 81, 0)
+    b = synthetic.fp4_packed(n, k, 81, 1)
+    one = np.full((m, k // 16), 0x38, np.uint8)
+    oneb = np.full((n, k // 16), 0x38, np.uint8)
+    tab = np.array([float(_e2m1_table()[c]) for c in range(16)], np.float32)
+    ab = torch_bf16_bits(tab[oracle.unpack_e2m1(a)])
+    bb = torch_bf16_bits(tab[oracle.unpack_e2m1(b)])
+    assert np.array_equal(oracle.gemm_fp4_ref(a, one, b, oneb), oracle.gemm_bf16_ref(ab, bb))
+
+
+def test_fp4_power_of_two_scales_exact_in_fp32():
+    """Scales in {1, 2}: every partial sum is a multiple of 1/4 below 2^21."""
+    m, n, k = 4, 4, 8192
+    a = synthetic.fp4_packed(m, k, 82, 0)
+    b = synthetic.fp4_packed(n, k, 82, 1)
+    sfa = synthetic.e4m3_choice(m, k // 16, [0x38, 0x40], 82, 4)
+    sfb = synthetic.e4m3_choice(n, k // 16, [0x38, 0x40], 82, 5)
+    ref = oracle.gemm_fp4_ref(a, sfa, b, sfb)
+    assert np.array_equal(ref, ref.astype(np.float32).astype(np.float64))
+    assert np.array_equal(ref * 4, np.round(ref * 4))
