@@ -1,0 +1,200 @@
+// C ABI entry points: argument validation, device check, kernel dispatch.
+//
+// Validation is plain host code that touches no HIP API, so every error path
+// is reachable without a GPU; the device check runs only once the arguments
+// are known to be good. Nothing is enqueued unless every check passes.
+#include <atomic>
+#include <cstring>
+
+#include "bg_internal.hpp"
+
+namespace {
+
+constexpr uint32_t kMaxDim = 0x7FFFFFFFu;   // kernels index rows and K with int32
+constexpr uint32_t kMaxSplits = 64;
+
+struct Range {
+    uintptr_t lo, hi;   // [lo, hi), empty when lo == hi
+};
+
+Range range_of(const void* p, uint64_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + (uintptr_t)bytes};
+}
+
+bool overlap(Range x, Range y) {
+    if (x.lo == x.hi || y.lo == y.hi) return false;
+    return x.lo < y.hi && y.lo < x.hi;
+}
+
+bool misaligned(const void* p, uint64_t bytes) {
+    return bytes != 0 && (reinterpret_cast<uintptr_t>(p) & 15u) != 0;
+}
+
+bool missing(const void* p, uint64_t bytes) { return bytes != 0 && p == nullptr; }
+
+bool dims_ok(uint32_t M, uint32_t N, uint32_t K) {
+    return M <= kMaxDim && N <= kMaxDim && K <= kMaxDim;
+}
+
+// Per-device cache of "is gfx950": 0 unknown, 1 yes, 2 no.
+std::atomic<int> g_arch_ok[64];
+
+bg_status check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return BG_ERR_DEVICE;
+    if (dev < 64) {
+        const int cached = g_arch_ok[dev].load(std::memory_order_relaxed);
+        if (cached == 1) return BG_OK;
+        if (cached == 2) return BG_ERR_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return BG_ERR_DEVICE;
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? BG_OK : BG_ERR_DEVICE;
+}
+
+bg_status launched(hipError_t e) { return e == hipSuccess ? BG_OK : BG_ERR_LAUNCH; }
+
+// Common checks of a dense BF16 problem A[M,K], B[N,K] -> out[M,N] of
+// `out_elem` bytes per element.
+bg_status check_dense(const void* A, const void* B, const void* out, uint32_t M, uint32_t N,
+                      uint32_t K, uint64_t out_elem) {
+    if (!dims_ok(M, N, K)) return BG_ERR_SHAPE;
+    const uint64_t a_bytes = (uint64_t)M * K * 2, b_bytes = (uint64_t)N * K * 2;
+    const uint64_t o_bytes = (uint64_t)M * N * out_elem;
+    if (M == 0 || N == 0) return BG_OK;
+    if (missing(A, a_bytes) || missing(B, b_bytes) || missing(out, o_bytes)) return BG_ERR_NULL;
+    if (misaligned(A, a_bytes) || misaligned(B, b_bytes) || misaligned(out, o_bytes))
+        return BG_ERR_ALIGN;
+    const Range ro = range_of(out, o_bytes);
+    if (overlap(ro, range_of(A, a_bytes)) || overlap(ro, range_of(B, b_bytes))) return BG_ERR_ALIAS;
+    return BG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bg_status_string(bg_status s) {
+    switch (s) {
+        case BG_OK: return "ok";
+        case BG_ERR_NULL: return "a required pointer is NULL";
+        case BG_ERR_SHAPE: return "invalid dimensions for this operation";
+        case BG_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
+        case BG_ERR_WORKSPACE: return "split-K workspace missing or too small";
+        case BG_ERR_ALIAS: return "an output overlaps an input";
+        case BG_ERR_DEVICE: return "no current HIP device, or it is not gfx950";
+        case BG_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+bg_status gemm_bf16(const uint16_t* A, const uint16_t* B, uint16_t* C, uint32_t M, uint32_t N,
+                    uint32_t K, void* stream) {
+    bg_status s = check_dense(A, B, C, M, N, K, 2);
+    if (s != BG_OK || M == 0 || N == 0) return s;
+    if ((s = check_device()) != BG_OK) return s;
+    bg::DenseProblem p{A, B, C, M, N, K, K, 1, 0.0f};
+    return launched(bg::launch_dense(p, bg::EPI_STORE_BF16, (hipStream_t)stream));
+}
+
+bg_status gemm_bf16_scaled_acc(const uint16_t* X, const uint16_t* B, uint16_t* out, uint32_t M,
+                               uint32_t N, uint32_t K, float scale, void* stream) {
+    bg_status s = check_dense(X, B, out, M, N, K, 2);
+    if (s != BG_OK || M == 0 || N == 0) return s;
+    if ((s = check_device()) != BG_OK) return s;
+    bg::DenseProblem p{X, B, out, M, N, K, K, 1, scale};
+    return launched(bg::launch_dense(p, bg::EPI_SCALED_ACC, (hipStream_t)stream));
+}
+
+size_t gemm_bf16_splitk_workspace_bytes(uint32_t M, uint32_t N, uint32_t k_splits) {
+    return (size_t)k_splits * (size_t)M * (size_t)N * sizeof(float);
+}
+
+bg_status gemm_bf16_splitk(const uint16_t* A, const uint16_t* B, uint16_t* C, float* workspace,
+                           size_t workspace_bytes, uint32_t M, uint32_t N, uint32_t K,
+                           uint32_t k_splits, void* stream) {
+    if (k_splits == 0 || k_splits > kMaxSplits) return BG_ERR_SHAPE;
+    bg_status s = check_dense(A, B, C, M, N, K, 2);
+    if (s != BG_OK || M == 0 || N == 0) return s;
+    // chunk = ceil(K / k_splits) rounded up to a multiple of 64
+    const uint64_t per = ((uint64_t)K + k_splits - 1) / k_splits;
+    const uint32_t chunk = (uint32_t)((per + 63) / 64 * 64);
+    if (k_splits > 1) {
+        const uint64_t need = (uint64_t)k_splits * M * N * 4;
+        if (workspace == nullptr || workspace_bytes < need) return BG_ERR_WORKSPACE;
+        if (misaligned(workspace, need)) return BG_ERR_ALIGN;
+        const Range rw = range_of(workspace, need);
+        if (overlap(rw, range_of(A, (uint64_t)M * K * 2)) ||
+            overlap(rw, range_of(B, (uint64_t)N * K * 2)) ||
+            overlap(rw, range_of(C, (uint64_t)M * N * 2)))
+            return BG_ERR_ALIAS;
+    }
+    if ((s = check_device()) != BG_OK) return s;
+    const hipStream_t st = (hipStream_t)stream;
+    if (k_splits == 1) {
+        bg::DenseProblem p{A, B, C, M, N, K, K, 1, 0.0f};
+        return launched(bg::launch_dense(p, bg::EPI_STORE_BF16, st));
+    }
+    bg::DenseProblem p{A, B, workspace, M, N, K, chunk, k_splits, 0.0f};
+    hipError_t e = bg::launch_dense(p, bg::EPI_STORE_F32, st);
+    if (e != hipSuccess) return BG_ERR_LAUNCH;
+    return launched(bg::launch_splitk_reduce(workspace, C, M, N, k_splits, st));
+}
+
+bg_status gemm_bf16_ordered(const uint16_t* A, const uint16_t* B, uint16_t* C, uint32_t M,
+                            uint32_t N, uint32_t K, void* stream) {
+    bg_status s = check_dense(A, B, C, M, N, K, 2);
+    if (s != BG_OK || M == 0 || N == 0) return s;
+    if ((s = check_device()) != BG_OK) return s;
+    return launched(bg::launch_ordered(A, B, C, false, M, N, K, (hipStream_t)stream));
+}
+
+bg_status gemm_bf16_ordered_f32(const uint16_t* A, const uint16_t* B, float* C32, uint32_t M,
+                                uint32_t N, uint32_t K, void* stream) {
+    bg_status s = check_dense(A, B, C32, M, N, K, 4);
+    if (s != BG_OK || M == 0 || N == 0) return s;
+    if ((s = check_device()) != BG_OK) return s;
+    return launched(bg::launch_ordered(A, B, C32, true, M, N, K, (hipStream_t)stream));
+}
+
+bg_status gemm_fp4_blockscaled(const uint8_t* A, const uint8_t* SFA, const uint8_t* B,
+                               const uint8_t* SFB, uint16_t* C, uint32_t M, uint32_t N, uint32_t K,
+                               void* stream) {
+    if (!dims_ok(M, N, K) || (K % 16) != 0) return BG_ERR_SHAPE;
+    if (M == 0 || N == 0) return BG_OK;
+    const uint64_t a_bytes = (uint64_t)M * (K / 2), sa_bytes = (uint64_t)M * (K / 16);
+    const uint64_t b_bytes = (uint64_t)N * (K / 2), sb_bytes = (uint64_t)N * (K / 16);
+    const uint64_t c_bytes = (uint64_t)M * N * 2;
+    if (missing(A, a_bytes) || missing(SFA, sa_bytes) || missing(B, b_bytes) ||
+        missing(SFB, sb_bytes) || missing(C, c_bytes))
+        return BG_ERR_NULL;
+    if (misaligned(A, a_bytes) || misaligned(SFA, sa_bytes) || misaligned(B, b_bytes) ||
+        misaligned(SFB, sb_bytes) || misaligned(C, c_bytes))
+        return BG_ERR_ALIGN;
+    const Range rc = range_of(C, c_bytes);
+    if (overlap(rc, range_of(A, a_bytes)) || overlap(rc, range_of(SFA, sa_bytes)) ||
+        overlap(rc, range_of(B, b_bytes)) || overlap(rc, range_of(SFB, sb_bytes)))
+        return BG_ERR_ALIAS;
+    bg_status s = check_device();
+    if (s != BG_OK) return s;
+    bg::Fp4Problem p{A, SFA, B, SFB, C, M, N, K};
+    return launched(bg::launch_fp4(p, (hipStream_t)stream));
+}
+
+bg_status bf16_scaled_add(uint16_t* out, const uint16_t* delta, size_t count, float scale,
+                          void* stream) {
+    if (count == 0) return BG_OK;
+    if (count > ((size_t)1 << 62)) return BG_ERR_SHAPE;
+    const uint64_t bytes = (uint64_t)count * 2;
+    if (missing(out, bytes) || missing(delta, bytes)) return BG_ERR_NULL;
+    if (misaligned(out, bytes) || misaligned(delta, bytes)) return BG_ERR_ALIGN;
+    if (overlap(range_of(out, bytes), range_of(delta, bytes))) return BG_ERR_ALIAS;
+    bg_status s = check_device();
+    if (s != BG_OK) return s;
+    return launched(bg::launch_scaled_add(out, delta, count, scale, (hipStream_t)stream));
+}
+
+}  // extern "C"

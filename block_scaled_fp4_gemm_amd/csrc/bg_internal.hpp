@@ -1,0 +1,51 @@
+// Internal host-side declarations shared by the C-ABI layer and the kernel
+// translation units. Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/blockgemm.h"
+
+namespace bg {
+
+// Epilogue applied to the FP32 accumulator tile of the MFMA core.
+enum Epilogue : int {
+    EPI_STORE_BF16 = 0,   // C = bf16(acc)
+    EPI_SCALED_ACC = 1,   // out = bf16(out + scale * bf16(acc)), in place
+    EPI_STORE_F32 = 2,    // plane[blockIdx.z] = acc (split-K partials)
+};
+
+struct DenseProblem {
+    const uint16_t* A;   // [M, K] bf16
+    const uint16_t* B;   // [N, K] bf16
+    void* C;             // [M, N] bf16, or [splits][M][N] f32 planes
+    uint32_t M, N, K;
+    uint32_t k_chunk;    // K elements per split (multiple of 64, or K)
+    uint32_t splits;
+    float scale;
+};
+
+struct Fp4Problem {
+    const uint8_t* A;    // [M, K/2]
+    const uint8_t* SFA;  // [M, K/16]
+    const uint8_t* B;    // [N, K/2]
+    const uint8_t* SFB;  // [N, K/16]
+    uint16_t* C;         // [M, N] bf16
+    uint32_t M, N, K;
+};
+
+// Kernel launchers (defined in the .hip files). They enqueue on `stream` and
+// return hipGetLastError() of the launch. Shapes are already validated and
+// non-empty (M > 0, N > 0).
+hipError_t launch_dense(const DenseProblem& p, Epilogue epi, hipStream_t stream);
+hipError_t launch_fp4(const Fp4Problem& p, hipStream_t stream);
+hipError_t launch_ordered(const uint16_t* A, const uint16_t* B, void* C, bool f32_out,
+                          uint32_t M, uint32_t N, uint32_t K, hipStream_t stream);
+hipError_t launch_splitk_reduce(const float* ws, uint16_t* C, uint32_t M, uint32_t N,
+                                uint32_t splits, hipStream_t stream);
+hipError_t launch_scaled_add(uint16_t* out, const uint16_t* delta, size_t count, float scale,
+                             hipStream_t stream);
+
+}  // namespace bg

@@ -1,0 +1,220 @@
+// Order-preserving GEMM (router logits) on the FP32 vector ALU.
+//
+// gemm_dense.rs page, doc comment of dense_gemm_router: each output is the
+// strict k = 0..K-1 FP32 recurrence of the scalar dense kernel, built without
+// FMA contraction (bit-identical to it), made faster by register blocking and
+// vectorized staging; matrix cores reassociate and are not allowed here.
+//
+// Per output: acc = +0.0f; for k ascending: acc = fl32(acc + fl32(a*b)).
+// This file is compiled with FP contraction off and, in addition, every
+// product and sum goes through __fmul_rn / __fadd_rn, so no multiply-add can
+// be fused. FP32 denormals are kept (the library is built without flushing).
+//
+// Design (CDNA4): a workgroup of 16x16 threads owns a (16*RM) x (16*RN)
+// output tile; each thread keeps an RM x RN block of accumulators. K is
+// walked in steps of KT; each step stages A and B rows as FP32 into LDS,
+// K-major ([k][row]), so a thread reads its RM (or RN) operands at one k with
+// 16-byte LDS loads: A reads are broadcast across the 16 threads of a row
+// group, B reads from 16 threads are contiguous. The per-output k order is
+// untouched by the tiling: tiles are visited in ascending k and, inside a
+// tile, k ascends.
+#include "bg_internal.hpp"
+
+#pragma clang fp contract(off)
+
+namespace bg {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int KT = 32;   // K elements per LDS step
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+    return __builtin_bit_cast(float, h << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);   // v_cvt_pk_bf16_f32, nearest even
+}
+
+// Stage rows [row0, row0+ROWS) x k in [k0, k0+KT) of a [nrows, K] BF16 matrix
+// into lds[k][ROWS] as FP32. Positions with k >= K, or rows >= nrows, get 0.
+// A unit is 8 consecutive k of one row; consecutive threads take consecutive
+// rows, so the eight FP32 writes of a unit land in distinct banks.
+template <int ROWS, int NT>
+__device__ __forceinline__ void stage(float* lds, const uint16_t* src, int row0, int nrows,
+                                      int K, int k0, bool vec, int tid) {
+    constexpr int UNITS = ROWS * (KT / 8);
+    static_assert(UNITS % NT == 0, "tile not divisible");
+#pragma unroll
+    for (int i = 0; i < UNITS / NT; ++i) {
+        const int u = tid + i * NT;
+        const int row = u % ROWS, c = u / ROWS;
+        const int grow = row0 + row, gk = k0 + c * 8;
+        uint32_t h[8];
+        if (vec && grow < nrows && gk + 7 < K) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(src + (int64_t)grow * K + gk);
+            h[0] = w.x & 0xFFFFu; h[1] = w.x >> 16; h[2] = w.y & 0xFFFFu; h[3] = w.y >> 16;
+            h[4] = w.z & 0xFFFFu; h[5] = w.z >> 16; h[6] = w.w & 0xFFFFu; h[7] = w.w >> 16;
+        } else {
+#pragma unroll
+            for (int x = 0; x < 8; ++x)
+                h[x] = (grow < nrows && gk + x < K) ? (uint32_t)src[(int64_t)grow * K + gk + x] : 0u;
+        }
+#pragma unroll
+        for (int x = 0; x < 8; ++x) lds[(c * 8 + x) * ROWS + row] = bf16_bits_to_f32(h[x]);
+    }
+}
+
+template <int RM, int RN, bool F32_OUT>
+__global__ void __launch_bounds__(256)
+gemm_ordered_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* C,
+                    int M, int N, int K, int tiles_n) {
+    constexpr int TM = 16 * RM, TN = 16 * RN;
+    static_assert(RM % 4 == 0 && RN % 4 == 0, "register blocks are built from float4 reads");
+    __shared__ __attribute__((aligned(16))) float sA[KT * TM];
+    __shared__ __attribute__((aligned(16))) float sB[KT * TN];
+
+    const int tid = threadIdx.x;
+    const int tx = tid & 15, ty = tid >> 4;
+    const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+    const int m0 = tm * TM, n0 = tn * TN;
+    const bool vec = (K & 7) == 0;
+
+    float acc[RM][RN];
+#pragma unroll
+    for (int i = 0; i < RM; ++i)
+#pragma unroll
+        for (int j = 0; j < RN; ++j) acc[i][j] = 0.0f;
+
+    // thread rows: ty*4 + 64*a + {0..3};  thread cols: tx*4 + 64*b + {0..3}
+    for (int k0 = 0; k0 < K; k0 += KT) {
+        __syncthreads();
+        stage<TM, 256>(sA, A, m0, M, K, k0, vec, tid);
+        stage<TN, 256>(sB, B, n0, N, K, k0, vec, tid);
+        __syncthreads();
+        const int kn = min(KT, K - k0);
+        for (int kk = 0; kk < kn; ++kk) {
+            float a[RM], b[RN];
+#pragma unroll
+            for (int q = 0; q < RM / 4; ++q) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(&sA[kk * TM + q * 64 + ty * 4]);
+                a[4 * q + 0] = v.x; a[4 * q + 1] = v.y; a[4 * q + 2] = v.z; a[4 * q + 3] = v.w;
+            }
+#pragma unroll
+            for (int q = 0; q < RN / 4; ++q) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(&sB[kk * TN + q * 64 + tx * 4]);
+                b[4 * q + 0] = v.x; b[4 * q + 1] = v.y; b[4 * q + 2] = v.z; b[4 * q + 3] = v.w;
+            }
+#pragma unroll
+            for (int i = 0; i < RM; ++i)
+#pragma unroll
+                for (int j = 0; j < RN; ++j)
+                    acc[i][j] = __fadd_rn(acc[i][j], __fmul_rn(a[i], b[j]));
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < RM; ++i) {
+        const int m = m0 + (i / 4) * 64 + ty * 4 + (i % 4);
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < RN; ++j) {
+            const int n = n0 + (j / 4) * 64 + tx * 4 + (j % 4);
+            if (n >= N) continue;
+            if constexpr (F32_OUT)
+                reinterpret_cast<float*>(C)[(int64_t)m * N + n] = acc[i][j];
+            else
+                reinterpret_cast<uint16_t*>(C)[(int64_t)m * N + n] = f32_to_bf16_rne(acc[i][j]);
+        }
+    }
+}
+
+template <int RM, int RN>
+hipError_t launch_ordered_cfg(const uint16_t* A, const uint16_t* B, void* C, bool f32_out, int M,
+                              int N, int K, hipStream_t stream) {
+    const int tiles_m = (M + 16 * RM - 1) / (16 * RM);
+    const int tiles_n = (N + 16 * RN - 1) / (16 * RN);
+    dim3 grid((unsigned)(tiles_m * tiles_n));
+    if (f32_out)
+        hipLaunchKernelGGL((gemm_ordered_kernel<RM, RN, true>), grid, dim3(256), 0, stream, A, B, C,
+                           M, N, K, tiles_n);
+    else
+        hipLaunchKernelGGL((gemm_ordered_kernel<RM, RN, false>), grid, dim3(256), 0, stream, A, B,
+                           C, M, N, K, tiles_n);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Split-K reduction: C = bf16(((P0 + P1) + P2) + ...), one FP32 add per plane
+// in ascending split order (gemm_dense.rs page, dense_gemm_splitk phase 2:
+// reduce the FP32 workspace and write BF16). Four columns per thread.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(const float* __restrict__ ws, uint16_t* __restrict__ C, int64_t count,
+                     int splits, bool vec) {
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t e0 = q * 4;
+    if (e0 >= count) return;
+    if (vec && e0 + 3 < count) {
+        f32x4 s = *reinterpret_cast<const f32x4*>(ws + e0);
+        for (int p = 1; p < splits; ++p) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(ws + (int64_t)p * count + e0);
+            s.x = __fadd_rn(s.x, v.x);
+            s.y = __fadd_rn(s.y, v.y);
+            s.z = __fadd_rn(s.z, v.z);
+            s.w = __fadd_rn(s.w, v.w);
+        }
+        const uint32_t lo = (uint32_t)f32_to_bf16_rne(s.x) | ((uint32_t)f32_to_bf16_rne(s.y) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16_rne(s.z) | ((uint32_t)f32_to_bf16_rne(s.w) << 16);
+        *reinterpret_cast<uint2*>(C + e0) = make_uint2(lo, hi);
+    } else {
+        for (int64_t e = e0; e < count && e < e0 + 4; ++e) {
+            float s = ws[e];
+            for (int p = 1; p < splits; ++p) s = __fadd_rn(s, ws[(int64_t)p * count + e]);
+            C[e] = f32_to_bf16_rne(s);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Unfused second half of the LoRA fold: out = bf16(out + fl32(scale*delta)).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+scaled_add_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ delta, int64_t count,
+                  float scale) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= count) return;
+    const float o = bf16_bits_to_f32(out[e]);
+    const float d = bf16_bits_to_f32(delta[e]);
+    out[e] = f32_to_bf16_rne(__fadd_rn(o, __fmul_rn(scale, d)));
+}
+
+}  // namespace
+
+hipError_t launch_ordered(const uint16_t* A, const uint16_t* B, void* C, bool f32_out, uint32_t M,
+                          uint32_t N, uint32_t K, hipStream_t stream) {
+    return launch_ordered_cfg<4, 4>(A, B, C, f32_out, (int)M, (int)N, (int)K, stream);
+}
+
+hipError_t launch_splitk_reduce(const float* ws, uint16_t* C, uint32_t M, uint32_t N,
+                                uint32_t splits, hipStream_t stream) {
+    const int64_t count = (int64_t)M * N;
+    const int64_t threads = (count + 3) / 4;
+    dim3 grid((unsigned)((threads + 255) / 256));
+    const bool vec = (count % 4) == 0;   // every plane then starts 16-byte aligned
+    hipLaunchKernelGGL(splitk_reduce_kernel, grid, dim3(256), 0, stream, ws, C, count, (int)splits,
+                       vec);
+    return hipGetLastError();
+}
+
+hipError_t launch_scaled_add(uint16_t* out, const uint16_t* delta, size_t count, float scale,
+                             hipStream_t stream) {
+    dim3 grid((unsigned)((count + 255) / 256));
+    hipLaunchKernelGGL(scaled_add_kernel, grid, dim3(256), 0, stream, out, delta, (int64_t)count,
+                       scale);
+    return hipGetLastError();
+}
+
+}  // namespace bg

@@ -1,0 +1,175 @@
+/*
+ * blockgemm.h - C ABI of the MI355X (gfx950) dense-BF16 / block-scaled-FP4
+ * GEMM library.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Layout: A is [M, K], B is [N, K], C is [M, N], all row-major and densely
+ *    packed, so both operands are K-contiguous and C = A * B^T. This is the
+ *    layout of the gemm_dense.rs page (doc comment of the dense BF16 GEMM:
+ *    A [M, K] activations, B [N, K] weights in HuggingFace layout, C [M, N]).
+ *  - BF16 values travel as their raw 16-bit patterns (uint16_t).
+ *  - Every data pointer is a DEVICE pointer on the current HIP device. The
+ *    caller allocates and owns every buffer (including the split-K workspace);
+ *    the library never allocates, frees or retains device memory and never
+ *    synchronizes. Buffers must stay alive until the enqueued work finishes.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *    All work is enqueued on that stream in order.
+ *  - Every FP32 -> BF16 conversion rounds to nearest, ties to even; NaN stays
+ *    NaN. Accumulation is FP32.
+ *  - Return value: BG_OK, or the first failed check. Arguments are validated
+ *    completely before anything is enqueued, so a failing call enqueues
+ *    nothing. Device-side faults surface at the caller's next synchronization.
+ *  - M == 0 or N == 0 is a valid empty problem (BG_OK, nothing enqueued).
+ *    K == 0 is the empty sum: C = +0 (gemm_bf16_scaled_acc then leaves the
+ *    values of `out` unchanged).
+ *  - Base pointers of non-empty tensors must be 16-byte aligned
+ *    (BG_ERR_ALIGN otherwise). Row pitches need no alignment: shapes whose rows
+ *    are not a multiple of 16 bytes take a slower guarded load path.
+ *  - An output may not overlap any input (BG_ERR_ALIAS).
+ *  - The current device must be gfx950 (BG_ERR_DEVICE). Kernels are compiled
+ *    into the library; there is no runtime compilation.
+ *  - Calls on different streams are thread-safe. A workspace must not be
+ *    shared by calls that may run concurrently.
+ */
+#ifndef BLOCKGEMM_H
+#define BLOCKGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bg_status {
+    BG_OK = 0,
+    BG_ERR_NULL = 1,      /* a required pointer is NULL                         */
+    BG_ERR_SHAPE = 2,     /* dimensions invalid for this entry point            */
+    BG_ERR_ALIGN = 3,     /* a base pointer is not 16-byte aligned              */
+    BG_ERR_WORKSPACE = 4, /* split-K workspace missing or too small             */
+    BG_ERR_ALIAS = 5,     /* an output overlaps an input                        */
+    BG_ERR_DEVICE = 6,    /* no current HIP device, or it is not gfx950         */
+    BG_ERR_LAUNCH = 7     /* the HIP runtime rejected a kernel launch           */
+} bg_status;
+
+/*
+ * gemm_bf16: C[M,N] = bf16( sum_k A[i,k] * B[j,k] ), FP32 accumulation.
+ *
+ * The plain BF16 matmul of the sm121a_matmul.py page (module docstring and
+ * kernel: FP32 accumulator, K tail contributes zeros, cast to BF16 at the
+ * masked store), in the A * B^T layout of the gemm_dense.rs page's dense BF16
+ * GEMM. Summation order inside the FP32 accumulator is unspecified (MFMA).
+ *
+ *  A: [M, K] BF16, read only.   B: [N, K] BF16, read only.
+ *  C: [M, N] BF16, written.     Dimensions: any M, N, K (M*K, N*K, M*N < 2^63).
+ */
+bg_status gemm_bf16(const uint16_t* A, const uint16_t* B, uint16_t* C,
+                    uint32_t M, uint32_t N, uint32_t K, void* stream);
+
+/*
+ * gemm_bf16_scaled_acc: fused LoRA expand+fold, in place on `out`:
+ *   out[i,j] = bf16( f32(out[i,j]) + fl32( scale * f32(bf16(delta[i,j])) ) ),
+ *   delta = X * B^T accumulated in FP32.
+ *
+ * gemm_dense.rs page, doc comment of dense_gemm_tc_scaled_acc: the delta is
+ * rounded to BF16 before the scale is applied, so the result is bit-identical
+ * to writing bf16(X * B^T) to a scratch tensor and then running a BF16 scaled
+ * add over it; fusing removes that scratch round trip. The multiply and the
+ * add are separate FP32 operations (no FMA contraction).
+ *
+ *  X: [M, K] BF16.  B: [N, K] BF16.  out: [M, N] BF16, read and written.
+ *  `out` must not overlap X or B.
+ */
+bg_status gemm_bf16_scaled_acc(const uint16_t* X, const uint16_t* B, uint16_t* out,
+                               uint32_t M, uint32_t N, uint32_t K, float scale,
+                               void* stream);
+
+/*
+ * gemm_bf16_splitk: C = bf16( sum_s P_s ), P_s[i,j] = FP32 partial sum of
+ * A[i,k] * B[j,k] over K chunk s, planes added in ascending s in FP32.
+ *
+ * gemm_dense.rs page, dense_gemm_splitk: phase 1 writes k_splits partial
+ * products into an FP32 workspace of k_splits * M * N * 4 bytes, phase 2
+ * reduces them and writes BF16; both phases go on the same stream. Chunking
+ * (the page leaves it open): chunk length Kc = ceil(K / k_splits) rounded up
+ * to a multiple of 64; split s covers k in [s*Kc, min(K, (s+1)*Kc)); empty
+ * chunks contribute +0. The reduction is deterministic (no atomics).
+ *
+ *  workspace: device FP32 buffer of at least
+ *             gemm_bf16_splitk_workspace_bytes(M, N, k_splits) bytes, laid out
+ *             as planes [k_splits][M][N]; on return (after the stream runs)
+ *             plane s holds P_s. It may be NULL when k_splits == 1, in which
+ *             case the result is computed without it and is bit-identical.
+ *  k_splits:  1 .. 64 (BG_ERR_SHAPE otherwise).
+ */
+bg_status gemm_bf16_splitk(const uint16_t* A, const uint16_t* B, uint16_t* C,
+                           float* workspace, size_t workspace_bytes,
+                           uint32_t M, uint32_t N, uint32_t K, uint32_t k_splits,
+                           void* stream);
+
+/* Bytes of FP32 workspace gemm_bf16_splitk needs: k_splits * M * N * 4. */
+size_t gemm_bf16_splitk_workspace_bytes(uint32_t M, uint32_t N, uint32_t k_splits);
+
+/*
+ * gemm_bf16_ordered: order-preserving GEMM for router logits.
+ *   acc = +0.0f; for k = 0, 1, ..., K-1: acc = fl32(acc + fl32(A[i,k] * B[j,k]));
+ *   C[i,j] = bf16(acc).
+ *
+ * gemm_dense.rs page, doc comment of dense_gemm_router: same math and the
+ * same strict k = 0..K-1 per-output FP32 order as the scalar dense kernel,
+ * built without FMA contraction, so the output is bit-identical to it; matrix
+ * cores reassociate and are not used. Computed with FP32 vector ALU only.
+ *
+ *  A: [M, K] BF16.  B: [N, K] BF16.  C: [M, N] BF16.
+ */
+bg_status gemm_bf16_ordered(const uint16_t* A, const uint16_t* B, uint16_t* C,
+                            uint32_t M, uint32_t N, uint32_t K, void* stream);
+
+/*
+ * gemm_bf16_ordered_f32: as gemm_bf16_ordered but stores the FP32 sums
+ * (C32: [M, N] float) instead of rounding them to BF16. Same kernel, same
+ * order; exists so tests can compare the accumulator bit for bit.
+ */
+bg_status gemm_bf16_ordered_f32(const uint16_t* A, const uint16_t* B, float* C32,
+                                uint32_t M, uint32_t N, uint32_t K, void* stream);
+
+/*
+ * gemm_fp4_blockscaled: C[i,j] = bf16( sum_k a[i,k] * b[j,k] ), FP32 accumulation,
+ *   a[i,k] = e2m1(A nibble [i,k]) * e4m3fn(SFA[i, k/16]),
+ *   b[j,k] = e2m1(B nibble [j,k]) * e4m3fn(SFB[j, k/16]).
+ *
+ * kernelbot NVFP4 GEMM page (submission 123329): the "SCALE FACTORS" loop
+ * (one scale per 16 K elements, plain [rows, K/16] layout) applied to both
+ * operands, followed by a block-scaled dot product with FP32 accumulation.
+ * Each dequantized element is exact in BF16 (at most 6 significant bits) and
+ * is fed to BF16 matrix cores.
+ *
+ *  A:   [M, K/2] bytes, two E2M1 codes per byte, element 2t in the LOW nibble
+ *       of byte t (sign bit 3, exponent bits 2..1, mantissa bit 0).
+ *  SFA: [M, K/16] E4M3FN bytes (bias 7, 0x7F/0xFF = NaN), row-major.
+ *  B:   [N, K/2] bytes; SFB: [N, K/16] bytes; same encodings.
+ *  C:   [M, N] BF16, written.
+ *  K must be a multiple of 16 (BG_ERR_SHAPE otherwise).
+ */
+bg_status gemm_fp4_blockscaled(const uint8_t* A, const uint8_t* SFA,
+                               const uint8_t* B, const uint8_t* SFB, uint16_t* C,
+                               uint32_t M, uint32_t N, uint32_t K, void* stream);
+
+/*
+ * bf16_scaled_add: out[i] = bf16( f32(out[i]) + fl32(scale * f32(delta[i])) )
+ * over `count` BF16 elements. The second half of the unfused LoRA fold that
+ * gemm_bf16_scaled_acc must equal bit for bit (gemm_dense.rs page, doc comment
+ * of dense_gemm_tc_scaled_acc); kept so the identity can be tested on the GPU.
+ */
+bg_status bf16_scaled_add(uint16_t* out, const uint16_t* delta, size_t count,
+                          float scale, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* bg_status_string(bg_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BLOCKGEMM_H */

@@ -1,0 +1,124 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/blockgemm.h declares, and rejects bad arguments before touching the
+device.
+
+Fake device addresses are used only with arguments that fail validation, so no
+kernel is ever launched on them; the single valid-argument call is skipped when
+a GPU is present.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import block_scaled_fp4_gemm_amd as bg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "blockgemm.h")
+
+# fake, 16-byte aligned, far-apart addresses (never dereferenced)
+A, B, C, W, S1, S2 = (0x10000000 * i for i in range(1, 7))
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", src)) - {"if", "sizeof"})
+
+
+def test_header_and_binding_agree():
+    names = declared_functions()
+    assert set(names) == set(bg.EXPORTS)
+
+
+@pytest.mark.parametrize("name", declared_functions())
+def test_library_exports_symbol(name):
+    lib = ctypes.CDLL(bg._LIB_PATH)
+    assert hasattr(lib, name)
+
+
+def test_status_strings():
+    for s in range(8):
+        assert bg.bg_status_string(s)
+    assert bg.bg_status_string(99) == "unknown status"
+
+
+def test_workspace_bytes():
+    assert bg.gemm_bf16_splitk_workspace_bytes(5120, 2048, 8) == 8 * 5120 * 2048 * 4
+    assert bg.gemm_bf16_splitk_workspace_bytes(0, 7, 3) == 0
+
+
+def test_empty_problems_are_ok_without_pointers():
+    L = bg.lib
+    assert L.gemm_bf16(None, None, None, 0, 5, 7, None) == bg.BG_OK
+    assert L.gemm_bf16(None, None, None, 5, 0, 7, None) == bg.BG_OK
+    assert L.gemm_bf16_scaled_acc(None, None, None, 0, 0, 0, 1.0, None) == bg.BG_OK
+    assert L.gemm_bf16_ordered(None, None, None, 0, 3, 3, None) == bg.BG_OK
+    assert L.gemm_fp4_blockscaled(None, None, None, None, None, 0, 4, 32, None) == bg.BG_OK
+    assert L.bf16_scaled_add(None, None, 0, 1.0, None) == bg.BG_OK
+    assert L.gemm_bf16_splitk(None, None, None, None, 0, 0, 4, 64, 4, None) == bg.BG_OK
+
+
+def test_null_pointers():
+    L = bg.lib
+    assert L.gemm_bf16(None, B, C, 4, 4, 4, None) == bg.BG_ERR_NULL
+    assert L.gemm_bf16(A, None, C, 4, 4, 4, None) == bg.BG_ERR_NULL
+    assert L.gemm_bf16(A, B, None, 4, 4, 4, None) == bg.BG_ERR_NULL
+    assert L.gemm_bf16_ordered_f32(A, B, None, 4, 4, 4, None) == bg.BG_ERR_NULL
+    assert L.gemm_fp4_blockscaled(A, None, B, S2, C, 4, 4, 32, None) == bg.BG_ERR_NULL
+    assert L.bf16_scaled_add(None, B, 8, 1.0, None) == bg.BG_ERR_NULL
+
+
+def test_misaligned_pointers():
+    L = bg.lib
+    assert L.gemm_bf16(A + 2, B, C, 4, 4, 8, None) == bg.BG_ERR_ALIGN
+    assert L.gemm_bf16(A, B, C + 8, 4, 4, 8, None) == bg.BG_ERR_ALIGN
+    assert L.gemm_bf16_scaled_acc(A, B + 4, C, 4, 4, 8, 2.0, None) == bg.BG_ERR_ALIGN
+    assert L.gemm_fp4_blockscaled(A, S1 + 1, B, S2, C, 4, 4, 32, None) == bg.BG_ERR_ALIGN
+    assert L.gemm_bf16_splitk(A, B, C, W + 4, 1 << 20, 4, 4, 128, 2, None) == bg.BG_ERR_ALIGN
+
+
+def test_aliasing_outputs():
+    L = bg.lib
+    # C overlaps A
+    assert L.gemm_bf16(A, B, A + 16, 4, 4, 64, None) == bg.BG_ERR_ALIAS
+    # out overlaps B
+    assert L.gemm_bf16_scaled_acc(A, B, B, 4, 4, 64, 2.0, None) == bg.BG_ERR_ALIAS
+    # split-K workspace overlaps C
+    assert L.gemm_bf16_splitk(A, B, C, C, 1 << 20, 4, 4, 128, 2, None) == bg.BG_ERR_ALIAS
+    # FP4 C overlaps a scale tensor
+    assert L.gemm_fp4_blockscaled(A, S1, B, S2, S1, 4, 4, 32, None) == bg.BG_ERR_ALIAS
+    assert L.bf16_scaled_add(A, A + 16, 64, 1.0, None) == bg.BG_ERR_ALIAS
+    # adjacent but disjoint ranges are fine up to the device check
+    if torch.cuda.device_count() == 0:
+        assert L.gemm_bf16(A, A + 4 * 64 * 2, A + 2 * 4 * 64 * 2, 4, 4, 64, None) == bg.BG_ERR_DEVICE
+
+
+def test_shape_rules():
+    L = bg.lib
+    assert L.gemm_fp4_blockscaled(A, S1, B, S2, C, 4, 4, 40, None) == bg.BG_ERR_SHAPE   # K % 16
+    assert L.gemm_bf16_splitk(A, B, C, W, 1 << 30, 4, 4, 128, 0, None) == bg.BG_ERR_SHAPE
+    assert L.gemm_bf16_splitk(A, B, C, W, 1 << 30, 4, 4, 128, 65, None) == bg.BG_ERR_SHAPE
+    assert L.gemm_bf16(A, B, C, 1 << 31, 4, 4, None) == bg.BG_ERR_SHAPE
+
+
+def test_workspace_rules():
+    L = bg.lib
+    need = 2 * 4 * 4 * 4
+    assert L.gemm_bf16_splitk(A, B, C, None, need, 4, 4, 128, 2, None) == bg.BG_ERR_WORKSPACE
+    assert L.gemm_bf16_splitk(A, B, C, W, need - 1, 4, 4, 128, 2, None) == bg.BG_ERR_WORKSPACE
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="valid call would launch on fake pointers")
+def test_valid_arguments_reach_the_device_check():
+    L = bg.lib
+    assert L.gemm_bf16(A, B, C, 4, 4, 8, None) == bg.BG_ERR_DEVICE
+    assert L.gemm_bf16_splitk(A, B, C, None, 0, 4, 4, 8, 1, None) == bg.BG_ERR_DEVICE
+
+
+def test_python_binding_raises_on_status():
+    with pytest.raises(bg.BlockGemmError) as e:
+        bg._check(bg.BG_ERR_SHAPE, "x")
+    assert e.value.status == bg.BG_ERR_SHAPE
