@@ -1,0 +1,344 @@
+"""Benchmark: throughput of the dense-BF16 MLP block at M = 5120 on one MI355X.
+
+A step is the MLP block of a 2B-class decoder at one packed LoRA step (the
+sm121a_matmul.py page's shape list): gate and up projections
+A[5120,2048] x W[11008,2048]^T, then the down projection
+H[5120,11008] x W[2048,11008]^T through split-K (best k_splits of 1/2/4/8,
+chosen during warm-up). Inputs are seeded synthetic BF16 tensors resident in
+HBM before timing starts. `value` = 3 * 2*M*N*K flops per step / step time.
+
+Every other row of the hot path is timed in the same run and reported under
+"rows": attention projections, the fused LoRA fold (HBM roofline), the
+order-preserving router GEMM (FP32 VALU roofline), the block-scaled FP4 GEMM
+and the small dense case, each warm and after a 1 GiB cache flush.
+
+Output: one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense BF16 MFMA, published
+FP4_PEAK_TFLOPS = 10100.0     # MI355X dense FP4 MFMA, published
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, published
+# FP32 vector ALU without FMA and without packed-FP32 ops: 256 CUs x 4 SIMDs x
+# 16 lanes x 2.4 GHz = 39.3 T FP32 operations/s; a multiply plus an add per
+# multiply-accumulate makes this 39.3 TFLOP/s of GEMM flops.
+VALU_NOFMA_PEAK_TFLOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+M, HID, INTER = 5120, 2048, 11008
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--splitk", default="auto", help="auto or a fixed k_splits for the down projection")
+    p.add_argument("--no-rows", action="store_true", help="skip the per-row table")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--calib-copy", action="store_true",
+                   help="only run a plain 1 GiB device copy (counter calibration) and exit")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_scaled_fp4_gemm_amd as bg
+    import synthetic
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    if args.calib_copy:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 3 x 1 GiB device-to-device")
+        return
+
+    def up16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def u8(b):
+        return torch.from_numpy(np.ascontiguousarray(b)).to(dev)
+
+    t_gen = time.time()
+    x_np, wg_np = synthetic.mlp_gate_up()
+    wu_np = synthetic.normal_bf16((INTER, HID), 0.02, 2, synthetic.TID_B2 + 10)
+    h_np, wd_np = synthetic.mlp_down()
+    X, Wg, Wu, H, Wd = up16(x_np), up16(wg_np), up16(wu_np), up16(h_np), up16(wd_np)
+    G = torch.empty((M, INTER), dtype=torch.bfloat16, device=dev)
+    U = torch.empty((M, INTER), dtype=torch.bfloat16, device=dev)
+    D = torch.empty((M, HID), dtype=torch.bfloat16, device=dev)
+    WS = torch.empty((8, M, HID), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs generated and uploaded in {time.time() - t_gen:.1f}s")
+
+    stream = torch.cuda.current_stream()
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    def down(ks):
+        bg.gemm_bf16_splitk(H, Wd, ks, workspace=WS, out=D)
+
+    # choose the down-projection split during warm-up
+    if args.splitk == "auto":
+        best = None
+        for ks in (1, 2, 4, 8):
+            for _ in range(3):
+                down(ks)
+            s = ev()
+            for _ in range(10):
+                down(ks)
+            e = ev()
+            torch.cuda.synchronize()
+            t = s.elapsed_time(e) / 10
+            log(f"down k_splits={ks}: {t * 1e3:.1f} us")
+            if best is None or t < best[1]:
+                best = (ks, t)
+        ks_down = best[0]
+    else:
+        ks_down = int(args.splitk)
+
+    def step(rec=None):
+        e0 = ev() if rec is not None else None
+        bg.gemm_bf16(X, Wg, out=G)
+        e1 = ev() if rec is not None else None
+        bg.gemm_bf16(X, Wu, out=U)
+        e2 = ev() if rec is not None else None
+        down(ks_down)
+        if rec is not None:
+            rec.append((e0, e1, e2, ev()))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    rec = []
+    start = ev()
+    for _ in range(args.steps):
+        step(rec)
+    end = ev()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    flops_gemm = 2.0 * M * INTER * HID
+    flops_step = 3 * flops_gemm
+    value = flops_step / (ms_step * 1e-3) / 1e12
+
+    gate_up_ms = [r[0].elapsed_time(r[1]) for r in rec] + [r[1].elapsed_time(r[2]) for r in rec]
+    down_ms = [r[2].elapsed_time(r[3]) for r in rec]
+    gu_avg = float(np.mean(gate_up_ms))
+    achieved = flops_gemm / (gu_avg * 1e-3) / 1e12
+    log(f"step {ms_step * 1e3:.1f} us: gate/up {gu_avg * 1e3:.1f} us avg, down {np.mean(down_ms) * 1e3:.1f} us avg")
+
+    roofline = {
+        "bound": "mfma",
+        "kernel": "gemm_mfma_kernel (gemm_bf16, MLP gate/up 5120x11008x2048)",
+        "achieved": round(achieved, 1),
+        "peak": BF16_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+        "traffic": traffic_for_current_kernel(),
+    }
+
+    result = {
+        "metric": "TFLOP/s and % of bf16 MFMA peak at M=5120 MLP gate/up/down shapes",
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "MLP block at M=5120: gate and up 5120x11008x2048, down 5120x2048x11008 split-K",
+            "m": M, "hidden": HID, "intermediate": INTER, "down_k_splits": ks_down,
+            "parallelism": "none (1 GPU)",
+        },
+        "pct_of_bf16_peak": round(100.0 * value / BF16_PEAK_TFLOPS, 2),
+        "gate_up_us": round(gu_avg * 1e3, 2),
+        "down_us": round(float(np.mean(down_ms)) * 1e3, 2),
+        "roofline": roofline,
+    }
+
+    if not args.no_rows:
+        result["rows"] = measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream)
+
+    del X, Wg, Wu, H, Wd, G, U, D, WS
+    torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(x_np, wg_np, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+def traffic_for_current_kernel():
+    """HBM bytes per gate/up launch from the committed counter summary, or None
+    if the GEMM kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_gate_up.json")
+    src = os.path.join(ROOT, "block_scaled_fp4_gemm_amd", "csrc", "gemm_mfma.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if rec.get("kernel_source_sha256") != sha:
+            return None
+        return rec.get("traffic_bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream):
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def timed(fn, reps=20):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        warm, cold = [], []
+        for mode, out in (("warm", warm), ("cold", cold)):
+            for _ in range(reps):
+                if mode == "cold":
+                    flush.zero_()
+                s = torch.cuda.Event(enable_timing=True)
+                e = torch.cuda.Event(enable_timing=True)
+                s.record(stream)
+                fn()
+                e.record(stream)
+                torch.cuda.synchronize()
+                out.append(s.elapsed_time(e) * 1e3)
+        return float(np.median(warm)), float(np.median(cold))
+
+    rows = {}
+
+    def dense_row(name, m, n, k, a, b):
+        A, B = up16(a), up16(b)
+        C = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        w, c = timed(lambda: bg.gemm_bf16(A, B, out=C))
+        fl = 2.0 * m * n * k
+        rows[name] = {"shape": [m, n, k], "us_warm": round(w, 2), "us_cold": round(c, 2),
+                      "tflops_warm": round(fl / w / 1e6, 1), "tflops_cold": round(fl / c / 1e6, 1),
+                      "frac_bf16_peak_warm": round(fl / w / 1e6 / BF16_PEAK_TFLOPS, 4)}
+        log(name, rows[name])
+
+    a, b = synthetic.dense_small()
+    dense_row("dense_128x256x512", 128, 256, 512, a, b)
+    a, b = synthetic.attn_proj(n=2048)
+    dense_row("attn_qo_5120x2048x2048", 5120, 2048, 2048, a, b)
+    a, b = synthetic.attn_proj(n=512)
+    dense_row("attn_kv_5120x512x2048", 5120, 512, 2048, a, b)
+    a, b = synthetic.mlp_gate_up()
+    dense_row("mlp_gate_up_5120x11008x2048", 5120, 11008, 2048, a, b)
+
+    h, wd = synthetic.mlp_down()
+    H, WD = up16(h), up16(wd)
+    D = torch.empty((5120, 2048), dtype=torch.bfloat16, device=dev)
+    WS = torch.empty((8, 5120, 2048), dtype=torch.float32, device=dev)
+    fl = 2.0 * 5120 * 2048 * 11008
+    for ks in (1, 2, 4, 8):
+        w, c = timed(lambda: bg.gemm_bf16_splitk(H, WD, ks, workspace=WS, out=D))
+        rows[f"mlp_down_5120x2048x11008_k{ks}"] = {
+            "us_warm": round(w, 2), "us_cold": round(c, 2), "tflops_warm": round(fl / w / 1e6, 1),
+            "tflops_cold": round(fl / c / 1e6, 1), "frac_bf16_peak_warm": round(fl / w / 1e6 / BF16_PEAK_TFLOPS, 4),
+            "workspace_bytes": ks * 5120 * 2048 * 4 if ks > 1 else 0}
+        log(f"down k{ks}", rows[f"mlp_down_5120x2048x11008_k{ks}"])
+    del H, WD, D, WS
+
+    out, x, bl, scale = synthetic.lora_fold()
+    O, X, BL = up16(out), up16(x), up16(bl)
+    w, c = timed(lambda: bg.gemm_bf16_scaled_acc(X, BL, O, scale))
+    byts = 2 * 2048 * 17408 * 2 + (2048 + 17408) * 64 * 2
+    rows["lora_fold_2048x17408x64"] = {"us_warm": round(w, 2), "us_cold": round(c, 2),
+                                       "gbs_warm": round(byts / w / 1e3, 1), "gbs_cold": round(byts / c / 1e3, 1),
+                                       "frac_hbm_cold": round(byts / c / 1e3 / HBM_PEAK_GBS, 4),
+                                       "algorithmic_bytes": byts}
+    log("lora", rows["lora_fold_2048x17408x64"])
+    del O, X, BL
+
+    for m in (4510, 2255):
+        x, wr = synthetic.router(m=m)
+        X, W = up16(x), up16(wr)
+        C = torch.empty((m, 256), dtype=torch.bfloat16, device=dev)
+        w, c = timed(lambda: bg.gemm_bf16_ordered(X, W, out=C))
+        fl = 2.0 * m * 256 * 2048
+        rows[f"router_ordered_{m}x256x2048"] = {
+            "us_warm": round(w, 2), "us_cold": round(c, 2), "tflops_warm": round(fl / w / 1e6, 2),
+            "frac_valu_nofma_peak": round(fl / w / 1e6 / VALU_NOFMA_PEAK_TFLOPS, 4)}
+        log(f"router {m}", rows[f"router_ordered_{m}x256x2048"])
+
+    a4, sfa, b4, sfb = synthetic.fp4_gemm()
+    A4, SA, B4, SB = u8(a4), u8(sfa), u8(b4), u8(sfb)
+    C = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
+    w, c = timed(lambda: bg.gemm_fp4_blockscaled(A4, SA, B4, SB, out=C))
+    fl = 2.0 * 4096 * 4096 * 8192
+    rows["fp4_4096x4096x8192"] = {"us_warm": round(w, 2), "us_cold": round(c, 2),
+                                  "tflops_warm": round(fl / w / 1e6, 1),
+                                  "frac_bf16_peak_warm": round(fl / w / 1e6 / BF16_PEAK_TFLOPS, 4),
+                                  "frac_fp4_peak_warm": round(fl / w / 1e6 / FP4_PEAK_TFLOPS, 4)}
+    log("fp4", rows["fp4_4096x4096x8192"])
+    del flush
+    return rows
+
+
+def cpu_baseline(x_np, w_np, seconds):
+    """The oracle's FP64 GEMM (decode + numpy matmul) on the host, over row
+    blocks of the gate projection until `seconds` of wall time are used."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+
+    k = x_np.shape[1]
+    n = w_np.shape[0]
+    rows_done = 0
+    t0 = time.time()
+    blk = 128
+    while time.time() - t0 < seconds and rows_done < x_np.shape[0]:
+        oracle.gemm_bf16_ref(x_np[rows_done:rows_done + blk], w_np)
+        rows_done += blk
+    dt = time.time() - t0
+    fl = 2.0 * rows_done * n * k
+    threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    return {"value": round(fl / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"gemm_bf16_ref (FP64) on the first {rows_done} rows of the gate projection "
+                      f"{x_np.shape[0]}x{n}x{k} ({dt:.1f} s wall)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -26,6 +26,8 @@
 // dense_gemm_splitk's FP32 partial planes); kernelbot NVFP4 GEMM page
 // ("SCALE FACTORS": one E4M3 scale per 16 K elements multiplied into each
 // E2M1 element, then an FP32-accumulated dot product).
+#include <cstdlib>
+
 #include "bg_internal.hpp"
 
 #pragma clang fp contract(off)
@@ -60,11 +62,17 @@ struct KParams {
     float scale;
 };
 
-// Swizzled 16-byte chunk slot of logical chunk c in tile row `row`.
-// Any 8 consecutive rows, and the 8 even (or odd) rows of any 16 consecutive
-// rows, map one logical chunk to 8 distinct slots.
+// Swizzled 16-byte chunk slot of logical chunk c in a tile row of CPR chunks
+// (CPR = BK/8). The XOR keeps the eight (CPR = 8) or four (CPR = 4) chunks of a
+// row in distinct slots, and gives one logical chunk distinct banks across the
+// 8 consecutive rows (or the 16 rows, for 256-byte bank windows) that the
+// lanes of one 16-byte LDS read touch. It is an involution in c.
+template <int CPR>
 __device__ __forceinline__ int chunk_slot(int row, int c) {
-    return c ^ ((row ^ (row >> 3)) & 7);
+    if constexpr (CPR == 8)
+        return c ^ ((row ^ (row >> 3)) & 7);
+    else
+        return c ^ (((row >> 1) ^ (row >> 3)) & 3);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -108,15 +116,16 @@ __device__ __forceinline__ void tile_of_block(int tiles_m, int tiles_n, int& tm,
 // are never stored); K positions at or beyond k_end are zero.
 // ---------------------------------------------------------------------------
 
-template <int ROWS, int NT, int SRC>
+template <int ROWS, int NT, int SRC, int BKS = BK>
 struct Stager;
 
 // BF16 rows whose pitch is a multiple of 16 bytes (K % 8 == 0): one 16-byte
 // chunk per load, eight threads per 128-byte row segment.
-template <int ROWS, int NT>
-struct Stager<ROWS, NT, SRC_BF16_VEC> {
-    static constexpr int PER = ROWS * (BK / 8) / NT;
-    static_assert(PER * NT == ROWS * (BK / 8), "tile not divisible among threads");
+template <int ROWS, int NT, int BKS>
+struct Stager<ROWS, NT, SRC_BF16_VEC, BKS> {
+    static constexpr int CPR = BKS / 8;
+    static constexpr int PER = ROWS * CPR / NT;
+    static_assert(PER * NT == ROWS * CPR, "tile not divisible among threads");
     u32x4 r[PER];
 
     __device__ __forceinline__ void load(const uint16_t* base, int row0, int nrows, int K,
@@ -124,7 +133,7 @@ struct Stager<ROWS, NT, SRC_BF16_VEC> {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int q = tid + i * NT;
-            const int row = q >> 3, c = q & 7;
+            const int row = q / CPR, c = q % CPR;
             const int grow = min(row0 + row, nrows - 1);
             const int gk = k0 + c * 8;
             if (gk < k_end)
@@ -137,16 +146,17 @@ struct Stager<ROWS, NT, SRC_BF16_VEC> {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int q = tid + i * NT;
-            const int row = q >> 3, c = q & 7;
-            *reinterpret_cast<u32x4*>(lds + row * BK + chunk_slot(row, c) * 8) = r[i];
+            const int row = q / CPR, c = q % CPR;
+            *reinterpret_cast<u32x4*>(lds + row * BKS + chunk_slot<CPR>(row, c) * 8) = r[i];
         }
     }
 };
 
 // BF16 rows with an unaligned pitch: element-wise guarded loads.
-template <int ROWS, int NT>
-struct Stager<ROWS, NT, SRC_BF16_SCALAR> {
-    static constexpr int PER = ROWS * (BK / 8) / NT;
+template <int ROWS, int NT, int BKS>
+struct Stager<ROWS, NT, SRC_BF16_SCALAR, BKS> {
+    static constexpr int CPR = BKS / 8;
+    static constexpr int PER = ROWS * CPR / NT;
     u32x4 r[PER];
 
     __device__ __forceinline__ void load(const uint16_t* base, int row0, int nrows, int K,
@@ -154,7 +164,7 @@ struct Stager<ROWS, NT, SRC_BF16_SCALAR> {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int q = tid + i * NT;
-            const int row = q >> 3, c = q & 7;
+            const int row = q / CPR, c = q % CPR;
             const int grow = min(row0 + row, nrows - 1);
             const uint16_t* src = base + (int64_t)grow * K;
             uint32_t h[8];
@@ -171,8 +181,8 @@ struct Stager<ROWS, NT, SRC_BF16_SCALAR> {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int q = tid + i * NT;
-            const int row = q >> 3, c = q & 7;
-            *reinterpret_cast<u32x4*>(lds + row * BK + chunk_slot(row, c) * 8) = r[i];
+            const int row = q / CPR, c = q % CPR;
+            *reinterpret_cast<u32x4*>(lds + row * BKS + chunk_slot<CPR>(row, c) * 8) = r[i];
         }
     }
 };
@@ -182,7 +192,7 @@ struct Stager<ROWS, NT, SRC_BF16_SCALAR> {
 // to LDS as two 16-byte chunks. e2m1 * e4m3 has at most 6 significant bits,
 // so the FP32 product and its BF16 conversion are exact.
 template <int ROWS, int NT>
-struct Stager<ROWS, NT, SRC_FP4> {
+struct Stager<ROWS, NT, SRC_FP4, BK> {
     static constexpr int PER = ROWS * (BK / 16) / NT;
     static_assert(PER * NT == ROWS * (BK / 16), "tile not divisible among threads");
     u32x2 w[PER];
@@ -227,104 +237,113 @@ struct Stager<ROWS, NT, SRC_FP4> {
                               deq2(w[i].x, sc, 3)};
             const u32x4 hi = {deq2(w[i].y, sc, 0), deq2(w[i].y, sc, 1), deq2(w[i].y, sc, 2),
                               deq2(w[i].y, sc, 3)};
-            *reinterpret_cast<u32x4*>(lds + row * BK + chunk_slot(row, 2 * g) * 8) = lo;
-            *reinterpret_cast<u32x4*>(lds + row * BK + chunk_slot(row, 2 * g + 1) * 8) = hi;
+            *reinterpret_cast<u32x4*>(lds + row * BK + chunk_slot<8>(row, 2 * g) * 8) = lo;
+            *reinterpret_cast<u32x4*>(lds + row * BK + chunk_slot<8>(row, 2 * g + 1) * 8) = hi;
         }
     }
 };
 
 // ---------------------------------------------------------------------------
-// The kernel
+// Direct global -> LDS staging (gfx950 global_load_lds_dwordx4) for BF16 rows
+// with a 16-byte-multiple pitch. One instruction moves 64 lanes x 16 bytes
+// into one contiguous 1 KB LDS segment (lane i lands at byte 16*i), i.e.
+// 512/BKS tile rows of 2*BKS bytes. The XOR swizzle is applied on the global
+// side: the lane that lands in slot s of row r fetches logical chunk
+// chunk_slot(r, s) (an involution). The lanes of one row still read that
+// row's whole 2*BKS-byte segment. Only whole BKS steps use this path; rows
+// beyond the matrix are clamped to its last row.
+// ---------------------------------------------------------------------------
+template <int ROWS, int NT, int BKS>
+struct DirectStager {
+    static constexpr int CPR = BKS / 8;          // 16-byte chunks per row
+    static constexpr int RPS = 64 / CPR;         // rows per 1 KB segment
+    static constexpr int NW = NT / 64;
+    static constexpr int SEGS = ROWS / RPS;
+    static constexpr int PER = SEGS / NW;        // instructions per wave
+    static_assert(PER * NW == SEGS && RPS * CPR == 64, "segments not divisible among waves");
+
+    __device__ __forceinline__ static void issue(const uint16_t* base, int row0, int nrows, int K,
+                                                 int k0, uint16_t* lds_tile, int wave, int lane) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int seg = wave + j * NW;
+            const int row = seg * RPS + lane / CPR;
+            const int c = chunk_slot<CPR>(row, lane % CPR);
+            const int grow = min(row0 + row, nrows - 1);
+            const uint16_t* g = base + (int64_t)grow * K + k0 + c * 8;
+            const uint32_t l = (uint32_t)(uintptr_t)(
+                (__attribute__((address_space(3))) uint16_t*)(lds_tile + seg * 512));
+            // Emitted as inline assembly on purpose: the compiler's wait
+            // insertion cannot tell the ring buffers apart and would make every
+            // later LDS read wait for these loads. Their completion is tracked
+            // explicitly with s_waitcnt vmcnt before each step barrier.
+            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(l));
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Shared pieces of the kernels: MFMAs over one LDS stage, and the epilogue.
 // ---------------------------------------------------------------------------
 
-template <int BM, int BN, int WM, int WN, int EPI, int SRC>
-__global__ void __launch_bounds__(WM * WN * 64)
-gemm_mfma_kernel(KParams p) {
-    constexpr int NT = WM * WN * 64;
-    constexpr int TM = BM / WM, TN = BN / WN;   // wave sub-tile
-    constexpr int FM = TM / 32, FN = TN / 32;   // 32x32 MFMA blocks per wave
-    static_assert(FM * 32 * WM == BM && FN * 32 * WN == BN, "bad tile split");
-    constexpr int STAGE = (BM + BN) * BK;       // BF16 elements per LDS stage
+template <int FM, int FN, int TM, int TN, int BKS>
+__device__ __forceinline__ void mma_stage(const uint16_t* sA, const uint16_t* sB, int wm, int wn,
+                                          int lane, f32x16 (&acc)[FM][FN]) {
+    constexpr int CPR = BKS / 8;
+#pragma unroll
+    for (int kk = 0; kk < BKS / 16; ++kk) {
+        const int c = kk * 2 + (lane >> 5);
+        bf16x8 fa[FM], fb[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int row = wm * TM + i * 32 + (lane & 31);
+            fa[i] = *reinterpret_cast<const bf16x8*>(sA + row * BKS + chunk_slot<CPR>(row, c) * 8);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int row = wn * TN + j * 32 + (lane & 31);
+            fb[j] = *reinterpret_cast<const bf16x8*>(sB + row * BKS + chunk_slot<CPR>(row, c) * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    }
+}
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+template <int FM, int FN, int TM, int TN, int BKS>
+__device__ __forceinline__ void load_frags(const uint16_t* sA, const uint16_t* sB, int wm, int wn,
+                                           int lane, int kk, bf16x8 (&fa)[FM], bf16x8 (&fb)[FN]) {
+    constexpr int CPR = BKS / 8;
+    const int c = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int row = wm * TM + i * 32 + (lane & 31);
+        fa[i] = *reinterpret_cast<const bf16x8*>(sA + row * BKS + chunk_slot<CPR>(row, c) * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int row = wn * TN + j * 32 + (lane & 31);
+        fb[j] = *reinterpret_cast<const bf16x8*>(sB + row * BKS + chunk_slot<CPR>(row, c) * 8);
+    }
+}
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
-
-    int tm, tn;
-    tile_of_block(p.tiles_m, p.tiles_n, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-
-    const int split = blockIdx.y;
-    const int kb = (int)min((int64_t)p.K, (int64_t)split * p.k_chunk);
-    const int ke = (int)min((int64_t)p.K, (int64_t)kb + p.k_chunk);
-    const int nk = (ke - kb + BK - 1) / BK;
-
-    f32x16 acc[FM][FN];
+template <int FM, int FN>
+__device__ __forceinline__ void mfma_block(const bf16x8 (&fa)[FM], const bf16x8 (&fb)[FN],
+                                           f32x16 (&acc)[FM][FN]) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+}
 
-    Stager<BM, NT, SRC> sa;
-    Stager<BN, NT, SRC> sb;
-    auto load_step = [&](int k0) {
-        if constexpr (SRC == SRC_FP4) {
-            sa.load(p.Aq, p.SFA, m0, p.M, p.K, k0, ke, tid);
-            sb.load(p.Bq, p.SFB, n0, p.N, p.K, k0, ke, tid);
-        } else {
-            sa.load(p.A, m0, p.M, p.K, k0, ke, tid);
-            sb.load(p.B, n0, p.N, p.K, k0, ke, tid);
-        }
-    };
-
-    if (nk > 0) {
-        load_step(kb);
-        sa.store(smem, tid);
-        sb.store(smem + BM * BK, tid);
-    }
-    __syncthreads();
-
-    for (int t = 0; t < nk; ++t) {
-        const int cur = t & 1;
-        if (t + 1 < nk) load_step(kb + (t + 1) * BK);
-
-        const uint16_t* sA = smem + cur * STAGE;
-        const uint16_t* sB = sA + BM * BK;
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int c = kk * 2 + (lane >> 5);
-            bf16x8 fa[FM], fb[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int row = wm * TM + i * 32 + (lane & 31);
-                fa[i] = *reinterpret_cast<const bf16x8*>(sA + row * BK + chunk_slot(row, c) * 8);
-            }
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int row = wn * TN + j * 32 + (lane & 31);
-                fb[j] = *reinterpret_cast<const bf16x8*>(sB + row * BK + chunk_slot(row, c) * 8);
-            }
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-        }
-
-        if (t + 1 < nk) {
-            uint16_t* nxt = smem + (cur ^ 1) * STAGE;
-            sa.store(nxt, tid);
-            sb.store(nxt + BM * BK, tid);
-        }
-        __syncthreads();
-    }
-
-    // Epilogue. acc[i][j][4g + e] is C[m][n + e] with
-    //   m = m0 + wm*TM + i*32 + lane%32,  n = n0 + wn*TN + j*32 + 8g + 4*(lane/32).
+// acc[i][j][4g + e] is C[m][n + e] with
+//   m = m0 + wm*TM + i*32 + lane%32,  n = n0 + wn*TN + j*32 + 8g + 4*(lane/32).
+template <int EPI, int FM, int FN, int TM, int TN>
+__device__ __forceinline__ void epilogue(const KParams& p, const f32x16 (&acc)[FM][FN], int m0,
+                                         int n0, int wm, int wn, int lane, int split) {
     const int M = p.M, N = p.N;
     const bool vec_ok = (N & 3) == 0;
 #pragma unroll
@@ -386,6 +405,233 @@ gemm_mfma_kernel(KParams p) {
     }
 }
 
+// Scheduling groups for one sub-step: NM MFMAs, ND LDS reads and NV direct
+// (VMEM) loads, issued as MFMA, LDS read, VMEM, MFMA, ... until the memory
+// instructions run out, then the remaining MFMAs.
+template <int NM, int ND, int NV>
+__device__ __forceinline__ void interleave_mfma() {
+#pragma unroll
+    for (int q = 0; q < NM; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // MFMA
+        if (q < ND) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // LDS read
+        if (q < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);         // VMEM read
+    }
+    if (NV > NM) __builtin_amdgcn_sched_group_barrier(0x020, NV - NM, 0);
+    if (ND > NM) __builtin_amdgcn_sched_group_barrier(0x100, ND - NM, 0);
+}
+
+template <int FM, int FN>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[FM][FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 1: register-staged operands (any source: BF16 vector / guarded, FP4).
+// ---------------------------------------------------------------------------
+
+template <int BM, int BN, int WM, int WN, int EPI, int SRC>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_mfma_kernel(KParams p) {
+    constexpr int NT = WM * WN * 64;
+    constexpr int TM = BM / WM, TN = BN / WN;   // wave sub-tile
+    constexpr int FM = TM / 32, FN = TN / 32;   // 32x32 MFMA blocks per wave
+    static_assert(FM * 32 * WM == BM && FN * 32 * WN == BN, "bad tile split");
+    constexpr int STAGE = (BM + BN) * BK;       // BF16 elements per LDS stage
+
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+
+    int tm, tn;
+    tile_of_block(p.tiles_m, p.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int split = blockIdx.y;
+    const int kb = (int)min((int64_t)p.K, (int64_t)split * p.k_chunk);
+    const int ke = (int)min((int64_t)p.K, (int64_t)kb + p.k_chunk);
+    const int nk = (ke - kb + BK - 1) / BK;
+
+    f32x16 acc[FM][FN];
+    zero_acc(acc);
+
+    Stager<BM, NT, SRC> sa;
+    Stager<BN, NT, SRC> sb;
+    auto load_step = [&](int k0) {
+        if constexpr (SRC == SRC_FP4) {
+            sa.load(p.Aq, p.SFA, m0, p.M, p.K, k0, ke, tid);
+            sb.load(p.Bq, p.SFB, n0, p.N, p.K, k0, ke, tid);
+        } else {
+            sa.load(p.A, m0, p.M, p.K, k0, ke, tid);
+            sb.load(p.B, n0, p.N, p.K, k0, ke, tid);
+        }
+    };
+
+    if (nk > 0) {
+        load_step(kb);
+        sa.store(smem, tid);
+        sb.store(smem + BM * BK, tid);
+    }
+    __syncthreads();
+
+    for (int t = 0; t < nk; ++t) {
+        const int cur = t & 1;
+        if (t + 1 < nk) load_step(kb + (t + 1) * BK);
+        const uint16_t* sA = smem + cur * STAGE;
+        mma_stage<FM, FN, TM, TN, BK>(sA, sA + BM * BK, wm, wn, lane, acc);
+        if (t + 1 < nk) {
+            uint16_t* nxt = smem + (cur ^ 1) * STAGE;
+            sa.store(nxt, tid);
+            sb.store(nxt + BM * BK, tid);
+        }
+        __syncthreads();
+    }
+
+    epilogue<EPI, FM, FN, TM, TN>(p, acc, m0, n0, wm, wn, lane, split);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 2: BF16 operands with K % 8 == 0. Whole BKS steps are loaded straight
+// into LDS (no VGPR round trip, no LDS write instructions) through a ring of
+// STAGES buffers: the loads for step t + STAGES - 1 are issued while step t
+// is multiplied, so STAGES - 1 steps of MFMA work cover the load latency.
+// ---------------------------------------------------------------------------
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier that orders LDS only. __syncthreads() would also wait for
+// every outstanding global load of the wave (its release fence covers global
+// memory), which would drain the direct-load ring at every step. Before the
+// barrier this wave's LDS reads and writes are complete; the direct loads
+// the caller needs are covered by its own vmcnt wait.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int BM, int BN, int BKS, int WM, int WN, int STAGES, int EPI>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_mfma_direct_kernel(KParams p) {
+    constexpr int NT = WM * WN * 64;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    static_assert(FM * 32 * WM == BM && FN * 32 * WN == BN, "bad tile split");
+    static_assert(STAGES >= 2, "at least double buffering");
+    constexpr int STAGE = (BM + BN) * BKS;
+    // direct-load instructions one wave issues per step
+    constexpr int L = DirectStager<BM, NT, BKS>::PER + DirectStager<BN, NT, BKS>::PER;
+
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+
+    int tm, tn;
+    tile_of_block(p.tiles_m, p.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int split = blockIdx.y;
+    const int kb = (int)min((int64_t)p.K, (int64_t)split * p.k_chunk);
+    const int ke = (int)min((int64_t)p.K, (int64_t)kb + p.k_chunk);
+    // A ragged K remainder (length not a multiple of BKS) is taken as the
+    // FIRST step, through the guarded register path; every later step is a
+    // whole BKS step loaded directly. The FP32 summation order inside the
+    // MFMAs is unspecified, so visiting the remainder first changes nothing
+    // the interface promises.
+    const int ragged = (ke - kb) % BKS;
+    const int nsteps = (ke - kb) / BKS + (ragged ? 1 : 0);
+
+    f32x16 acc[FM][FN];
+    zero_acc(acc);
+
+    auto issue = [&](int k0, uint16_t* buf) {
+        DirectStager<BM, NT, BKS>::issue(p.A, m0, p.M, p.K, k0, buf, wave, lane);
+        DirectStager<BN, NT, BKS>::issue(p.B, n0, p.N, p.K, k0, buf + BM * BKS, wave, lane);
+    };
+
+    // Direct loads are issued at a uniform rate: STAGES stages in the
+    // prologue and exactly one per loop iteration, so "stage t+1 has landed"
+    // is always "at most (STAGES-2)*L direct loads are still in flight".
+    // Stages past the end re-load the last whole step (a valid address whose
+    // buffer is never read again) instead of branching.
+    const bool has_full = (ke - kb) >= BKS;
+    const int k_last = ke - BKS;   // start of the last whole step (valid when has_full)
+    int k_next = kb;
+    if (ragged) {
+        Stager<BM, NT, SRC_BF16_VEC, BKS> sa;
+        Stager<BN, NT, SRC_BF16_VEC, BKS> sb;
+        sa.load(p.A, m0, p.M, p.K, kb, kb + ragged, tid);
+        sb.load(p.B, n0, p.N, p.K, kb, kb + ragged, tid);
+        sa.store(smem, tid);
+        sb.store(smem + BM * BKS, tid);
+        k_next = kb + ragged;
+    } else if (has_full) {
+        issue(k_next, smem);
+        k_next += BKS;
+    }
+    if (has_full) {
+#pragma unroll
+        for (int st = 1; st < STAGES; ++st) {
+            issue(min(k_next, k_last), smem + st * STAGE);
+            k_next += BKS;
+        }
+    }
+    wait_vmcnt<(STAGES - 1) * L>();
+    lds_barrier();
+
+    // Sub-step kk of a step multiplies fragments loaded during sub-step kk-1
+    // while the fragments of kk+1 are read; MFMAs and LDS reads alternate.
+    // The barrier that retires step t sits before its LAST sub-step's MFMAs
+    // (their fragments are already in registers), so the matrix core has work
+    // while the freed buffer is refilled and step t+1's first fragments are
+    // fetched.
+    constexpr int KK = BKS / 16;
+    static_assert(KK % 2 == 0, "fragment double buffer assumes an even sub-step count");
+    constexpr int LAST = (KK - 1) & 1;
+    bf16x8 fa[2][FM], fb[2][FN];
+    if (nsteps > 0) load_frags<FM, FN, TM, TN, BKS>(smem, smem + BM * BKS, wm, wn, lane, 0, fa[0], fb[0]);
+
+    auto leading_substeps = [&](const uint16_t* sA) {
+#pragma unroll
+        for (int kk = 0; kk + 1 < KK; ++kk) {
+            const int cur = kk & 1;
+            load_frags<FM, FN, TM, TN, BKS>(sA, sA + BM * BKS, wm, wn, lane, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
+            mfma_block<FM, FN>(fa[cur], fb[cur], acc);
+            interleave_mfma<FM * FN, FM + FN, 0>();
+        }
+    };
+
+    for (int t = 0; t + 1 < nsteps; ++t) {
+        leading_substeps(smem + (t % STAGES) * STAGE);
+        wait_vmcnt<(STAGES - 2) * L>();   // stage t+1 landed for this wave
+        lds_barrier();                    // ... and for every wave; stage t is free
+        issue(min(k_next, k_last), smem + (t % STAGES) * STAGE);
+        k_next += BKS;
+        const uint16_t* nA = smem + ((t + 1) % STAGES) * STAGE;
+        load_frags<FM, FN, TM, TN, BKS>(nA, nA + BM * BKS, wm, wn, lane, 0, fa[LAST ^ 1], fb[LAST ^ 1]);
+        mfma_block<FM, FN>(fa[LAST], fb[LAST], acc);
+        interleave_mfma<FM * FN, FM + FN, 0>();
+    }
+    if (nsteps > 0) {
+        leading_substeps(smem + ((nsteps - 1) % STAGES) * STAGE);
+        mfma_block<FM, FN>(fa[LAST], fb[LAST], acc);
+    }
+    wait_vmcnt<0>();   // drain the re-loads past the end before LDS is reused or the wave exits
+
+    epilogue<EPI, FM, FN, TM, TN>(p, acc, m0, n0, wm, wn, lane, split);
+}
+
 template <int BM, int BN, int WM, int WN, int EPI, int SRC>
 hipError_t launch_cfg(const KParams& kp, int splits, hipStream_t stream) {
     KParams q = kp;
@@ -397,8 +643,49 @@ hipError_t launch_cfg(const KParams& kp, int splits, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int BM, int BN, int BKS, int WM, int WN, int STAGES, int EPI>
+hipError_t launch_direct(const KParams& kp, int splits, hipStream_t stream) {
+    KParams q = kp;
+    q.tiles_m = (kp.M + BM - 1) / BM;
+    q.tiles_n = (kp.N + BN - 1) / BN;
+    dim3 grid((unsigned)(q.tiles_m * q.tiles_n), (unsigned)splits, 1);
+    hipLaunchKernelGGL((gemm_mfma_direct_kernel<BM, BN, BKS, WM, WN, STAGES, EPI>), grid,
+                       dim3(WM * WN * 64), 0, stream, q);
+    return hipGetLastError();
+}
+
+// Tile configuration for the BF16 paths. `BLOCKGEMM_TILE` (tuning only)
+// forces one of the table entries below.
+int forced_tile() {
+    static int v = [] {
+        const char* e = getenv("BLOCKGEMM_TILE");
+        return e ? atoi(e) : -1;
+    }();
+    return v;
+}
+
+template <int EPI>
+hipError_t launch_dense_vec(const KParams& kp, int splits, hipStream_t stream) {
+    int cfg = forced_tile();
+    if (cfg < 0) cfg = 2;
+    switch (cfg) {
+        //                                  BM   BN  BK WM WN ST
+        case 0: return launch_cfg<128, 128, 2, 2, EPI, SRC_BF16_VEC>(kp, splits, stream);
+        case 1: return launch_direct<256, 256, 64, 2, 2, 2, EPI>(kp, splits, stream);
+        case 2: return launch_direct<256, 256, 64, 2, 4, 2, EPI>(kp, splits, stream);
+        case 3: return launch_direct<256, 256, 32, 2, 2, 4, EPI>(kp, splits, stream);
+        case 4: return launch_direct<256, 256, 32, 2, 4, 4, EPI>(kp, splits, stream);
+        case 5: return launch_direct<256, 128, 64, 2, 2, 3, EPI>(kp, splits, stream);
+        case 6: return launch_direct<128, 128, 64, 2, 2, 2, EPI>(kp, splits, stream);
+        case 7: return launch_direct<128, 128, 64, 2, 2, 4, EPI>(kp, splits, stream);
+        case 8: return launch_direct<256, 256, 32, 2, 4, 5, EPI>(kp, splits, stream);
+        default: return launch_direct<256, 128, 64, 4, 2, 3, EPI>(kp, splits, stream);
+    }
+}
+
 template <int EPI, int SRC>
 hipError_t launch_dense_src(const KParams& kp, int splits, hipStream_t stream) {
+    if constexpr (SRC == SRC_BF16_VEC) return launch_dense_vec<EPI>(kp, splits, stream);
     return launch_cfg<128, 128, 2, 2, EPI, SRC>(kp, splits, stream);
 }
 
