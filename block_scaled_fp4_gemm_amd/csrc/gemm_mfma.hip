@@ -75,6 +75,21 @@ __device__ __forceinline__ int chunk_slot(int row, int c) {
         return c ^ (((row >> 1) ^ (row >> 3)) & 3);
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier that orders LDS only. __syncthreads() would also wait for
+// every outstanding global load of the wave (its release fence covers global
+// memory), which would drain the direct-load ring at every step. Before the
+// barrier this wave's LDS reads and writes are complete; the direct loads
+// the caller needs are covered by its own vmcnt wait.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     bf16x2 v = {(__bf16)lo, (__bf16)hi};   // v_cvt_pk_bf16_f32: round to nearest even
     return __builtin_bit_cast(uint32_t, v);
@@ -420,6 +435,109 @@ __device__ __forceinline__ void interleave_mfma() {
     if (ND > NM) __builtin_amdgcn_sched_group_barrier(0x100, ND - NM, 0);
 }
 
+// Epilogue through LDS: each wave writes its accumulator tile into LDS, then
+// the whole workgroup streams complete rows to memory, 16 contiguous bytes
+// per lane (a wave covers 1 KB of consecutive row bytes per store), instead
+// of each lane scattering 8-byte pieces over 32 rows. 16-byte chunks are
+// XOR-swizzled by row within LDS. When the tile does not fit the LDS
+// capacity (FP32 planes), rows are staged in passes of whole wave rows.
+template <int EPI, int BM, int BN, int WM, int WN, int FM, int FN, int NT, int CAP>
+__device__ __forceinline__ void staged_epilogue(const KParams& p, const f32x16 (&acc)[FM][FN],
+                                                uint8_t* lds, int m0, int n0, int wm, int wn,
+                                                int lane, int tid, int split) {
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int ELEM = (EPI == EPI_STORE_F32) ? 4 : 2;
+    constexpr int ROWB = BN * ELEM;            // bytes per staged row
+    constexpr int CPR16 = ROWB / 16;           // 16-byte chunks per row
+    constexpr int ROWS_FIT = CAP / ROWB;
+    constexpr int RP = (ROWS_FIT >= BM) ? BM : (ROWS_FIT / TM) * TM;   // rows per pass
+    static_assert(RP >= TM && BM % RP == 0, "a pass holds whole wave rows");
+    constexpr int EPC = 16 / ELEM;             // elements per chunk
+    const int M = p.M, N = p.N;
+    const bool vec_ok = (N % EPC) == 0;
+
+    constexpr int SWM = (CPR16 < 32 ? CPR16 : 32) - 1;   // XOR stays inside the row
+    static_assert((CPR16 & (CPR16 - 1)) == 0, "power-of-two chunks per row");
+    auto slot = [](int row, int chunk) { return row * ROWB + ((chunk ^ (row & SWM)) << 4); };
+
+#pragma unroll
+    for (int pass = 0; pass < BM / RP; ++pass) {
+        lds_barrier();   // previous users of LDS (main loop or previous pass) are done
+        if (wm * TM >= pass * RP && wm * TM < (pass + 1) * RP) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int row = wm * TM + i * 32 + (lane & 31) - pass * RP;
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int n_local = wn * TN + j * 32 + g * 8 + (lane >> 5) * 4;
+                        const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
+                        const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+                        if constexpr (EPI == EPI_STORE_F32) {
+                            *reinterpret_cast<f32x4*>(lds + slot(row, n_local >> 2)) = f32x4{v0, v1, v2, v3};
+                        } else {
+                            *reinterpret_cast<u32x2*>(lds + slot(row, n_local >> 3) + (lane >> 5) * 8) =
+                                u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+                        }
+                    }
+                }
+            }
+        }
+        lds_barrier();
+#pragma unroll 4
+        for (int q = tid; q < RP * CPR16; q += NT) {
+            const int row = q / CPR16, chunk = q % CPR16;
+            const int m = m0 + pass * RP + row;
+            const int n = n0 + chunk * EPC;
+            if (m >= M || n >= N) continue;
+            const u32x4 w = *reinterpret_cast<const u32x4*>(lds + slot(row, chunk));
+            const int64_t off = (int64_t)m * N + n;
+            const bool full = vec_ok && n + EPC <= N;
+            if constexpr (EPI == EPI_STORE_F32) {
+                float* plane = reinterpret_cast<float*>(p.C) + (int64_t)split * M * N;
+                if (full) {
+                    *reinterpret_cast<u32x4*>(plane + off) = w;
+                } else {
+                    const uint32_t e4[4] = {w.x, w.y, w.z, w.w};
+                    for (int e = 0; e < 4 && n + e < N; ++e) plane[off + e] = __builtin_bit_cast(float, e4[e]);
+                }
+            } else if constexpr (EPI == EPI_STORE_BF16) {
+                uint16_t* C = reinterpret_cast<uint16_t*>(p.C);
+                if (full) {
+                    *reinterpret_cast<u32x4*>(C + off) = w;
+                } else {
+                    const uint32_t e4[4] = {w.x, w.y, w.z, w.w};
+                    for (int e = 0; e < 8 && n + e < N; ++e) C[off + e] = (uint16_t)(e4[e >> 1] >> ((e & 1) * 16));
+                }
+            } else {  // EPI_SCALED_ACC: out = bf16(out + scale * delta), delta already BF16
+                uint16_t* O = reinterpret_cast<uint16_t*>(p.C);
+                const float sc = p.scale;
+                const uint32_t d4[4] = {w.x, w.y, w.z, w.w};
+                if (full) {
+                    const u32x4 o = *reinterpret_cast<const u32x4*>(O + off);
+                    const uint32_t o4[4] = {o.x, o.y, o.z, o.w};
+                    uint32_t r4[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float lo = bf16_lo(o4[e]) + sc * bf16_lo(d4[e]);
+                        const float hi = bf16_hi(o4[e]) + sc * bf16_hi(d4[e]);
+                        r4[e] = pack_bf16x2(lo, hi);
+                    }
+                    *reinterpret_cast<u32x4*>(O + off) = u32x4{r4[0], r4[1], r4[2], r4[3]};
+                } else {
+                    for (int e = 0; e < 8 && n + e < N; ++e) {
+                        const uint32_t dh = (d4[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+                        const float o = __builtin_bit_cast(float, (uint32_t)O[off + e] << 16);
+                        const float r = o + sc * __builtin_bit_cast(float, dh << 16);
+                        O[off + e] = (uint16_t)pack_bf16x2(r, 0.0f);
+                    }
+                }
+            }
+        }
+    }
+}
+
 template <int FM, int FN>
 __device__ __forceinline__ void zero_acc(f32x16 (&acc)[FM][FN]) {
 #pragma unroll
@@ -502,21 +620,6 @@ gemm_mfma_kernel(KParams p) {
 // STAGES buffers: the loads for step t + STAGES - 1 are issued while step t
 // is multiplied, so STAGES - 1 steps of MFMA work cover the load latency.
 // ---------------------------------------------------------------------------
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N <= 63, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Workgroup barrier that orders LDS only. __syncthreads() would also wait for
-// every outstanding global load of the wave (its release fence covers global
-// memory), which would drain the direct-load ring at every step. Before the
-// barrier this wave's LDS reads and writes are complete; the direct loads
-// the caller needs are covered by its own vmcnt wait.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 template <int BM, int BN, int BKS, int WM, int WN, int STAGES, int EPI>
 __global__ void __launch_bounds__(WM * WN * 64)
@@ -629,7 +732,8 @@ gemm_mfma_direct_kernel(KParams p) {
     }
     wait_vmcnt<0>();   // drain the re-loads past the end before LDS is reused or the wave exits
 
-    epilogue<EPI, FM, FN, TM, TN>(p, acc, m0, n0, wm, wn, lane, split);
+    staged_epilogue<EPI, BM, BN, WM, WN, FM, FN, NT, STAGES * STAGE * 2>(
+        p, acc, reinterpret_cast<uint8_t*>(smem), m0, n0, wm, wn, lane, tid, split);
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, int SRC>
