@@ -37,22 +37,33 @@ bool dims_ok(uint32_t M, uint32_t N, uint32_t K) {
     return M <= kMaxDim && N <= kMaxDim && K <= kMaxDim;
 }
 
-// Per-device cache of "is gfx950": 0 unknown, 1 yes, 2 no.
-std::atomic<int> g_arch_ok[64];
+// Per-device cache: 0 unknown, 2 not gfx950, otherwise 2 + compute-unit count.
+std::atomic<int> g_dev_info[64];
 
-bg_status check_device() {
+// Checks the current device and reports its compute-unit count.
+bg_status check_device(uint32_t* cus) {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return BG_ERR_DEVICE;
     if (dev < 64) {
-        const int cached = g_arch_ok[dev].load(std::memory_order_relaxed);
-        if (cached == 1) return BG_OK;
+        const int cached = g_dev_info[dev].load(std::memory_order_relaxed);
         if (cached == 2) return BG_ERR_DEVICE;
+        if (cached > 2) {
+            *cus = (uint32_t)(cached - 2);
+            return BG_OK;
+        }
     }
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return BG_ERR_DEVICE;
     const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-    if (dev < 64) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    const int n = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+    if (dev < 64) g_dev_info[dev].store(ok ? 2 + n : 2, std::memory_order_relaxed);
+    *cus = (uint32_t)n;
     return ok ? BG_OK : BG_ERR_DEVICE;
+}
+
+bg_status check_device() {
+    uint32_t cus = 0;
+    return check_device(&cus);
 }
 
 bg_status launched(hipError_t e) { return e == hipSuccess ? BG_OK : BG_ERR_LAUNCH; }
@@ -95,8 +106,9 @@ bg_status gemm_bf16(const uint16_t* A, const uint16_t* B, uint16_t* C, uint32_t 
                     uint32_t K, void* stream) {
     bg_status s = check_dense(A, B, C, M, N, K, 2);
     if (s != BG_OK || M == 0 || N == 0) return s;
-    if ((s = check_device()) != BG_OK) return s;
-    bg::DenseProblem p{A, B, C, M, N, K, K, 1, 0.0f};
+    uint32_t cus = 0;
+    if ((s = check_device(&cus)) != BG_OK) return s;
+    bg::DenseProblem p{A, B, C, M, N, K, K, 1, 0.0f, cus};
     return launched(bg::launch_dense(p, bg::EPI_STORE_BF16, (hipStream_t)stream));
 }
 
@@ -104,8 +116,9 @@ bg_status gemm_bf16_scaled_acc(const uint16_t* X, const uint16_t* B, uint16_t* o
                                uint32_t N, uint32_t K, float scale, void* stream) {
     bg_status s = check_dense(X, B, out, M, N, K, 2);
     if (s != BG_OK || M == 0 || N == 0) return s;
-    if ((s = check_device()) != BG_OK) return s;
-    bg::DenseProblem p{X, B, out, M, N, K, K, 1, scale};
+    uint32_t cus = 0;
+    if ((s = check_device(&cus)) != BG_OK) return s;
+    bg::DenseProblem p{X, B, out, M, N, K, K, 1, scale, cus};
     return launched(bg::launch_dense(p, bg::EPI_SCALED_ACC, (hipStream_t)stream));
 }
 
@@ -132,13 +145,14 @@ bg_status gemm_bf16_splitk(const uint16_t* A, const uint16_t* B, uint16_t* C, fl
             overlap(rw, range_of(C, (uint64_t)M * N * 2)))
             return BG_ERR_ALIAS;
     }
-    if ((s = check_device()) != BG_OK) return s;
+    uint32_t cus = 0;
+    if ((s = check_device(&cus)) != BG_OK) return s;
     const hipStream_t st = (hipStream_t)stream;
     if (k_splits == 1) {
-        bg::DenseProblem p{A, B, C, M, N, K, K, 1, 0.0f};
+        bg::DenseProblem p{A, B, C, M, N, K, K, 1, 0.0f, cus};
         return launched(bg::launch_dense(p, bg::EPI_STORE_BF16, st));
     }
-    bg::DenseProblem p{A, B, workspace, M, N, K, chunk, k_splits, 0.0f};
+    bg::DenseProblem p{A, B, workspace, M, N, K, chunk, k_splits, 0.0f, cus};
     hipError_t e = bg::launch_dense(p, bg::EPI_STORE_F32, st);
     if (e != hipSuccess) return BG_ERR_LAUNCH;
     return launched(bg::launch_splitk_reduce(workspace, C, M, N, k_splits, st));

@@ -25,6 +25,7 @@ struct DenseProblem {
     uint32_t k_chunk;    // K elements per split (multiple of 64, or K)
     uint32_t splits;
     float scale;
+    uint32_t cus;        // compute units of the current device (tile choice), 0 = unknown
 };
 
 struct Fp4Problem {

@@ -60,6 +60,7 @@ struct KParams {
     int k_chunk;           // K elements per split (blockIdx.y)
     int tiles_m, tiles_n;
     float scale;
+    int cus;               // compute units of the device (tile choice)
 };
 
 // Swizzled 16-byte chunk slot of logical chunk c in a tile row of CPR chunks
@@ -139,8 +140,7 @@ struct Stager;
 template <int ROWS, int NT, int BKS>
 struct Stager<ROWS, NT, SRC_BF16_VEC, BKS> {
     static constexpr int CPR = BKS / 8;
-    static constexpr int PER = ROWS * CPR / NT;
-    static_assert(PER * NT == ROWS * CPR, "tile not divisible among threads");
+    static constexpr int PER = (ROWS * CPR + NT - 1) / NT;
     u32x4 r[PER];
 
     __device__ __forceinline__ void load(const uint16_t* base, int row0, int nrows, int K,
@@ -148,6 +148,7 @@ struct Stager<ROWS, NT, SRC_BF16_VEC, BKS> {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int q = tid + i * NT;
+            if (PER * NT != ROWS * CPR && q >= ROWS * CPR) break;
             const int row = q / CPR, c = q % CPR;
             const int grow = min(row0 + row, nrows - 1);
             const int gk = k0 + c * 8;
@@ -161,6 +162,7 @@ struct Stager<ROWS, NT, SRC_BF16_VEC, BKS> {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int q = tid + i * NT;
+            if (PER * NT != ROWS * CPR && q >= ROWS * CPR) break;
             const int row = q / CPR, c = q % CPR;
             *reinterpret_cast<u32x4*>(lds + row * BKS + chunk_slot<CPR>(row, c) * 8) = r[i];
         }
@@ -171,7 +173,7 @@ struct Stager<ROWS, NT, SRC_BF16_VEC, BKS> {
 template <int ROWS, int NT, int BKS>
 struct Stager<ROWS, NT, SRC_BF16_SCALAR, BKS> {
     static constexpr int CPR = BKS / 8;
-    static constexpr int PER = ROWS * CPR / NT;
+    static constexpr int PER = (ROWS * CPR + NT - 1) / NT;
     u32x4 r[PER];
 
     __device__ __forceinline__ void load(const uint16_t* base, int row0, int nrows, int K,
@@ -179,6 +181,7 @@ struct Stager<ROWS, NT, SRC_BF16_SCALAR, BKS> {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int q = tid + i * NT;
+            if (PER * NT != ROWS * CPR && q >= ROWS * CPR) break;
             const int row = q / CPR, c = q % CPR;
             const int grow = min(row0 + row, nrows - 1);
             const uint16_t* src = base + (int64_t)grow * K;
@@ -196,6 +199,7 @@ struct Stager<ROWS, NT, SRC_BF16_SCALAR, BKS> {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int q = tid + i * NT;
+            if (PER * NT != ROWS * CPR && q >= ROWS * CPR) break;
             const int row = q / CPR, c = q % CPR;
             *reinterpret_cast<u32x4*>(lds + row * BKS + chunk_slot<CPR>(row, c) * 8) = r[i];
         }
@@ -439,7 +443,7 @@ __device__ __forceinline__ void interleave_mfma() {
 // the whole workgroup streams complete rows to memory, 16 contiguous bytes
 // per lane (a wave covers 1 KB of consecutive row bytes per store), instead
 // of each lane scattering 8-byte pieces over 32 rows. 16-byte chunks are
-// XOR-swizzled by row within LDS. When the tile does not fit the LDS
+// rotated by row within LDS. When the tile does not fit the LDS
 // capacity (FP32 planes), rows are staged in passes of whole wave rows.
 template <int EPI, int BM, int BN, int WM, int WN, int FM, int FN, int NT, int CAP>
 __device__ __forceinline__ void staged_epilogue(const KParams& p, const f32x16 (&acc)[FM][FN],
@@ -450,43 +454,45 @@ __device__ __forceinline__ void staged_epilogue(const KParams& p, const f32x16 (
     constexpr int ROWB = BN * ELEM;            // bytes per staged row
     constexpr int CPR16 = ROWB / 16;           // 16-byte chunks per row
     constexpr int ROWS_FIT = CAP / ROWB;
-    constexpr int RP = (ROWS_FIT >= BM) ? BM : (ROWS_FIT / TM) * TM;   // rows per pass
-    static_assert(RP >= TM && BM % RP == 0, "a pass holds whole wave rows");
+    constexpr int RP = (ROWS_FIT >= BM) ? BM : (ROWS_FIT / 32) * 32;   // rows per pass
+    static_assert(RP >= 32, "a pass holds at least one 32-row MFMA block");
+    constexpr int NPASS = (BM + RP - 1) / RP;
     constexpr int EPC = 16 / ELEM;             // elements per chunk
     const int M = p.M, N = p.N;
     const bool vec_ok = (N % EPC) == 0;
 
-    constexpr int SWM = (CPR16 < 32 ? CPR16 : 32) - 1;   // XOR stays inside the row
-    static_assert((CPR16 & (CPR16 - 1)) == 0, "power-of-two chunks per row");
-    auto slot = [](int row, int chunk) { return row * ROWB + ((chunk ^ (row & SWM)) << 4); };
+    // chunks rotate by the row index, so the 32 rows one store instruction
+    // covers spread over the banks for any row length
+    auto slot = [](int row, int chunk) { return row * ROWB + (((chunk + row) % CPR16) << 4); };
 
 #pragma unroll
-    for (int pass = 0; pass < BM / RP; ++pass) {
+    for (int pass = 0; pass < NPASS; ++pass) {
         lds_barrier();   // previous users of LDS (main loop or previous pass) are done
-        if (wm * TM >= pass * RP && wm * TM < (pass + 1) * RP) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int row = wm * TM + i * 32 + (lane & 31) - pass * RP;
+        for (int i = 0; i < FM; ++i) {
+            const int blk = wm * TM + i * 32;            // first row of this MFMA row block
+            if (blk < pass * RP || blk >= (pass + 1) * RP) continue;
+            const int row = blk + (lane & 31) - pass * RP;
 #pragma unroll
-                for (int j = 0; j < FN; ++j) {
+            for (int j = 0; j < FN; ++j) {
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int n_local = wn * TN + j * 32 + g * 8 + (lane >> 5) * 4;
-                        const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
-                        const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-                        if constexpr (EPI == EPI_STORE_F32) {
-                            *reinterpret_cast<f32x4*>(lds + slot(row, n_local >> 2)) = f32x4{v0, v1, v2, v3};
-                        } else {
-                            *reinterpret_cast<u32x2*>(lds + slot(row, n_local >> 3) + (lane >> 5) * 8) =
-                                u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-                        }
+                for (int g = 0; g < 4; ++g) {
+                    const int n_local = wn * TN + j * 32 + g * 8 + (lane >> 5) * 4;
+                    const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
+                    const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+                    if constexpr (EPI == EPI_STORE_F32) {
+                        *reinterpret_cast<f32x4*>(lds + slot(row, n_local >> 2)) = f32x4{v0, v1, v2, v3};
+                    } else {
+                        *reinterpret_cast<u32x2*>(lds + slot(row, n_local >> 3) + (lane >> 5) * 8) =
+                            u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
                     }
                 }
             }
         }
         lds_barrier();
+        const int rows_here = min(RP, BM - pass * RP);
 #pragma unroll 4
-        for (int q = tid; q < RP * CPR16; q += NT) {
+        for (int q = tid; q < rows_here * CPR16; q += NT) {
             const int row = q / CPR16, chunk = q % CPR16;
             const int m = m0 + pass * RP + row;
             const int n = n0 + chunk * EPC;
@@ -761,28 +767,60 @@ hipError_t launch_direct(const KParams& kp, int splits, hipStream_t stream) {
 // Tile configuration for the BF16 paths. `BLOCKGEMM_TILE` (tuning only)
 // forces one of the table entries below.
 int forced_tile() {
-    static int v = [] {
-        const char* e = getenv("BLOCKGEMM_TILE");
-        return e ? atoi(e) : -1;
-    }();
-    return v;
+    const char* e = getenv("BLOCKGEMM_TILE");
+    return e ? atoi(e) : -1;
+}
+
+// Shape -> tile choice. Tiles are scheduled in rounds of (CUs x blocks per
+// CU); the estimate is rounds x (blocks per CU) x tile area / measured
+// sustained rate of that configuration with every CU busy (TFLOP/s on
+// MI355X, random BF16 operands). Problems with a tiny K are bound by the
+// output traffic, where the narrower 160x128 tile streams best.
+struct TileChoice {
+    int cfg, bm, bn, occ;
+    double rate;
+};
+constexpr TileChoice kTileChoices[] = {
+    {2, 256, 256, 1, 1096.0},
+    {8, 160, 256, 1, 972.0},
+    {9, 160, 128, 2, 884.0},
+    {6, 128, 128, 2, 808.0},
+};
+
+int choose_tile(int M, int N, int K, int splits, int cus) {
+    if (K <= 128) return 9;
+    int best = 2;
+    double best_t = 1e300;
+    for (const TileChoice& c : kTileChoices) {
+        const double tiles = (double)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn) * splits;
+        const double slots = (double)cus * c.occ;
+        const double rounds = tiles <= cus ? 1.0 : (double)(int64_t)((tiles + slots - 1) / slots);
+        const double occ = tiles <= cus ? 1.0 : c.occ;
+        const double t = rounds * occ * c.bm * c.bn / c.rate;
+        if (t < best_t) {
+            best_t = t;
+            best = c.cfg;
+        }
+    }
+    return best;
 }
 
 template <int EPI>
 hipError_t launch_dense_vec(const KParams& kp, int splits, hipStream_t stream) {
     int cfg = forced_tile();
-    if (cfg < 0) cfg = 2;
+    if (cfg < 0) cfg = choose_tile(kp.M, kp.N, kp.K, splits, kp.cus);
     switch (cfg) {
         //                                  BM   BN  BK WM WN ST
         case 0: return launch_cfg<128, 128, 2, 2, EPI, SRC_BF16_VEC>(kp, splits, stream);
         case 1: return launch_direct<256, 256, 64, 2, 2, 2, EPI>(kp, splits, stream);
         case 2: return launch_direct<256, 256, 64, 2, 4, 2, EPI>(kp, splits, stream);
-        case 3: return launch_direct<256, 256, 32, 2, 2, 4, EPI>(kp, splits, stream);
-        case 4: return launch_direct<256, 256, 32, 2, 4, 4, EPI>(kp, splits, stream);
-        case 5: return launch_direct<256, 128, 64, 2, 2, 3, EPI>(kp, splits, stream);
+        case 3: return launch_direct<160, 256, 64, 1, 4, 3, EPI>(kp, splits, stream);
+        case 4: return launch_direct<128, 64, 64, 2, 1, 2, EPI>(kp, splits, stream);
+        case 5: return launch_direct<256, 224, 64, 4, 1, 2, EPI>(kp, splits, stream);
         case 6: return launch_direct<128, 128, 64, 2, 2, 2, EPI>(kp, splits, stream);
-        case 7: return launch_direct<128, 128, 64, 2, 2, 4, EPI>(kp, splits, stream);
-        case 8: return launch_direct<256, 256, 32, 2, 4, 5, EPI>(kp, splits, stream);
+        case 7: return launch_direct<224, 256, 64, 1, 4, 2, EPI>(kp, splits, stream);
+        case 8: return launch_direct<160, 256, 64, 1, 4, 2, EPI>(kp, splits, stream);
+        case 9: return launch_direct<160, 128, 64, 1, 4, 2, EPI>(kp, splits, stream);
         default: return launch_direct<256, 128, 64, 4, 2, 3, EPI>(kp, splits, stream);
     }
 }
@@ -805,6 +843,7 @@ hipError_t launch_dense(const DenseProblem& p, Epilogue epi, hipStream_t stream)
     kp.K = (int)p.K;
     kp.k_chunk = (int)p.k_chunk;
     kp.scale = p.scale;
+    kp.cus = p.cus > 0 ? (int)p.cus : 256;
     const bool vec = (p.K % 8) == 0;
     const int splits = (int)p.splits;
     switch (epi) {

@@ -96,3 +96,31 @@ def test_mlp_gate_up_sampled_rows_and_determinism():
     g1, g2 = bits_of(c1), bits_of(c2)
     assert_bits_equal(g1, g2, "repeat run")
     _sampled_check(a, b, g1, 2, "gate/up")
+
+
+# every entry of the tile table (BLOCKGEMM_TILE forces one; a tuning hook)
+TILE_CFGS = list(range(0, 11))
+CFG_SHAPES = [(1, 1, 8), (65, 129, 72), (161, 257, 136), (257, 225, 1000), (320, 448, 520), (33, 70, 64)]
+
+
+@pytest.mark.parametrize("cfg", TILE_CFGS)
+def test_every_tile_config_edge_shapes(cfg, monkeypatch):
+    monkeypatch.setenv("BLOCKGEMM_TILE", str(cfg))
+    for m, n, k in CFG_SHAPES:
+        a = synthetic.normal_bf16((m, k), 1.0, 3000 + m, 0)
+        b = synthetic.normal_bf16((n, k), 0.5, 3000 + n, 1)
+        got = _run(a, b)
+        check_close(got, oracle.gemm_bf16_ref(a, b), k, oracle.rms(oracle.bf16_to_f64(a)),
+                    oracle.rms(oracle.bf16_to_f64(b)), f"cfg {cfg} {m}x{n}x{k}")
+        ga = synthetic.grid_bf16((m, k), -8, 8, -5, 5, 0)
+        gb = synthetic.grid_bf16((n, k), -8, 8, -5, 5, 1)
+        want = oracle.f32_to_bf16(oracle.gemm_bf16_ref(ga, gb).astype(np.float32))
+        assert_bits_equal(_run(ga, gb), want, f"cfg {cfg} grid {m}x{n}x{k}")
+        # fused fold and split-K planes through the same tile
+        out = synthetic.normal_bf16((m, n), 1.0, 7, 2)
+        o = to_dev_bf16(out)
+        bg.gemm_bf16_scaled_acc(to_dev_bf16(ga), to_dev_bf16(gb), o, 2.0)
+        c3 = bg.gemm_bf16_splitk(to_dev_bf16(ga), to_dev_bf16(gb), 3)
+        torch.cuda.synchronize()
+        assert_bits_equal(bits_of(o), oracle.gemm_scaled_acc_exact(out, ga, gb, 2.0), f"cfg {cfg} fold")
+        assert_bits_equal(bits_of(c3), want, f"cfg {cfg} splitk3")
