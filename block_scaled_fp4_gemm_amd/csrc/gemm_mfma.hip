@@ -555,10 +555,16 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[FM][FN]) {
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 1: register-staged operands (any source: BF16 vector / guarded, FP4).
+// Kernel 1: register-staged operands (FP4 with in-register dequantization,
+// and BF16 rows whose pitch is not a multiple of 16 bytes). Global loads go
+// to registers two steps ahead (two register sets, loop unrolled by two);
+// during step t the set holding step t+1 is converted (FP4 -> exact BF16)
+// and written into the LDS buffer that step t-1 released, interleaved with
+// step t's MFMAs. Same MFMA / LDS-read interleave, step barrier placement
+// and LDS-staged epilogue as kernel 2.
 // ---------------------------------------------------------------------------
 
-template <int BM, int BN, int WM, int WN, int EPI, int SRC>
+template <int BM, int BN, int WM, int WN, int EPI, int SRC, int RSETS = 2>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_mfma_kernel(KParams p) {
     constexpr int NT = WM * WN * 64;
@@ -566,8 +572,10 @@ gemm_mfma_kernel(KParams p) {
     constexpr int FM = TM / 32, FN = TN / 32;   // 32x32 MFMA blocks per wave
     static_assert(FM * 32 * WM == BM && FN * 32 * WN == BN, "bad tile split");
     constexpr int STAGE = (BM + BN) * BK;       // BF16 elements per LDS stage
+    constexpr int KK = BK / 16;
+    constexpr int LAST = (KK - 1) & 1;
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -580,14 +588,14 @@ gemm_mfma_kernel(KParams p) {
     const int split = blockIdx.y;
     const int kb = (int)min((int64_t)p.K, (int64_t)split * p.k_chunk);
     const int ke = (int)min((int64_t)p.K, (int64_t)kb + p.k_chunk);
-    const int nk = (ke - kb + BK - 1) / BK;
+    const int nsteps = (ke - kb + BK - 1) / BK;   // the last step may be ragged (masked loads)
 
     f32x16 acc[FM][FN];
     zero_acc(acc);
 
-    Stager<BM, NT, SRC> sa;
-    Stager<BN, NT, SRC> sb;
-    auto load_step = [&](int k0) {
+    Stager<BM, NT, SRC> sa0, sa1;
+    Stager<BN, NT, SRC> sb0, sb1;
+    auto load = [&](auto& sa, auto& sb, int k0) {
         if constexpr (SRC == SRC_FP4) {
             sa.load(p.Aq, p.SFA, m0, p.M, p.K, k0, ke, tid);
             sb.load(p.Bq, p.SFB, n0, p.N, p.K, k0, ke, tid);
@@ -596,28 +604,77 @@ gemm_mfma_kernel(KParams p) {
             sb.load(p.B, n0, p.N, p.K, k0, ke, tid);
         }
     };
+    auto store = [&](auto& sa, auto& sb, uint16_t* buf) {
+        sa.store(buf, tid);
+        sb.store(buf + BM * BK, tid);
+    };
 
-    if (nk > 0) {
-        load_step(kb);
-        sa.store(smem, tid);
-        sb.store(smem + BM * BK, tid);
+    if (nsteps > 0) {
+        load(sa0, sb0, kb);
+        store(sa0, sb0, smem);
     }
-    __syncthreads();
+    if (RSETS == 2 && nsteps > 1) load(sa1, sb1, kb + BK);
+    lds_barrier();
 
-    for (int t = 0; t < nk; ++t) {
-        const int cur = t & 1;
-        if (t + 1 < nk) load_step(kb + (t + 1) * BK);
-        const uint16_t* sA = smem + cur * STAGE;
-        mma_stage<FM, FN, TM, TN, BK>(sA, sA + BM * BK, wm, wn, lane, acc);
-        if (t + 1 < nk) {
-            uint16_t* nxt = smem + (cur ^ 1) * STAGE;
-            sa.store(nxt, tid);
-            sb.store(nxt + BM * BK, tid);
+    bf16x8 fa[2][FM], fb[2][FN];
+    if (nsteps > 0) load_frags<FM, FN, TM, TN, BK>(smem, smem + BM * BK, wm, wn, lane, 0, fa[0], fb[0]);
+
+    // One K step. `held` carries step t+1 (loaded during step t-1), `next`
+    // receives step t+2.
+    auto step = [&](int t, auto& held_a, auto& held_b, auto& next_a, auto& next_b) {
+        const uint16_t* sA = smem + (t & 1) * STAGE;
+        if (t + 2 < nsteps) load(next_a, next_b, kb + (t + 2) * BK);
+#pragma unroll
+        for (int kk = 0; kk + 1 < KK; ++kk) {
+            const int cur = kk & 1;
+            load_frags<FM, FN, TM, TN, BK>(sA, sA + BM * BK, wm, wn, lane, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
+            mfma_block<FM, FN>(fa[cur], fb[cur], acc);
+            interleave_mfma<FM * FN, FM + FN, 0>();
+            if (kk == 0 && t + 1 < nsteps) store(held_a, held_b, smem + ((t + 1) & 1) * STAGE);
         }
-        __syncthreads();
+        if (t + 1 < nsteps) {
+            lds_barrier();   // step t+1 is in LDS for every wave; step t's buffer is free
+            const uint16_t* nA = smem + ((t + 1) & 1) * STAGE;
+            load_frags<FM, FN, TM, TN, BK>(nA, nA + BM * BK, wm, wn, lane, 0, fa[LAST ^ 1], fb[LAST ^ 1]);
+        }
+        mfma_block<FM, FN>(fa[LAST], fb[LAST], acc);
+        interleave_mfma<FM * FN, FM + FN, 0>();
+    };
+
+    // One register set: step t+1 is loaded at the start of step t and
+    // converted / stored before step t's last sub-step (less latency cover,
+    // fewer registers).
+    auto step1 = [&](int t) {
+        const uint16_t* sA = smem + (t & 1) * STAGE;
+        if (t + 1 < nsteps) load(sa0, sb0, kb + (t + 1) * BK);
+#pragma unroll
+        for (int kk = 0; kk + 1 < KK; ++kk) {
+            const int cur = kk & 1;
+            load_frags<FM, FN, TM, TN, BK>(sA, sA + BM * BK, wm, wn, lane, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
+            mfma_block<FM, FN>(fa[cur], fb[cur], acc);
+            interleave_mfma<FM * FN, FM + FN, 0>();
+            if (kk == KK - 2 && t + 1 < nsteps) store(sa0, sb0, smem + ((t + 1) & 1) * STAGE);
+        }
+        if (t + 1 < nsteps) {
+            lds_barrier();
+            const uint16_t* nA = smem + ((t + 1) & 1) * STAGE;
+            load_frags<FM, FN, TM, TN, BK>(nA, nA + BM * BK, wm, wn, lane, 0, fa[LAST ^ 1], fb[LAST ^ 1]);
+        }
+        mfma_block<FM, FN>(fa[LAST], fb[LAST], acc);
+        interleave_mfma<FM * FN, FM + FN, 0>();
+    };
+
+    if constexpr (RSETS == 2) {
+        for (int t = 0; t < nsteps; t += 2) {
+            step(t, sa1, sb1, sa0, sb0);
+            if (t + 1 < nsteps) step(t + 1, sa0, sb0, sa1, sb1);
+        }
+    } else {
+        for (int t = 0; t < nsteps; ++t) step1(t);
     }
 
-    epilogue<EPI, FM, FN, TM, TN>(p, acc, m0, n0, wm, wn, lane, split);
+    staged_epilogue<EPI, BM, BN, WM, WN, FM, FN, NT, 2 * STAGE * 2>(
+        p, acc, reinterpret_cast<uint8_t*>(smem), m0, n0, wm, wn, lane, tid, split);
 }
 
 // ---------------------------------------------------------------------------
@@ -742,13 +799,13 @@ gemm_mfma_direct_kernel(KParams p) {
         p, acc, reinterpret_cast<uint8_t*>(smem), m0, n0, wm, wn, lane, tid, split);
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int SRC>
+template <int BM, int BN, int WM, int WN, int EPI, int SRC, int RSETS = 2>
 hipError_t launch_cfg(const KParams& kp, int splits, hipStream_t stream) {
     KParams q = kp;
     q.tiles_m = (kp.M + BM - 1) / BM;
     q.tiles_n = (kp.N + BN - 1) / BN;
     dim3 grid((unsigned)(q.tiles_m * q.tiles_n), (unsigned)splits, 1);
-    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, EPI, SRC>), grid, dim3(WM * WN * 64), 0,
+    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, EPI, SRC, RSETS>), grid, dim3(WM * WN * 64), 0,
                        stream, q);
     return hipGetLastError();
 }
@@ -871,7 +928,14 @@ hipError_t launch_fp4(const Fp4Problem& p, hipStream_t stream) {
     kp.N = (int)p.N;
     kp.K = (int)p.K;
     kp.k_chunk = (int)p.K;
-    return launch_cfg<128, 128, 2, 2, EPI_STORE_BF16, SRC_FP4>(kp, 1, stream);
+    const char* e = getenv("BLOCKGEMM_FP4_TILE");   // tuning only
+    const int cfg = e ? atoi(e) : 0;
+    switch (cfg) {
+        case 1: return launch_cfg<256, 256, 2, 4, EPI_STORE_BF16, SRC_FP4, 2>(kp, 1, stream);
+        case 2: return launch_cfg<128, 128, 2, 2, EPI_STORE_BF16, SRC_FP4, 2>(kp, 1, stream);
+        case 3: return launch_cfg<256, 256, 2, 4, EPI_STORE_BF16, SRC_FP4, 1>(kp, 1, stream);
+        default: return launch_cfg<256, 256, 2, 2, EPI_STORE_BF16, SRC_FP4, 1>(kp, 1, stream);
+    }
 }
 
 }  // namespace bg

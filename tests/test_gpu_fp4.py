@@ -65,3 +65,21 @@ def test_fp4_config_sampled_rows():
     ref = oracle.gemm_fp4_ref(a[rows], sfa[rows], b, sfb)
     check_close(got[rows], ref, 8192, oracle.rms(oracle.dequant_fp4(a, sfa)),
                 oracle.rms(oracle.dequant_fp4(b, sfb)), "fp4 config")
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+def test_every_fp4_tile_config(cfg, monkeypatch):
+    """Each FP4 tile variant (BLOCKGEMM_FP4_TILE, a tuning hook) on ragged shapes."""
+    monkeypatch.setenv("BLOCKGEMM_FP4_TILE", str(cfg))
+    for m, n, k in [(1, 1, 16), (65, 129, 48), (257, 255, 1040), (300, 520, 208)]:
+        a, b = synthetic.fp4_packed(m, k, 70 + cfg, 0), synthetic.fp4_packed(n, k, 70 + cfg, 1)
+        sfa = synthetic.e4m3_uniform(m, k // 16, 2 ** -4, 2 ** 4, 70, 4)
+        sfb = synthetic.e4m3_uniform(n, k // 16, 2 ** -4, 2 ** 4, 70, 5)
+        got = _run(a, sfa, b, sfb)
+        check_close(got, oracle.gemm_fp4_ref(a, sfa, b, sfb), k, oracle.rms(oracle.dequant_fp4(a, sfa)),
+                    oracle.rms(oracle.dequant_fp4(b, sfb)), f"fp4 cfg {cfg} {m}x{n}x{k}")
+        # power-of-two scales: exact in FP32, so bit-exact
+        ea = synthetic.e4m3_choice(m, k // 16, [0x38, 0x40], 71, 4)
+        eb = synthetic.e4m3_choice(n, k // 16, [0x38, 0x40], 71, 5)
+        want = oracle.f32_to_bf16(oracle.gemm_fp4_ref(a, ea, b, eb).astype(np.float32))
+        assert_bits_equal(_run(a, ea, b, eb), want, f"fp4 cfg {cfg} exact {m}x{n}x{k}")
