@@ -229,11 +229,16 @@ def measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream):
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
 
     def timed(fn, reps=20):
+        """Median per-call time in us, warm and cold. Calls are enqueued
+        back to back (no host synchronisation between them), each inside its
+        own pair of events on the stream; cold calls are preceded by a 1 GiB
+        write that evicts the L2s and the 256 MB Infinity Cache."""
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
-        warm, cold = [], []
-        for mode, out in (("warm", warm), ("cold", cold)):
+        res = {}
+        for mode in ("warm", "cold"):
+            pairs = []
             for _ in range(reps):
                 if mode == "cold":
                     flush.zero_()
@@ -242,9 +247,10 @@ def measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream):
                 s.record(stream)
                 fn()
                 e.record(stream)
-                torch.cuda.synchronize()
-                out.append(s.elapsed_time(e) * 1e3)
-        return float(np.median(warm)), float(np.median(cold))
+                pairs.append((s, e))
+            torch.cuda.synchronize()
+            res[mode] = float(np.median([a.elapsed_time(b) * 1e3 for a, b in pairs]))
+        return res["warm"], res["cold"]
 
     rows = {}
 

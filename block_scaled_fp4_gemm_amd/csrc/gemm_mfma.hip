@@ -445,10 +445,11 @@ __device__ __forceinline__ void interleave_mfma() {
 // of each lane scattering 8-byte pieces over 32 rows. 16-byte chunks are
 // rotated by row within LDS. When the tile does not fit the LDS
 // capacity (FP32 planes), rows are staged in passes of whole wave rows.
-template <int EPI, int BM, int BN, int WM, int WN, int FM, int FN, int NT, int CAP>
+template <int EPI, int BM, int BN, int WM, int WN, int FM, int FN, int NT, int CAP, int NPRE = 0>
 __device__ __forceinline__ void staged_epilogue(const KParams& p, const f32x16 (&acc)[FM][FN],
                                                 uint8_t* lds, int m0, int n0, int wm, int wn,
-                                                int lane, int tid, int split) {
+                                                int lane, int tid, int split,
+                                                const u32x4* pre = nullptr) {
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int ELEM = (EPI == EPI_STORE_F32) ? 4 : 2;
     constexpr int ROWB = BN * ELEM;            // bytes per staged row
@@ -491,8 +492,11 @@ __device__ __forceinline__ void staged_epilogue(const KParams& p, const f32x16 (
         }
         lds_barrier();
         const int rows_here = min(RP, BM - pass * RP);
-#pragma unroll 4
-        for (int q = tid; q < rows_here * CPR16; q += NT) {
+        constexpr int ITER = (RP * CPR16 + NT - 1) / NT;
+#pragma unroll
+        for (int it = 0; it < ITER; ++it) {
+            const int q = tid + it * NT;
+            if (q >= rows_here * CPR16) break;
             const int row = q / CPR16, chunk = q % CPR16;
             const int m = m0 + pass * RP + row;
             const int n = n0 + chunk * EPC;
@@ -521,7 +525,11 @@ __device__ __forceinline__ void staged_epilogue(const KParams& p, const f32x16 (
                 const float sc = p.scale;
                 const uint32_t d4[4] = {w.x, w.y, w.z, w.w};
                 if (full) {
-                    const u32x4 o = *reinterpret_cast<const u32x4*>(O + off);
+                    u32x4 o;
+                    if constexpr (NPRE > 0)
+                        o = pre[it];   // loaded at kernel start (single pass)
+                    else
+                        o = *reinterpret_cast<const u32x4*>(O + off);
                     const uint32_t o4[4] = {o.x, o.y, o.z, o.w};
                     uint32_t r4[4];
 #pragma unroll
@@ -684,19 +692,21 @@ gemm_mfma_kernel(KParams p) {
 // is multiplied, so STAGES - 1 steps of MFMA work cover the load latency.
 // ---------------------------------------------------------------------------
 
-template <int BM, int BN, int BKS, int WM, int WN, int STAGES, int EPI>
+template <int BM, int BN, int BKS, int WM, int WN, int STAGES, int EPI, bool PREF = false>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_mfma_direct_kernel(KParams p) {
     constexpr int NT = WM * WN * 64;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
     static_assert(FM * 32 * WM == BM && FN * 32 * WN == BN, "bad tile split");
-    static_assert(STAGES >= 2, "at least double buffering");
+    static_assert(STAGES >= 1, "at least one LDS stage");
     constexpr int STAGE = (BM + BN) * BKS;
     // direct-load instructions one wave issues per step
     constexpr int L = DirectStager<BM, NT, BKS>::PER + DirectStager<BN, NT, BKS>::PER;
 
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * STAGE];
+    // the prefetching fold stages its whole BF16 tile in one epilogue pass
+    constexpr int SMEM_ELEMS = (PREF && BM * BN > STAGES * STAGE) ? BM * BN : STAGES * STAGE;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM_ELEMS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -753,7 +763,26 @@ gemm_mfma_direct_kernel(KParams p) {
             k_next += BKS;
         }
     }
-    wait_vmcnt<(STAGES - 1) * L>();
+    // Fused fold with a short K: the workgroup's `out` tile is fetched now,
+    // in the same 16-byte pieces the epilogue's row-streaming assigns to
+    // this thread, so its HBM latency overlaps the operand loads and MFMAs.
+    constexpr int PCPR = BN * 2 / 16;
+    constexpr int NPRE = PREF ? (BM * PCPR + NT - 1) / NT : 0;
+    static_assert(!PREF || EPI == EPI_SCALED_ACC, "prefetch is for the fold epilogue");
+    u32x4 pre[NPRE > 0 ? NPRE : 1];
+    if constexpr (PREF) {
+        const uint16_t* O = reinterpret_cast<const uint16_t*>(p.C);
+        const bool vec_ok = (p.N & 7) == 0;
+#pragma unroll
+        for (int it = 0; it < NPRE; ++it) {
+            const int q = tid + it * NT;
+            const int row = q / PCPR, chunk = q % PCPR;
+            const int m = m0 + row, n = n0 + chunk * 8;
+            if (q < BM * PCPR && m < p.M && vec_ok && n + 8 <= p.N)
+                pre[it] = *reinterpret_cast<const u32x4*>(O + (int64_t)m * p.N + n);
+        }
+    }
+    wait_vmcnt<(STAGES - 1) * L + NPRE>();
     lds_barrier();
 
     // Sub-step kk of a step multiplies fragments loaded during sub-step kk-1
@@ -780,7 +809,7 @@ gemm_mfma_direct_kernel(KParams p) {
 
     for (int t = 0; t + 1 < nsteps; ++t) {
         leading_substeps(smem + (t % STAGES) * STAGE);
-        wait_vmcnt<(STAGES - 2) * L>();   // stage t+1 landed for this wave
+        wait_vmcnt<(STAGES >= 2 ? (STAGES - 2) * L : 0)>();   // stage t+1 landed for this wave
         lds_barrier();                    // ... and for every wave; stage t is free
         issue(min(k_next, k_last), smem + (t % STAGES) * STAGE);
         k_next += BKS;
@@ -795,8 +824,8 @@ gemm_mfma_direct_kernel(KParams p) {
     }
     wait_vmcnt<0>();   // drain the re-loads past the end before LDS is reused or the wave exits
 
-    staged_epilogue<EPI, BM, BN, WM, WN, FM, FN, NT, STAGES * STAGE * 2>(
-        p, acc, reinterpret_cast<uint8_t*>(smem), m0, n0, wm, wn, lane, tid, split);
+    staged_epilogue<EPI, BM, BN, WM, WN, FM, FN, NT, SMEM_ELEMS * 2, NPRE>(
+        p, acc, reinterpret_cast<uint8_t*>(smem), m0, n0, wm, wn, lane, tid, split, pre);
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, int SRC, int RSETS = 2>
@@ -810,13 +839,17 @@ hipError_t launch_cfg(const KParams& kp, int splits, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int BM, int BN, int BKS, int WM, int WN, int STAGES, int EPI>
+template <int BM, int BN, int BKS, int WM, int WN, int STAGES, int EPI, bool PREF = false>
 hipError_t launch_direct(const KParams& kp, int splits, hipStream_t stream) {
+    // A single LDS stage only works when the whole K chunk is one step.
+    if constexpr (STAGES == 1) {
+        if (kp.k_chunk > BKS) return launch_direct<BM, BN, BKS, WM, WN, 2, EPI, PREF>(kp, splits, stream);
+    }
     KParams q = kp;
     q.tiles_m = (kp.M + BM - 1) / BM;
     q.tiles_n = (kp.N + BN - 1) / BN;
     dim3 grid((unsigned)(q.tiles_m * q.tiles_n), (unsigned)splits, 1);
-    hipLaunchKernelGGL((gemm_mfma_direct_kernel<BM, BN, BKS, WM, WN, STAGES, EPI>), grid,
+    hipLaunchKernelGGL((gemm_mfma_direct_kernel<BM, BN, BKS, WM, WN, STAGES, EPI, PREF>), grid,
                        dim3(WM * WN * 64), 0, stream, q);
     return hipGetLastError();
 }
@@ -844,8 +877,8 @@ constexpr TileChoice kTileChoices[] = {
     {6, 128, 128, 2, 808.0},
 };
 
-int choose_tile(int M, int N, int K, int splits, int cus) {
-    if (K <= 128) return 9;
+int choose_tile(int M, int N, int K, int splits, int cus, int epi) {
+    if (K <= 128) return epi == EPI_SCALED_ACC ? 11 : 9;
     int best = 2;
     double best_t = 1e300;
     for (const TileChoice& c : kTileChoices) {
@@ -865,7 +898,7 @@ int choose_tile(int M, int N, int K, int splits, int cus) {
 template <int EPI>
 hipError_t launch_dense_vec(const KParams& kp, int splits, hipStream_t stream) {
     int cfg = forced_tile();
-    if (cfg < 0) cfg = choose_tile(kp.M, kp.N, kp.K, splits, kp.cus);
+    if (cfg < 0) cfg = choose_tile(kp.M, kp.N, kp.K, splits, kp.cus, EPI);
     switch (cfg) {
         //                                  BM   BN  BK WM WN ST
         case 0: return launch_cfg<128, 128, 2, 2, EPI, SRC_BF16_VEC>(kp, splits, stream);
@@ -878,6 +911,26 @@ hipError_t launch_dense_vec(const KParams& kp, int splits, hipStream_t stream) {
         case 7: return launch_direct<224, 256, 64, 1, 4, 2, EPI>(kp, splits, stream);
         case 8: return launch_direct<160, 256, 64, 1, 4, 2, EPI>(kp, splits, stream);
         case 9: return launch_direct<160, 128, 64, 1, 4, 2, EPI>(kp, splits, stream);
+        case 11:
+            if constexpr (EPI == EPI_SCALED_ACC)
+                return launch_direct<160, 128, 64, 1, 4, 2, EPI, true>(kp, splits, stream);
+            else
+                return launch_direct<160, 128, 64, 1, 4, 2, EPI>(kp, splits, stream);
+        case 12:
+            if constexpr (EPI == EPI_SCALED_ACC)
+                return launch_direct<128, 128, 64, 2, 2, 2, EPI, true>(kp, splits, stream);
+            else
+                return launch_direct<128, 128, 64, 2, 2, 2, EPI>(kp, splits, stream);
+        case 13:
+            if constexpr (EPI == EPI_SCALED_ACC)
+                return launch_direct<160, 128, 64, 1, 4, 1, EPI, true>(kp, splits, stream);
+            else
+                return launch_direct<160, 128, 64, 1, 4, 1, EPI>(kp, splits, stream);
+        case 14:
+            if constexpr (EPI == EPI_SCALED_ACC)
+                return launch_direct<128, 128, 64, 2, 2, 1, EPI, true>(kp, splits, stream);
+            else
+                return launch_direct<128, 128, 64, 2, 2, 1, EPI>(kp, splits, stream);
         default: return launch_direct<256, 128, 64, 4, 2, 3, EPI>(kp, splits, stream);
     }
 }

@@ -13,11 +13,11 @@
 // Design (CDNA4): a workgroup of 16x16 threads owns a (16*RM) x (16*RN)
 // output tile; each thread keeps an RM x RN block of accumulators. K is
 // walked in steps of KT; each step stages A and B rows as FP32 into LDS,
-// K-major ([k][row]), so a thread reads its RM (or RN) operands at one k with
-// 16-byte LDS loads: A reads are broadcast across the 16 threads of a row
-// group, B reads from 16 threads are contiguous. The per-output k order is
-// untouched by the tiling: tiles are visited in ascending k and, inside a
-// tile, k ascends.
+// K-major ([k][row]). The per-output k order is untouched by the tiling:
+// tiles are visited in ascending k and, inside a tile, k ascends.
+#include <cmath>
+#include <cstdlib>
+
 #include "bg_internal.hpp"
 
 #pragma clang fp contract(off)
@@ -42,14 +42,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
 // into lds[k][ROWS] as FP32. Positions with k >= K, or rows >= nrows, get 0.
 // A unit is 8 consecutive k of one row; consecutive threads take consecutive
 // rows, so the eight FP32 writes of a unit land in distinct banks.
-template <int ROWS, int NT>
+template <int ROWS, int NT, int LD>
 __device__ __forceinline__ void stage(float* lds, const uint16_t* src, int row0, int nrows,
                                       int K, int k0, bool vec, int tid) {
     constexpr int UNITS = ROWS * (KT / 8);
-    static_assert(UNITS % NT == 0, "tile not divisible");
 #pragma unroll
-    for (int i = 0; i < UNITS / NT; ++i) {
+    for (int i = 0; i < (UNITS + NT - 1) / NT; ++i) {
         const int u = tid + i * NT;
+        if (UNITS % NT != 0 && u >= UNITS) break;
         const int row = u % ROWS, c = u / ROWS;
         const int grow = row0 + row, gk = k0 + c * 8;
         uint32_t h[8];
@@ -63,17 +63,24 @@ __device__ __forceinline__ void stage(float* lds, const uint16_t* src, int row0,
                 h[x] = (grow < nrows && gk + x < K) ? (uint32_t)src[(int64_t)grow * K + gk + x] : 0u;
         }
 #pragma unroll
-        for (int x = 0; x < 8; ++x) lds[(c * 8 + x) * ROWS + row] = bf16_bits_to_f32(h[x]);
+        for (int x = 0; x < 8; ++x) lds[(c * 8 + x) * LD + row] = bf16_bits_to_f32(h[x]);
     }
 }
 
+// A workgroup of 16 x 16 threads owns a (16*RM) x (16*RN) output tile; thread
+// (tx, ty) keeps outputs rows ty + 16*i (i < RM) x cols tx*RN + j (j < RN).
+// A rows are read as broadcast 4-byte LDS loads (16 threads share one row
+// set), B columns as RN-wide loads. The register block size is chosen per
+// shape so the number of waves lands just below a multiple of the SIMD
+// count: the work is pure VALU, and a SIMD holding one wave more than the
+// others sets the runtime.
 template <int RM, int RN, bool F32_OUT>
 __global__ void __launch_bounds__(256)
 gemm_ordered_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* C,
                     int M, int N, int K, int tiles_n) {
     constexpr int TM = 16 * RM, TN = 16 * RN;
-    static_assert(RM % 4 == 0 && RN % 4 == 0, "register blocks are built from float4 reads");
-    __shared__ __attribute__((aligned(16))) float sA[KT * TM];
+    constexpr int LDA = TM + (TM % 2 == 0 ? 1 : 0);   // odd stride: staging writes spread over banks
+    __shared__ __attribute__((aligned(16))) float sA[KT * LDA];
     __shared__ __attribute__((aligned(16))) float sB[KT * TN];
 
     const int tid = threadIdx.x;
@@ -88,24 +95,26 @@ gemm_ordered_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__
 #pragma unroll
         for (int j = 0; j < RN; ++j) acc[i][j] = 0.0f;
 
-    // thread rows: ty*4 + 64*a + {0..3};  thread cols: tx*4 + 64*b + {0..3}
     for (int k0 = 0; k0 < K; k0 += KT) {
         __syncthreads();
-        stage<TM, 256>(sA, A, m0, M, K, k0, vec, tid);
-        stage<TN, 256>(sB, B, n0, N, K, k0, vec, tid);
+        stage<TM, 256, LDA>(sA, A, m0, M, K, k0, vec, tid);
+        stage<TN, 256, TN>(sB, B, n0, N, K, k0, vec, tid);
         __syncthreads();
         const int kn = min(KT, K - k0);
+#pragma unroll 2
         for (int kk = 0; kk < kn; ++kk) {
             float a[RM], b[RN];
 #pragma unroll
-            for (int q = 0; q < RM / 4; ++q) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(&sA[kk * TM + q * 64 + ty * 4]);
-                a[4 * q + 0] = v.x; a[4 * q + 1] = v.y; a[4 * q + 2] = v.z; a[4 * q + 3] = v.w;
-            }
+            for (int i = 0; i < RM; ++i) a[i] = sA[kk * LDA + ty + 16 * i];
+            if constexpr (RN == 4) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(&sB[kk * TN + tx * 4]);
+                b[0] = v.x; b[1] = v.y; b[2] = v.z; b[3] = v.w;
+            } else if constexpr (RN == 2) {
+                const float2 v = *reinterpret_cast<const float2*>(&sB[kk * TN + tx * 2]);
+                b[0] = v.x; b[1] = v.y;
+            } else {
 #pragma unroll
-            for (int q = 0; q < RN / 4; ++q) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(&sB[kk * TN + q * 64 + tx * 4]);
-                b[4 * q + 0] = v.x; b[4 * q + 1] = v.y; b[4 * q + 2] = v.z; b[4 * q + 3] = v.w;
+                for (int j = 0; j < RN; ++j) b[j] = sB[kk * TN + tx * RN + j];
             }
 #pragma unroll
             for (int i = 0; i < RM; ++i)
@@ -117,11 +126,11 @@ gemm_ordered_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__
 
 #pragma unroll
     for (int i = 0; i < RM; ++i) {
-        const int m = m0 + (i / 4) * 64 + ty * 4 + (i % 4);
+        const int m = m0 + ty + 16 * i;
         if (m >= M) continue;
 #pragma unroll
         for (int j = 0; j < RN; ++j) {
-            const int n = n0 + (j / 4) * 64 + tx * 4 + (j % 4);
+            const int n = n0 + tx * RN + j;
             if (n >= N) continue;
             if constexpr (F32_OUT)
                 reinterpret_cast<float*>(C)[(int64_t)m * N + n] = acc[i][j];
@@ -184,18 +193,91 @@ splitk_reduce_kernel(const float* __restrict__ ws, uint16_t* __restrict__ C, int
 __global__ void __launch_bounds__(256)
 scaled_add_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ delta, int64_t count,
                   float scale) {
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= count) return;
-    const float o = bf16_bits_to_f32(out[e]);
-    const float d = bf16_bits_to_f32(delta[e]);
-    out[e] = f32_to_bf16_rne(__fadd_rn(o, __fmul_rn(scale, d)));
+    const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (e0 >= count) return;
+    if (e0 + 8 <= count) {   // base pointers are 16-byte aligned, so is every 8-element group
+        const u32x4 o = *reinterpret_cast<const u32x4*>(out + e0);
+        const u32x4 d = *reinterpret_cast<const u32x4*>(delta + e0);
+        const uint32_t o4[4] = {o.x, o.y, o.z, o.w}, d4[4] = {d.x, d.y, d.z, d.w};
+        uint32_t r4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float lo = __fadd_rn(bf16_bits_to_f32(o4[e] & 0xFFFFu), __fmul_rn(scale, bf16_bits_to_f32(d4[e] & 0xFFFFu)));
+            const float hi = __fadd_rn(bf16_bits_to_f32(o4[e] >> 16), __fmul_rn(scale, bf16_bits_to_f32(d4[e] >> 16)));
+            r4[e] = (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+        }
+        *reinterpret_cast<u32x4*>(out + e0) = u32x4{r4[0], r4[1], r4[2], r4[3]};
+    } else {
+        for (int64_t e = e0; e < count; ++e) {
+            const float o = bf16_bits_to_f32(out[e]);
+            const float d = bf16_bits_to_f32(delta[e]);
+            out[e] = f32_to_bf16_rne(__fadd_rn(o, __fmul_rn(scale, d)));
+        }
+    }
 }
 
 }  // namespace
 
+// Register-block choice, fitted to MI355X measurements of this kernel: the
+// VALU loop needs about three waves per SIMD to hide LDS and dependency
+// latency (one wave per SIMD runs at roughly half speed even when the waves
+// split evenly), two-column blocks read B most cheaply, and a larger block
+// reuses its operands better. Score = min(waves per SIMD, 3) x column factor
+// x (outputs per thread)^(1/4); the highest score wins.
+namespace {
+struct OrdChoice {
+    int rm, rn;
+};
+constexpr OrdChoice kOrdChoices[] = {{4, 4}, {2, 2}, {2, 4}, {6, 2}, {5, 2}, {4, 2}, {3, 2},
+                                     {9, 1}, {6, 1}, {4, 1}, {2, 1}, {1, 1}};
+
+template <int RM, int RN>
+hipError_t run_ordered(const uint16_t* A, const uint16_t* B, void* C, bool f32_out, int M, int N,
+                       int K, hipStream_t stream) {
+    return launch_ordered_cfg<RM, RN>(A, B, C, f32_out, M, N, K, stream);
+}
+}  // namespace
+
 hipError_t launch_ordered(const uint16_t* A, const uint16_t* B, void* C, bool f32_out, uint32_t M,
                           uint32_t N, uint32_t K, hipStream_t stream) {
-    return launch_ordered_cfg<4, 4>(A, B, C, f32_out, (int)M, (int)N, (int)K, stream);
+    int simds = 1024;
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+            simds = 4 * cus;
+    }
+    const char* e = getenv("BLOCKGEMM_ORD_TILE");   // tuning only: index into kOrdChoices
+    int pick = e ? atoi(e) : -1;
+    if (pick < 0 || pick >= (int)(sizeof(kOrdChoices) / sizeof(kOrdChoices[0]))) {
+        double best = -1.0;
+        for (int c = 0; c < (int)(sizeof(kOrdChoices) / sizeof(kOrdChoices[0])); ++c) {
+            const int rm = kOrdChoices[c].rm, rn = kOrdChoices[c].rn;
+            const double waves = 4.0 * ((M + 16 * rm - 1) / (16 * rm)) * (double)((N + 16 * rn - 1) / (16 * rn));
+            const double per_simd = waves / simds;
+            const double col = rn == 2 ? 1.0 : (rn == 4 ? 0.9 : 0.85);
+            const double score = (per_simd < 3.0 ? per_simd : 3.0) * col * std::sqrt(std::sqrt((double)(rm * rn)));
+            if (score > best) {
+                best = score;
+                pick = c;
+            }
+        }
+    }
+    const int m = (int)M, n = (int)N, k = (int)K;
+    switch (pick) {
+        case 0: return run_ordered<4, 4>(A, B, C, f32_out, m, n, k, stream);
+        case 1: return run_ordered<2, 2>(A, B, C, f32_out, m, n, k, stream);
+        case 2: return run_ordered<2, 4>(A, B, C, f32_out, m, n, k, stream);
+        case 3: return run_ordered<6, 2>(A, B, C, f32_out, m, n, k, stream);
+        case 4: return run_ordered<5, 2>(A, B, C, f32_out, m, n, k, stream);
+        case 5: return run_ordered<4, 2>(A, B, C, f32_out, m, n, k, stream);
+        case 6: return run_ordered<3, 2>(A, B, C, f32_out, m, n, k, stream);
+        case 7: return run_ordered<9, 1>(A, B, C, f32_out, m, n, k, stream);
+        case 8: return run_ordered<6, 1>(A, B, C, f32_out, m, n, k, stream);
+        case 9: return run_ordered<4, 1>(A, B, C, f32_out, m, n, k, stream);
+        case 10: return run_ordered<2, 1>(A, B, C, f32_out, m, n, k, stream);
+        default: return run_ordered<1, 1>(A, B, C, f32_out, m, n, k, stream);
+    }
 }
 
 hipError_t launch_splitk_reduce(const float* ws, uint16_t* C, uint32_t M, uint32_t N,
@@ -211,7 +293,8 @@ hipError_t launch_splitk_reduce(const float* ws, uint16_t* C, uint32_t M, uint32
 
 hipError_t launch_scaled_add(uint16_t* out, const uint16_t* delta, size_t count, float scale,
                              hipStream_t stream) {
-    dim3 grid((unsigned)((count + 255) / 256));
+    const int64_t threads = ((int64_t)count + 7) / 8;
+    dim3 grid((unsigned)((threads + 255) / 256));
     hipLaunchKernelGGL(scaled_add_kernel, grid, dim3(256), 0, stream, out, delta, (int64_t)count,
                        scale);
     return hipGetLastError();

@@ -166,3 +166,29 @@ def test_ordered_worked_cases_on_gpu():
     torch.cuda.synchronize()
     assert int(c32.cpu().numpy().view(np.uint32)[0, 0]) == 0
     assert int(d32.cpu().numpy().view(np.uint32)[0, 0]) == 3
+
+
+@pytest.mark.parametrize("choice", list(range(12)))
+def test_every_ordered_register_block_bit_exact(choice, monkeypatch):
+    """Each register-block variant (BLOCKGEMM_ORD_TILE, a tuning hook) keeps the strict order."""
+    monkeypatch.setenv("BLOCKGEMM_ORD_TILE", str(choice))
+    for m, n, k in [(1, 1, 1), (37, 70, 300), (150, 33, 65), (145, 256, 2048)]:
+        x = synthetic.normal_bf16((m, k), 1.0, 90 + choice, 0)
+        w = synthetic.normal_bf16((n, k), 0.5, 90 + choice, 1)
+        dx, dw = to_dev_bf16(x), to_dev_bf16(w)
+        c32 = bg.gemm_bf16_ordered_f32(dx, dw)
+        c16 = bg.gemm_bf16_ordered(dx, dw)
+        torch.cuda.synchronize()
+        want = oracle.gemm_ordered_f32(x, w)
+        assert_bits_equal(c32.cpu().numpy().view(np.uint32), want.view(np.uint32), f"ord {choice} {m}x{n}x{k}")
+        assert_bits_equal(bits_of(c16), oracle.f32_to_bf16(want), f"ord bf16 {choice} {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("count", [1, 7, 8, 9, 1000, 4099])
+def test_bf16_scaled_add_matches_epilogue_definition(count):
+    out = synthetic.normal_bf16((count,), 1.0, 11, 2)
+    d = synthetic.normal_bf16((count,), 0.3, 11, 3)
+    o = to_dev_bf16(out)
+    bg.bf16_scaled_add(o, to_dev_bf16(d), 0.7)
+    torch.cuda.synchronize()
+    assert_bits_equal(bits_of(o), oracle.scaled_acc_epilogue(out, d, 0.7), f"scaled_add {count}")
