@@ -100,12 +100,14 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
 // E4M3FN byte -> FP32 (exact): bias 7, subnormal m*2^-9, S.1111.111 = NaN.
+// Written with selects only, so it stays in straight-line code.
 __device__ __forceinline__ float e4m3fn_to_f32(uint32_t b) {
     const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-    float mag = (e == 0) ? (float)m * 0x1p-9f
-                         : __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20));
-    if (e == 15u && m == 7u) mag = __builtin_nanf("");
-    return (b & 0x80u) ? -mag : mag;
+    const float normal = __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20));
+    const float subnormal = (float)m * 0x1p-9f;
+    float mag = e != 0u ? normal : subnormal;
+    mag = (b & 0x7Fu) == 0x7Fu ? __builtin_nanf("") : mag;
+    return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, mag) | ((b & 0x80u) << 24));
 }
 
 // Workgroup -> (tile_m, tile_n). Dispatch places workgroup b on XCD b % 8;
@@ -216,6 +218,7 @@ struct Stager<ROWS, NT, SRC_FP4, BK> {
     static_assert(PER * NT == ROWS * (BK / 16), "tile not divisible among threads");
     u32x2 w[PER];
     uint32_t s[PER];
+    uint32_t valid;   // bit i: unit i lies inside the K range (applied when converting)
 
     __device__ __forceinline__ void load(const uint8_t* q, const uint8_t* sf, int row0,
                                          int nrows, int K, int k0, int k_end, int tid) {
@@ -225,13 +228,13 @@ struct Stager<ROWS, NT, SRC_FP4, BK> {
             const int row = u >> 2, g = u & 3;
             const int grow = min(row0 + row, nrows - 1);
             const int gk = k0 + g * 16;
-            if (gk < k_end) {
-                w[i] = *reinterpret_cast<const u32x2*>(q + (int64_t)grow * (K >> 1) + (gk >> 1));
-                s[i] = sf[(int64_t)grow * (K >> 4) + (gk >> 4)];
-            } else {
-                w[i] = u32x2{0u, 0u};
-                s[i] = 0u;
-            }
+            // always load from a valid group (K >= 16 whenever a step exists),
+            // then zero what lies past the end of this K range
+            const int gkc = min(gk, K - 16);
+            w[i] = *reinterpret_cast<const u32x2*>(q + (int64_t)grow * (K >> 1) + (gkc >> 1));
+            s[i] = sf[(int64_t)grow * (K >> 4) + (gkc >> 4)];
+            if (i == 0) valid = 0u;
+            valid |= (gk < k_end ? 1u : 0u) << i;
         }
     }
 
@@ -251,11 +254,11 @@ struct Stager<ROWS, NT, SRC_FP4, BK> {
         for (int i = 0; i < PER; ++i) {
             const int u = tid + i * NT;
             const int row = u >> 2, g = u & 3;
-            const float sc = e4m3fn_to_f32(s[i]);
-            const u32x4 lo = {deq2(w[i].x, sc, 0), deq2(w[i].x, sc, 1), deq2(w[i].x, sc, 2),
-                              deq2(w[i].x, sc, 3)};
-            const u32x4 hi = {deq2(w[i].y, sc, 0), deq2(w[i].y, sc, 1), deq2(w[i].y, sc, 2),
-                              deq2(w[i].y, sc, 3)};
+            const bool in = (valid >> i) & 1u;
+            const uint32_t wx = in ? w[i].x : 0u, wy = in ? w[i].y : 0u;
+            const float sc = e4m3fn_to_f32(in ? s[i] : 0u);
+            const u32x4 lo = {deq2(wx, sc, 0), deq2(wx, sc, 1), deq2(wx, sc, 2), deq2(wx, sc, 3)};
+            const u32x4 hi = {deq2(wy, sc, 0), deq2(wy, sc, 1), deq2(wy, sc, 2), deq2(wy, sc, 3)};
             *reinterpret_cast<u32x4*>(lds + row * BK + chunk_slot<8>(row, 2 * g) * 8) = lo;
             *reinterpret_cast<u32x4*>(lds + row * BK + chunk_slot<8>(row, 2 * g + 1) * 8) = hi;
         }
@@ -278,14 +281,17 @@ struct DirectStager {
     static constexpr int RPS = 64 / CPR;         // rows per 1 KB segment
     static constexpr int NW = NT / 64;
     static constexpr int SEGS = ROWS / RPS;
-    static constexpr int PER = SEGS / NW;        // instructions per wave
-    static_assert(PER * NW == SEGS && RPS * CPR == 64, "segments not divisible among waves");
+    // Instructions per wave. When the segments do not divide evenly, the
+    // surplus slots re-load the last segment (the same bytes to the same LDS
+    // place), so every wave issues the same count for the vmcnt bookkeeping.
+    static constexpr int PER = (SEGS + NW - 1) / NW;
+    static_assert(SEGS * RPS == ROWS && RPS * CPR == 64, "whole 1 KB segments");
 
     __device__ __forceinline__ static void issue(const uint16_t* base, int row0, int nrows, int K,
                                                  int k0, uint16_t* lds_tile, int wave, int lane) {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
-            const int seg = wave + j * NW;
+            const int seg = min(wave + j * NW, SEGS - 1);
             const int row = seg * RPS + lane / CPR;
             const int c = chunk_slot<CPR>(row, lane % CPR);
             const int grow = min(row0 + row, nrows - 1);
@@ -654,14 +660,18 @@ gemm_mfma_kernel(KParams p) {
     // fewer registers).
     auto step1 = [&](int t) {
         const uint16_t* sA = smem + (t & 1) * STAGE;
-        if (t + 1 < nsteps) load(sa0, sb0, kb + (t + 1) * BK);
+        // Past the last step the masked loads return zeros without touching
+        // memory and the store lands in a buffer nobody reads again, so both
+        // run unconditionally and stay in one basic block with the MFMAs.
+        load(sa0, sb0, kb + (t + 1) * BK);
+        __builtin_amdgcn_sched_barrier(0);   // keep the loads at the top: their latency spans the step
 #pragma unroll
         for (int kk = 0; kk + 1 < KK; ++kk) {
             const int cur = kk & 1;
             load_frags<FM, FN, TM, TN, BK>(sA, sA + BM * BK, wm, wn, lane, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
+            if (kk == KK - 2) store(sa0, sb0, smem + ((t + 1) & 1) * STAGE);
             mfma_block<FM, FN>(fa[cur], fb[cur], acc);
             interleave_mfma<FM * FN, FM + FN, 0>();
-            if (kk == KK - 2 && t + 1 < nsteps) store(sa0, sb0, smem + ((t + 1) & 1) * STAGE);
         }
         if (t + 1 < nsteps) {
             lds_barrier();
@@ -931,6 +941,9 @@ hipError_t launch_dense_vec(const KParams& kp, int splits, hipStream_t stream) {
                 return launch_direct<128, 128, 64, 2, 2, 1, EPI, true>(kp, splits, stream);
             else
                 return launch_direct<128, 128, 64, 2, 2, 1, EPI>(kp, splits, stream);
+        case 15: return launch_direct<160, 256, 64, 1, 8, 2, EPI>(kp, splits, stream);
+        case 16: return launch_direct<320, 128, 64, 2, 2, 2, EPI>(kp, splits, stream);
+        case 17: return launch_direct<160, 128, 64, 1, 4, 3, EPI>(kp, splits, stream);
         default: return launch_direct<256, 128, 64, 4, 2, 3, EPI>(kp, splits, stream);
     }
 }
@@ -986,8 +999,8 @@ hipError_t launch_fp4(const Fp4Problem& p, hipStream_t stream) {
     switch (cfg) {
         case 1: return launch_cfg<256, 256, 2, 4, EPI_STORE_BF16, SRC_FP4, 2>(kp, 1, stream);
         case 2: return launch_cfg<128, 128, 2, 2, EPI_STORE_BF16, SRC_FP4, 2>(kp, 1, stream);
-        case 3: return launch_cfg<256, 256, 2, 4, EPI_STORE_BF16, SRC_FP4, 1>(kp, 1, stream);
-        default: return launch_cfg<256, 256, 2, 2, EPI_STORE_BF16, SRC_FP4, 1>(kp, 1, stream);
+        case 3: return launch_cfg<256, 256, 2, 2, EPI_STORE_BF16, SRC_FP4, 1>(kp, 1, stream);
+        default: return launch_cfg<256, 256, 2, 4, EPI_STORE_BF16, SRC_FP4, 1>(kp, 1, stream);
     }
 }
 
