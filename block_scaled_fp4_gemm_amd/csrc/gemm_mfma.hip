@@ -55,8 +55,9 @@ struct KParams {
     const uint8_t* SFA;    // e4m3fn [M,K/16]
     const uint8_t* Bq;
     const uint8_t* SFB;
-    void* C;               // bf16 [M,N] or f32 planes [splits][M][N]
+    void* C;               // bf16 [M,N] or f32 planes [splits][M][N], rows ldc elements apart
     int M, N, K;
+    int ldc;               // elements between consecutive rows of C (N, or more for a column range)
     int k_chunk;           // K elements per split (blockIdx.y)
     int tiles_m, tiles_n;
     float scale;
@@ -110,15 +111,17 @@ __device__ __forceinline__ float e4m3fn_to_f32(uint32_t b) {
     return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, mag) | ((b & 0x80u) << 24));
 }
 
-// Workgroup -> (tile_m, tile_n). Dispatch places workgroup b on XCD b % 8;
-// logical ids are assigned so each XCD receives one contiguous range, and the
-// range is walked in grouped order (GROUP_M tile-rows, m fastest).
-__device__ __forceinline__ void tile_of_block(int tiles_m, int tiles_n, int& tm, int& tn) {
-    const int nblocks = tiles_m * tiles_n;
-    const int b = blockIdx.x;
-    const int per = nblocks >> 3, rem = nblocks & 7;
+// Dispatch places workgroup b of an n-workgroup grid on XCD b % 8. The
+// returned logical id gives each XCD one contiguous range of ids.
+__device__ __forceinline__ int xcd_order(int b, int n) {
+    const int per = n >> 3, rem = n & 7;
     const int x = b & 7, j = b >> 3;
-    const int logical = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + j;
+    return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + j;
+}
+
+// Logical tile id -> (tile_m, tile_n) in grouped order: GROUP_M tile-rows at
+// a time, m fastest, so tiles that run together share B columns in L2.
+__device__ __forceinline__ void grouped_tile(int logical, int tiles_m, int tiles_n, int& tm, int& tn) {
     const int width = GROUP_M * tiles_n;
     const int g = logical / width;
     const int first_m = g * GROUP_M;
@@ -126,6 +129,11 @@ __device__ __forceinline__ void tile_of_block(int tiles_m, int tiles_n, int& tm,
     const int r = logical - g * width;
     tm = first_m + r % gsize;
     tn = r / gsize;
+}
+
+// One workgroup per tile: workgroup -> (tile_m, tile_n).
+__device__ __forceinline__ void tile_of_block(int tiles_m, int tiles_n, int& tm, int& tn) {
+    grouped_tile(xcd_order(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
 }
 
 // ---------------------------------------------------------------------------
@@ -369,8 +377,8 @@ __device__ __forceinline__ void mfma_block(const bf16x8 (&fa)[FM], const bf16x8 
 template <int EPI, int FM, int FN, int TM, int TN>
 __device__ __forceinline__ void epilogue(const KParams& p, const f32x16 (&acc)[FM][FN], int m0,
                                          int n0, int wm, int wn, int lane, int split) {
-    const int M = p.M, N = p.N;
-    const bool vec_ok = (N & 3) == 0;
+    const int M = p.M, N = p.N, ldc = p.ldc;
+    const bool vec_ok = (N & 3) == 0 && (ldc & 3) == 0;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         const int m = m0 + wm * TM + i * 32 + (lane & 31);
@@ -382,9 +390,9 @@ __device__ __forceinline__ void epilogue(const KParams& p, const f32x16 (&acc)[F
                 const int n = n0 + wn * TN + j * 32 + g * 8 + (lane >> 5) * 4;
                 const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
                 const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-                const int64_t off = (int64_t)m * N + n;
+                const int64_t off = (int64_t)m * ldc + n;
                 if constexpr (EPI == EPI_STORE_F32) {
-                    float* plane = reinterpret_cast<float*>(p.C) + (int64_t)split * M * N;
+                    float* plane = reinterpret_cast<float*>(p.C) + (int64_t)split * M * ldc;
                     if (vec_ok && n + 3 < N) {
                         *reinterpret_cast<f32x4*>(plane + off) = f32x4{v0, v1, v2, v3};
                     } else {
@@ -465,8 +473,8 @@ __device__ __forceinline__ void staged_epilogue(const KParams& p, const f32x16 (
     static_assert(RP >= 32, "a pass holds at least one 32-row MFMA block");
     constexpr int NPASS = (BM + RP - 1) / RP;
     constexpr int EPC = 16 / ELEM;             // elements per chunk
-    const int M = p.M, N = p.N;
-    const bool vec_ok = (N % EPC) == 0;
+    const int M = p.M, N = p.N, ldc = p.ldc;
+    const bool vec_ok = (N % EPC) == 0 && (ldc % EPC) == 0;
 
     // chunks rotate by the row index, so the 32 rows one store instruction
     // covers spread over the banks for any row length
@@ -508,10 +516,10 @@ __device__ __forceinline__ void staged_epilogue(const KParams& p, const f32x16 (
             const int n = n0 + chunk * EPC;
             if (m >= M || n >= N) continue;
             const u32x4 w = *reinterpret_cast<const u32x4*>(lds + slot(row, chunk));
-            const int64_t off = (int64_t)m * N + n;
+            const int64_t off = (int64_t)m * ldc + n;
             const bool full = vec_ok && n + EPC <= N;
             if constexpr (EPI == EPI_STORE_F32) {
-                float* plane = reinterpret_cast<float*>(p.C) + (int64_t)split * M * N;
+                float* plane = reinterpret_cast<float*>(p.C) + (int64_t)split * M * ldc;
                 if (full) {
                     *reinterpret_cast<u32x4*>(plane + off) = w;
                 } else {
@@ -702,34 +710,23 @@ gemm_mfma_kernel(KParams p) {
 // is multiplied, so STAGES - 1 steps of MFMA work cover the load latency.
 // ---------------------------------------------------------------------------
 
-template <int BM, int BN, int BKS, int WM, int WN, int STAGES, int EPI, bool PREF = false>
-__global__ void __launch_bounds__(WM * WN * 64)
-gemm_mfma_direct_kernel(KParams p) {
+// Multiplies the K range [kb, ke) of the BM x BN tile at (m0, n0) into acc.
+// LDS must be free on entry (the caller's barrier); on return every direct
+// load has landed and LDS may be reused once the workgroup has passed a
+// barrier. `extra` runs right after the prologue's loads are issued and may
+// issue NEXTRA more vector loads per thread that the first wait covers.
+template <int BM, int BN, int BKS, int WM, int WN, int STAGES, int NEXTRA, class Extra>
+__device__ __forceinline__ void direct_mainloop(const KParams& p, uint16_t* smem, int m0, int n0, int kb,
+                                                int ke, int wave, int lane, int tid,
+                                                f32x16 (&acc)[BM / WM / 32][BN / WN / 32], Extra&& extra) {
     constexpr int NT = WM * WN * 64;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
-    static_assert(FM * 32 * WM == BM && FN * 32 * WN == BN, "bad tile split");
-    static_assert(STAGES >= 1, "at least one LDS stage");
     constexpr int STAGE = (BM + BN) * BKS;
     // direct-load instructions one wave issues per step
     constexpr int L = DirectStager<BM, NT, BKS>::PER + DirectStager<BN, NT, BKS>::PER;
-
-    // the prefetching fold stages its whole BF16 tile in one epilogue pass
-    constexpr int SMEM_ELEMS = (PREF && BM * BN > STAGES * STAGE) ? BM * BN : STAGES * STAGE;
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM_ELEMS];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
 
-    int tm, tn;
-    tile_of_block(p.tiles_m, p.tiles_n, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-
-    const int split = blockIdx.y;
-    const int kb = (int)min((int64_t)p.K, (int64_t)split * p.k_chunk);
-    const int ke = (int)min((int64_t)p.K, (int64_t)kb + p.k_chunk);
     // A ragged K remainder (length not a multiple of BKS) is taken as the
     // FIRST step, through the guarded register path; every later step is a
     // whole BKS step loaded directly. The FP32 summation order inside the
@@ -737,9 +734,6 @@ gemm_mfma_direct_kernel(KParams p) {
     // the interface promises.
     const int ragged = (ke - kb) % BKS;
     const int nsteps = (ke - kb) / BKS + (ragged ? 1 : 0);
-
-    f32x16 acc[FM][FN];
-    zero_acc(acc);
 
     auto issue = [&](int k0, uint16_t* buf) {
         DirectStager<BM, NT, BKS>::issue(p.A, m0, p.M, p.K, k0, buf, wave, lane);
@@ -773,26 +767,8 @@ gemm_mfma_direct_kernel(KParams p) {
             k_next += BKS;
         }
     }
-    // Fused fold with a short K: the workgroup's `out` tile is fetched now,
-    // in the same 16-byte pieces the epilogue's row-streaming assigns to
-    // this thread, so its HBM latency overlaps the operand loads and MFMAs.
-    constexpr int PCPR = BN * 2 / 16;
-    constexpr int NPRE = PREF ? (BM * PCPR + NT - 1) / NT : 0;
-    static_assert(!PREF || EPI == EPI_SCALED_ACC, "prefetch is for the fold epilogue");
-    u32x4 pre[NPRE > 0 ? NPRE : 1];
-    if constexpr (PREF) {
-        const uint16_t* O = reinterpret_cast<const uint16_t*>(p.C);
-        const bool vec_ok = (p.N & 7) == 0;
-#pragma unroll
-        for (int it = 0; it < NPRE; ++it) {
-            const int q = tid + it * NT;
-            const int row = q / PCPR, chunk = q % PCPR;
-            const int m = m0 + row, n = n0 + chunk * 8;
-            if (q < BM * PCPR && m < p.M && vec_ok && n + 8 <= p.N)
-                pre[it] = *reinterpret_cast<const u32x4*>(O + (int64_t)m * p.N + n);
-        }
-    }
-    wait_vmcnt<(STAGES - 1) * L + NPRE>();
+    extra();
+    wait_vmcnt<(STAGES - 1) * L + NEXTRA>();
     lds_barrier();
 
     // Sub-step kk of a step multiplies fragments loaded during sub-step kk-1
@@ -833,6 +809,61 @@ gemm_mfma_direct_kernel(KParams p) {
         mfma_block<FM, FN>(fa[LAST], fb[LAST], acc);
     }
     wait_vmcnt<0>();   // drain the re-loads past the end before LDS is reused or the wave exits
+}
+
+template <int BM, int BN, int BKS, int WM, int WN, int STAGES, int EPI, bool PREF = false>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_mfma_direct_kernel(KParams p) {
+    constexpr int NT = WM * WN * 64;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    static_assert(FM * 32 * WM == BM && FN * 32 * WN == BN, "bad tile split");
+    static_assert(STAGES >= 1, "at least one LDS stage");
+    constexpr int STAGE = (BM + BN) * BKS;
+
+    // the prefetching fold stages its whole BF16 tile in one epilogue pass
+    constexpr int SMEM_ELEMS = (PREF && BM * BN > STAGES * STAGE) ? BM * BN : STAGES * STAGE;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM_ELEMS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+
+    int tm, tn;
+    tile_of_block(p.tiles_m, p.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int split = blockIdx.y;
+    const int kb = (int)min((int64_t)p.K, (int64_t)split * p.k_chunk);
+    const int ke = (int)min((int64_t)p.K, (int64_t)kb + p.k_chunk);
+
+    f32x16 acc[FM][FN];
+    zero_acc(acc);
+
+    // Fused fold with a short K: the workgroup's `out` tile is fetched while
+    // the operand loads are in flight, in the same 16-byte pieces the
+    // epilogue's row-streaming assigns to this thread, so its HBM latency
+    // overlaps the operand loads and MFMAs.
+    constexpr int PCPR = BN * 2 / 16;
+    constexpr int NPRE = PREF ? (BM * PCPR + NT - 1) / NT : 0;
+    static_assert(!PREF || EPI == EPI_SCALED_ACC, "prefetch is for the fold epilogue");
+    u32x4 pre[NPRE > 0 ? NPRE : 1];
+    direct_mainloop<BM, BN, BKS, WM, WN, STAGES, NPRE>(
+        p, smem, m0, n0, kb, ke, wave, lane, tid, acc, [&]() {
+            if constexpr (PREF) {
+                const uint16_t* O = reinterpret_cast<const uint16_t*>(p.C);
+                const bool vec_ok = (p.N & 7) == 0 && (p.ldc & 7) == 0;
+#pragma unroll
+                for (int it = 0; it < NPRE; ++it) {
+                    const int q = tid + it * NT;
+                    const int row = q / PCPR, chunk = q % PCPR;
+                    const int m = m0 + row, n = n0 + chunk * 8;
+                    if (q < BM * PCPR && m < p.M && vec_ok && n + 8 <= p.N)
+                        pre[it] = *reinterpret_cast<const u32x4*>(O + (int64_t)m * p.ldc + n);
+                }
+            }
+        });
 
     staged_epilogue<EPI, BM, BN, WM, WN, FM, FN, NT, SMEM_ELEMS * 2, NPRE>(
         p, acc, reinterpret_cast<uint8_t*>(smem), m0, n0, wm, wn, lane, tid, split, pre);
@@ -864,51 +895,16 @@ hipError_t launch_direct(const KParams& kp, int splits, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Tile configuration for the BF16 paths. `BLOCKGEMM_TILE` (tuning only)
-// forces one of the table entries below.
-int forced_tile() {
-    const char* e = getenv("BLOCKGEMM_TILE");
+// Tuning hooks (environment): `BLOCKGEMM_TILE` forces one of the table
+// entries below for the whole problem; `BLOCKGEMM_SPLIT=0` turns the column
+// split off.
+int env_int(const char* name) {
+    const char* e = getenv(name);
     return e ? atoi(e) : -1;
 }
 
-// Shape -> tile choice. Tiles are scheduled in rounds of (CUs x blocks per
-// CU); the estimate is rounds x (blocks per CU) x tile area / measured
-// sustained rate of that configuration with every CU busy (TFLOP/s on
-// MI355X, random BF16 operands). Problems with a tiny K are bound by the
-// output traffic, where the narrower 160x128 tile streams best.
-struct TileChoice {
-    int cfg, bm, bn, occ;
-    double rate;
-};
-constexpr TileChoice kTileChoices[] = {
-    {2, 256, 256, 1, 1096.0},
-    {8, 160, 256, 1, 972.0},
-    {9, 160, 128, 2, 884.0},
-    {6, 128, 128, 2, 808.0},
-};
-
-int choose_tile(int M, int N, int K, int splits, int cus, int epi) {
-    if (K <= 128) return epi == EPI_SCALED_ACC ? 11 : 9;
-    int best = 2;
-    double best_t = 1e300;
-    for (const TileChoice& c : kTileChoices) {
-        const double tiles = (double)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn) * splits;
-        const double slots = (double)cus * c.occ;
-        const double rounds = tiles <= cus ? 1.0 : (double)(int64_t)((tiles + slots - 1) / slots);
-        const double occ = tiles <= cus ? 1.0 : c.occ;
-        const double t = rounds * occ * c.bm * c.bn / c.rate;
-        if (t < best_t) {
-            best_t = t;
-            best = c.cfg;
-        }
-    }
-    return best;
-}
-
 template <int EPI>
-hipError_t launch_dense_vec(const KParams& kp, int splits, hipStream_t stream) {
-    int cfg = forced_tile();
-    if (cfg < 0) cfg = choose_tile(kp.M, kp.N, kp.K, splits, kp.cus, EPI);
+hipError_t launch_tile_cfg(const KParams& kp, int splits, int cfg, hipStream_t stream) {
     switch (cfg) {
         //                                  BM   BN  BK WM WN ST
         case 0: return launch_cfg<128, 128, 2, 2, EPI, SRC_BF16_VEC>(kp, splits, stream);
@@ -944,8 +940,106 @@ hipError_t launch_dense_vec(const KParams& kp, int splits, hipStream_t stream) {
         case 15: return launch_direct<160, 256, 64, 1, 8, 2, EPI>(kp, splits, stream);
         case 16: return launch_direct<320, 128, 64, 2, 2, 2, EPI>(kp, splits, stream);
         case 17: return launch_direct<160, 128, 64, 1, 4, 3, EPI>(kp, splits, stream);
-        default: return launch_direct<256, 128, 64, 4, 2, 3, EPI>(kp, splits, stream);
+        default: return launch_direct<256, 128, 64, 4, 2, 3, EPI>(kp, splits, stream);   // 10
     }
+}
+
+// Shape -> schedule. Time estimates in microseconds use the measured
+// sustained rate of each configuration with every CU busy (TFLOP/s on
+// MI355X, random BF16 operands); tiles run in rounds of (CUs x blocks per
+// CU). Problems with a tiny K are bound by the output traffic, where the
+// narrower 160x128 tile streams best.
+//
+// Column split: when the last round of 256x256 tiles would be poorly filled
+// (860 tiles on 256 CUs: the fourth round a third full), the first n1 columns
+// run as whole rounds of 256x256 tiles and the remaining columns as a second
+// launch with the tile that finishes them fastest (usually one round of a
+// half-size tile). Every output is still produced by one tile walking K in
+// the same order, so the result is bit-identical to the unsplit launch.
+struct TileChoice {
+    int cfg, bm, bn, occ;
+    double rate;
+};
+constexpr TileChoice kTileChoices[] = {
+    {2, 256, 256, 1, 1096.0},
+    {8, 160, 256, 1, 972.0},
+    {10, 256, 128, 1, 900.0},
+    {9, 160, 128, 2, 884.0},
+    {6, 128, 128, 2, 808.0},
+};
+constexpr double kLaunchGapUs = 2.0;   // second launch of a column split
+
+struct Schedule {
+    int cfg;       // configuration of columns [0, n1)
+    int n1;        // == N: no split
+    int cfg2;      // configuration of columns [n1, N)
+};
+
+double dp_us(const TileChoice& c, int M, int N, int K, int splits, int cus) {
+    const double tiles = (double)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn) * splits;
+    const double slots = (double)cus * c.occ;
+    const double rounds = tiles <= cus ? 1.0 : (double)(int64_t)((tiles + slots - 1) / slots);
+    const double occ = tiles <= cus ? 1.0 : c.occ;
+    return rounds * occ * 2.0 * c.bm * c.bn * ((double)K / splits) * cus / (c.rate * 1e6);
+}
+
+const TileChoice* best_single(int M, int N, int K, int splits, int cus, double* t_out) {
+    const TileChoice* best = &kTileChoices[0];
+    double best_t = 1e300;
+    for (const TileChoice& c : kTileChoices) {
+        const double t = dp_us(c, M, N, K, splits, cus);
+        if (t < best_t) {
+            best_t = t;
+            best = &c;
+        }
+    }
+    *t_out = best_t;
+    return best;
+}
+
+Schedule choose_schedule(int M, int N, int K, int splits, int cus, int epi) {
+    if (K <= 128) {
+        const int cfg = epi == EPI_SCALED_ACC ? 11 : 9;
+        return {cfg, N, cfg};
+    }
+    double best_t;
+    const TileChoice* one = best_single(M, N, K, splits, cus, &best_t);
+    Schedule best{one->cfg, N, one->cfg};
+    if (epi != EPI_STORE_BF16 || splits != 1) return best;
+    const TileChoice& big = kTileChoices[0];
+    for (int c1 = 1; c1 * big.bn < N; ++c1) {
+        const int n1 = c1 * big.bn;
+        double t2;
+        const TileChoice* rest = best_single(M, N - n1, K, 1, cus, &t2);
+        const double t = dp_us(big, M, n1, K, 1, cus) + t2 + kLaunchGapUs;
+        if (t < best_t) {
+            best_t = t;
+            best = {big.cfg, n1, rest->cfg};
+        }
+    }
+    return best;
+}
+
+template <int EPI>
+hipError_t launch_dense_vec(const KParams& kp, int splits, hipStream_t stream) {
+    const int forced = env_int("BLOCKGEMM_TILE");
+    if (forced >= 0) return launch_tile_cfg<EPI>(kp, splits, forced, stream);
+    Schedule sch = choose_schedule(kp.M, kp.N, kp.K, splits, kp.cus, EPI);
+    if (env_int("BLOCKGEMM_SPLIT") == 0 && sch.n1 < kp.N) {
+        double t;
+        sch = {best_single(kp.M, kp.N, kp.K, splits, kp.cus, &t)->cfg, kp.N, 0};
+    }
+    if (sch.n1 >= kp.N) return launch_tile_cfg<EPI>(kp, splits, sch.cfg, stream);
+    // columns [0, n1), then [n1, N) of the same C (row stride ldc)
+    KParams left = kp;
+    left.N = sch.n1;
+    hipError_t e = launch_tile_cfg<EPI>(left, splits, sch.cfg, stream);
+    if (e != hipSuccess) return e;
+    KParams right = kp;
+    right.B = kp.B + (int64_t)sch.n1 * kp.K;
+    right.C = reinterpret_cast<uint16_t*>(kp.C) + sch.n1;
+    right.N = kp.N - sch.n1;
+    return launch_tile_cfg<EPI>(right, splits, sch.cfg2, stream);
 }
 
 template <int EPI, int SRC>
@@ -964,6 +1058,7 @@ hipError_t launch_dense(const DenseProblem& p, Epilogue epi, hipStream_t stream)
     kp.M = (int)p.M;
     kp.N = (int)p.N;
     kp.K = (int)p.K;
+    kp.ldc = (int)p.N;
     kp.k_chunk = (int)p.k_chunk;
     kp.scale = p.scale;
     kp.cus = p.cus > 0 ? (int)p.cus : 256;
@@ -993,6 +1088,7 @@ hipError_t launch_fp4(const Fp4Problem& p, hipStream_t stream) {
     kp.M = (int)p.M;
     kp.N = (int)p.N;
     kp.K = (int)p.K;
+    kp.ldc = (int)p.N;
     kp.k_chunk = (int)p.K;
     const char* e = getenv("BLOCKGEMM_FP4_TILE");   // tuning only
     const int cfg = e ? atoi(e) : 0;
