@@ -37,9 +37,10 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -99,17 +100,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
-
-// E4M3FN byte -> FP32 (exact): bias 7, subnormal m*2^-9, S.1111.111 = NaN.
-// Written with selects only, so it stays in straight-line code.
-__device__ __forceinline__ float e4m3fn_to_f32(uint32_t b) {
-    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-    const float normal = __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20));
-    const float subnormal = (float)m * 0x1p-9f;
-    float mag = e != 0u ? normal : subnormal;
-    mag = (b & 0x7Fu) == 0x7Fu ? __builtin_nanf("") : mag;
-    return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, mag) | ((b & 0x80u) << 24));
-}
 
 // Dispatch places workgroup b of an n-workgroup grid on XCD b % 8. The
 // returned logical id gives each XCD one contiguous range of ids.
@@ -217,9 +207,13 @@ struct Stager<ROWS, NT, SRC_BF16_SCALAR, BKS> {
 };
 
 // Block-scaled FP4: a unit is one 16-element scale group of one row (8 packed
-// bytes + 1 scale byte); it is dequantized exactly to BF16 while being written
-// to LDS as two 16-byte chunks. e2m1 * e4m3 has at most 6 significant bits,
-// so the FP32 product and its BF16 conversion are exact.
+// bytes + 1 scale byte); it is dequantized exactly to FP16 while being written
+// to LDS as two 16-byte chunks, for the FP16 MFMA. Every e2m1 value and every
+// e4m3 scale is exact in FP16, and so is their product: at most 6 significant
+// bits, magnitude between 2^-10 and 2688 (or zero, or NaN from a NaN scale).
+// So the packed FP16 multiply rounds nothing, and the operands the MFMA sees
+// are exactly the dequantized values: one conversion and half a packed
+// multiply per element.
 template <int ROWS, int NT>
 struct Stager<ROWS, NT, SRC_FP4, BK> {
     static constexpr int PER = ROWS * (BK / 16) / NT;
@@ -246,15 +240,18 @@ struct Stager<ROWS, NT, SRC_FP4, BK> {
         }
     }
 
-    __device__ __forceinline__ static uint32_t deq2(uint32_t word, float sc, int byte) {
-        f32x2 v;
+    // Two e2m1 values (byte `byte` of word: low nibble first) times the scale
+    // in the low half of sc2, as packed FP16.
+    __device__ __forceinline__ static uint32_t deq2(uint32_t word, f16x2 sc2, int byte) {
+        f16x2 v;
         switch (byte) {   // byte select must be an immediate
-            case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0); break;
-            case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1); break;
-            case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2); break;
-            default: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3); break;
+            case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0); break;
+            case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1); break;
+            case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2); break;
+            default: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3); break;
         }
-        return pack_bf16x2(v.x * sc, v.y * sc);
+        const f16x2 sc = {sc2.x, sc2.x};
+        return __builtin_bit_cast(uint32_t, v * sc);   // v_pk_mul_f16, exact
     }
 
     __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
@@ -264,7 +261,9 @@ struct Stager<ROWS, NT, SRC_FP4, BK> {
             const int row = u >> 2, g = u & 3;
             const bool in = (valid >> i) & 1u;
             const uint32_t wx = in ? w[i].x : 0u, wy = in ? w[i].y : 0u;
-            const float sc = e4m3fn_to_f32(in ? s[i] : 0u);
+            // e4m3fn byte -> FP16 (exact, NaN stays NaN); a unit past the K
+            // range gets scale 0 and zero data
+            const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(in ? s[i] : 0u, 1.0f, false);
             const u32x4 lo = {deq2(wx, sc, 0), deq2(wx, sc, 1), deq2(wx, sc, 2), deq2(wx, sc, 3)};
             const u32x4 hi = {deq2(wy, sc, 0), deq2(wy, sc, 1), deq2(wy, sc, 2), deq2(wy, sc, 3)};
             *reinterpret_cast<u32x4*>(lds + row * BK + chunk_slot<8>(row, 2 * g) * 8) = lo;
@@ -362,14 +361,22 @@ __device__ __forceinline__ void load_frags(const uint16_t* sA, const uint16_t* s
     }
 }
 
-template <int FM, int FN>
+// F16: the fragments hold FP16 bit patterns (dequantized FP4), multiplied with
+// the FP16 MFMA of the same shape and rate.
+template <int FM, int FN, bool F16 = false>
 __device__ __forceinline__ void mfma_block(const bf16x8 (&fa)[FM], const bf16x8 (&fb)[FN],
                                            f32x16 (&acc)[FM][FN]) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < FN; ++j) {
+            if constexpr (F16)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, fb[j]),
+                                                                   __builtin_bit_cast(f16x8, fa[i]), acc[i][j], 0,
+                                                                   0, 0);
+            else
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+        }
 }
 
 // acc[i][j][4g + e] is C[m][n + e] with
@@ -580,7 +587,7 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[FM][FN]) {
 // Kernel 1: register-staged operands (FP4 with in-register dequantization,
 // and BF16 rows whose pitch is not a multiple of 16 bytes). Global loads go
 // to registers two steps ahead (two register sets, loop unrolled by two);
-// during step t the set holding step t+1 is converted (FP4 -> exact BF16)
+// during step t the set holding step t+1 is converted (FP4 -> exact FP16)
 // and written into the LDS buffer that step t-1 released, interleaved with
 // step t's MFMAs. Same MFMA / LDS-read interleave, step barrier placement
 // and LDS-staged epilogue as kernel 2.
@@ -650,7 +657,7 @@ gemm_mfma_kernel(KParams p) {
         for (int kk = 0; kk + 1 < KK; ++kk) {
             const int cur = kk & 1;
             load_frags<FM, FN, TM, TN, BK>(sA, sA + BM * BK, wm, wn, lane, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
-            mfma_block<FM, FN>(fa[cur], fb[cur], acc);
+            mfma_block<FM, FN, SRC == SRC_FP4>(fa[cur], fb[cur], acc);
             interleave_mfma<FM * FN, FM + FN, 0>();
             if (kk == 0 && t + 1 < nsteps) store(held_a, held_b, smem + ((t + 1) & 1) * STAGE);
         }
@@ -659,7 +666,7 @@ gemm_mfma_kernel(KParams p) {
             const uint16_t* nA = smem + ((t + 1) & 1) * STAGE;
             load_frags<FM, FN, TM, TN, BK>(nA, nA + BM * BK, wm, wn, lane, 0, fa[LAST ^ 1], fb[LAST ^ 1]);
         }
-        mfma_block<FM, FN>(fa[LAST], fb[LAST], acc);
+        mfma_block<FM, FN, SRC == SRC_FP4>(fa[LAST], fb[LAST], acc);
         interleave_mfma<FM * FN, FM + FN, 0>();
     };
 
@@ -678,7 +685,7 @@ gemm_mfma_kernel(KParams p) {
             const int cur = kk & 1;
             load_frags<FM, FN, TM, TN, BK>(sA, sA + BM * BK, wm, wn, lane, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
             if (kk == KK - 2) store(sa0, sb0, smem + ((t + 1) & 1) * STAGE);
-            mfma_block<FM, FN>(fa[cur], fb[cur], acc);
+            mfma_block<FM, FN, SRC == SRC_FP4>(fa[cur], fb[cur], acc);
             interleave_mfma<FM * FN, FM + FN, 0>();
         }
         if (t + 1 < nsteps) {
@@ -686,7 +693,7 @@ gemm_mfma_kernel(KParams p) {
             const uint16_t* nA = smem + ((t + 1) & 1) * STAGE;
             load_frags<FM, FN, TM, TN, BK>(nA, nA + BM * BK, wm, wn, lane, 0, fa[LAST ^ 1], fb[LAST ^ 1]);
         }
-        mfma_block<FM, FN>(fa[LAST], fb[LAST], acc);
+        mfma_block<FM, FN, SRC == SRC_FP4>(fa[LAST], fb[LAST], acc);
         interleave_mfma<FM * FN, FM + FN, 0>();
     };
 
