@@ -721,7 +721,10 @@ gemm_mfma_kernel(KParams p) {
 // LDS must be free on entry (the caller's barrier); on return every direct
 // load has landed and LDS may be reused once the workgroup has passed a
 // barrier. `extra` runs right after the prologue's loads are issued and may
-// issue NEXTRA more vector loads per thread that the first wait covers.
+// issue up to NEXTRA more vector load instructions per wave; it returns true
+// (uniformly) only when every wave issued exactly NEXTRA, which lets the
+// first wait leave them in flight. Otherwise the first wait counts none of
+// them and so also waits for whichever were issued.
 template <int BM, int BN, int BKS, int WM, int WN, int STAGES, int NEXTRA, class Extra>
 __device__ __forceinline__ void direct_mainloop(const KParams& p, uint16_t* smem, int m0, int n0, int kb,
                                                 int ke, int wave, int lane, int tid,
@@ -774,8 +777,10 @@ __device__ __forceinline__ void direct_mainloop(const KParams& p, uint16_t* smem
             k_next += BKS;
         }
     }
-    extra();
-    wait_vmcnt<(STAGES - 1) * L + NEXTRA>();
+    if (extra())
+        wait_vmcnt<(STAGES - 1) * L + NEXTRA>();
+    else
+        wait_vmcnt<(STAGES - 1) * L>();
     lds_barrier();
 
     // Sub-step kk of a step multiplies fragments loaded during sub-step kk-1
@@ -853,8 +858,11 @@ gemm_mfma_direct_kernel(KParams p) {
     // epilogue's row-streaming assigns to this thread, so its HBM latency
     // overlaps the operand loads and MFMAs.
     constexpr int PCPR = BN * 2 / 16;
-    constexpr int NPRE = PREF ? (BM * PCPR + NT - 1) / NT : 0;
+    constexpr int NPRE = PREF ? BM * PCPR / NT : 0;
     static_assert(!PREF || EPI == EPI_SCALED_ACC, "prefetch is for the fold epilogue");
+    // every thread has a piece in every prefetch round, so on an interior
+    // tile each wave issues exactly NPRE loads
+    static_assert(!PREF || NPRE * NT == BM * PCPR, "prefetch rounds cover the tile exactly");
     u32x4 pre[NPRE > 0 ? NPRE : 1];
     direct_mainloop<BM, BN, BKS, WM, WN, STAGES, NPRE>(
         p, smem, m0, n0, kb, ke, wave, lane, tid, acc, [&]() {
@@ -866,10 +874,13 @@ gemm_mfma_direct_kernel(KParams p) {
                     const int q = tid + it * NT;
                     const int row = q / PCPR, chunk = q % PCPR;
                     const int m = m0 + row, n = n0 + chunk * 8;
-                    if (q < BM * PCPR && m < p.M && vec_ok && n + 8 <= p.N)
+                    if (m < p.M && vec_ok && n + 8 <= p.N)
                         pre[it] = *reinterpret_cast<const u32x4*>(O + (int64_t)m * p.ldc + n);
                 }
+                // edge tiles skip some prefetch loads: uniform per workgroup
+                return vec_ok && m0 + BM <= p.M && n0 + BN <= p.N;
             }
+            return true;
         });
 
     staged_epilogue<EPI, BM, BN, WM, WN, FM, FN, NT, SMEM_ELEMS * 2, NPRE>(
@@ -944,6 +955,21 @@ hipError_t launch_tile_cfg(const KParams& kp, int splits, int cfg, hipStream_t s
                 return launch_direct<128, 128, 64, 2, 2, 1, EPI, true>(kp, splits, stream);
             else
                 return launch_direct<128, 128, 64, 2, 2, 1, EPI>(kp, splits, stream);
+        case 18:
+        case 19:
+        case 20:
+        case 21:
+        case 22:
+            // single-stage prefetching tiles for the fold (K of one step)
+            if constexpr (EPI == EPI_SCALED_ACC) {
+                if (cfg == 18) return launch_direct<64, 128, 64, 2, 2, 1, EPI, true>(kp, splits, stream);
+                if (cfg == 19) return launch_direct<64, 256, 64, 1, 4, 1, EPI, true>(kp, splits, stream);
+                if (cfg == 20) return launch_direct<32, 256, 64, 1, 4, 1, EPI, true>(kp, splits, stream);
+                if (cfg == 21) return launch_direct<128, 256, 64, 2, 4, 1, EPI, true>(kp, splits, stream);
+                return launch_direct<64, 128, 64, 1, 2, 1, EPI, true>(kp, splits, stream);
+            } else {
+                return launch_direct<160, 128, 64, 1, 4, 2, EPI>(kp, splits, stream);
+            }
         case 15: return launch_direct<160, 256, 64, 1, 8, 2, EPI>(kp, splits, stream);
         case 16: return launch_direct<320, 128, 64, 2, 2, 2, EPI>(kp, splits, stream);
         case 17: return launch_direct<160, 128, 64, 1, 4, 3, EPI>(kp, splits, stream);
@@ -954,8 +980,7 @@ hipError_t launch_tile_cfg(const KParams& kp, int splits, int cfg, hipStream_t s
 // Shape -> schedule. Time estimates in microseconds use the measured
 // sustained rate of each configuration with every CU busy (TFLOP/s on
 // MI355X, random BF16 operands); tiles run in rounds of (CUs x blocks per
-// CU). Problems with a tiny K are bound by the output traffic, where the
-// narrower 160x128 tile streams best.
+// CU). Problems with a tiny K are bound by the output traffic.
 //
 // Column split: when the last round of 256x256 tiles would be poorly filled
 // (860 tiles on 256 CUs: the fourth round a third full), the first n1 columns
@@ -1006,7 +1031,10 @@ const TileChoice* best_single(int M, int N, int K, int splits, int cus, double* 
 
 Schedule choose_schedule(int M, int N, int K, int splits, int cus, int epi) {
     if (K <= 128) {
-        const int cfg = epi == EPI_SCALED_ACC ? 11 : 9;
+        // Output-bound: the fold streams `out` best with small single-stage
+        // prefetching tiles (64x128: up to six workgroups per CU), a plain
+        // short-K product with the narrow 160x128 tile.
+        const int cfg = epi == EPI_SCALED_ACC ? 18 : 9;
         return {cfg, N, cfg};
     }
     double best_t;

@@ -126,6 +126,31 @@ def test_scaled_acc_worked_cases_on_gpu():
     assert int(_fold(out, x, b, float(np.float32(1 + 2.0 ** -22)))[0, 0]) == 0x3F80
 
 
+FOLD_PREFETCH_CFGS = [11, 12, 13, 14, 18, 19, 20, 21, 22]
+
+
+@pytest.mark.parametrize("cfg", FOLD_PREFETCH_CFGS)
+def test_fold_edge_tiles_every_prefetch_config(cfg, monkeypatch):
+    """Edge tiles (rows past M, N not a multiple of 8, ragged columns) skip
+    part of the early `out` prefetch; the operand tiles must still be in LDS
+    before the MFMAs read them. Each case runs ten times, and every result
+    must equal the exact one (grid inputs: the delta is exact in FP32)."""
+    monkeypatch.setenv("BLOCKGEMM_TILE", str(cfg))
+    for m, n, k in [(33, 70, 64), (7, 300, 64), (130, 66, 64), (100, 1000, 32), (65, 136, 128)]:
+        print(f"fold cfg={cfg} m={m} n={n} k={k}", flush=True)
+        out = synthetic.normal_bf16((m, n), 1.0, 80 + cfg, 2)
+        x = synthetic.grid_bf16((m, k), -8, 8, -5, 81, 0)
+        b = synthetic.grid_bf16((n, k), -8, 8, -5, 81, 1)
+        want = oracle.gemm_scaled_acc_exact(out, x, b, 2.0)
+        dx, db = to_dev_bf16(x), to_dev_bf16(b)
+        outs = [to_dev_bf16(out) for _ in range(10)]
+        for o in outs:
+            bg.gemm_bf16_scaled_acc(dx, db, o, 2.0)
+        torch.cuda.synchronize()
+        for r, o in enumerate(outs):
+            assert_bits_equal(bits_of(o), want, f"fold cfg {cfg} {m}x{n}x{k} run {r}")
+
+
 # ---------------------------------------------------------------------------
 # order-preserving mode
 # ---------------------------------------------------------------------------
