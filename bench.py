@@ -165,7 +165,8 @@ def main():
 
     roofline = {
         "bound": "mfma",
-        "kernel": "gemm_mfma_direct_kernel, 256x256 tile (gemm_bf16, MLP gate/up 5120x11008x2048)",
+        "kernel": ("gemm_bf16 MLP gate/up call 5120x11008x2048 (per call): gemm_mfma_direct_kernel 256x256 "
+                   "tiles over columns 0-9471, then 256x128 tiles over 9472-11007"),
         "achieved": round(achieved, 1),
         "peak": BF16_PEAK_TFLOPS,
         "unit": "TFLOP/s",
@@ -211,8 +212,9 @@ def main():
 
 
 def traffic_for_current_kernel():
-    """HBM bytes per gate/up launch from the committed counter summary, or None
-    if the GEMM kernel source changed since the counters were taken."""
+    """HBM bytes per gate/up call (both dispatches) from the committed counter
+    summary, or None if the GEMM kernel source changed since the counters
+    were taken."""
     path = os.path.join(ROOT, "profiles", "traffic_gate_up.json")
     src = os.path.join(ROOT, "block_scaled_fp4_gemm_amd", "csrc", "gemm_mfma.hip")
     try:
