@@ -27,6 +27,8 @@ from .gemm import (  # noqa: F401
     gemm_ordered_f32,
     gemm_scaled_acc_exact,
     gemm_splitk_planes_ref,
+    gemm_w4a16_exact,
+    gemm_w4a16_ref,
     rms,
     scaled_acc_candidates,
     scaled_acc_epilogue,

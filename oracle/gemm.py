@@ -208,3 +208,32 @@ def gemm_fp4_ref(a_packed, sfa, b_packed, sfb) -> np.ndarray:
     a = dequant_fp4(a_packed, sfa)
     b = dequant_fp4(b_packed, sfb)
     return a @ b.T
+
+
+def gemm_w4a16_ref(a_bits, b_packed, sfb, scale_2) -> np.ndarray:
+    """ref[i, j] = s2 * sum_k A[i, k] * deq(B)[j, k] in FP64, s2 = fl32(scale_2).
+
+    gemm_dense.rs page, w4a16_gemm doc comment: C = A @ dequant(B) with A
+    [M, K] BF16 activations and B NVFP4 weights: E2M1 values, one FP8 (E4M3)
+    scale per 16 K elements and one FP32 per-tensor scale. The page's
+    lossless BF16-MMA variant forms each dequantized weight exactly in BF16,
+    which fixes the reading: deq(B) = e2m1 * e4m3 (exact, the same per-group
+    dequantization as the FP4 GEMM), and the per-tensor scale multiplies the
+    FP32 dot product once, before the BF16 output rounding. B is [N, K/2]
+    bytes (low nibble = even k), its scales [N, K/16].
+    """
+    s2 = float(np.float32(scale_2))
+    return s2 * (bf16_to_f64(a_bits) @ dequant_fp4(b_packed, sfb).T)
+
+
+def gemm_w4a16_exact(a_bits, b_packed, sfb, scale_2) -> np.ndarray:
+    """BF16 C = bf16(fl32(s2 * acc)) for inputs whose dot products acc are
+    exact in FP32 whatever the summation order (the caller picks such data,
+    e.g. grid activations and power-of-two scales). Raises ValueError if a
+    dot product is not even representable in FP32."""
+    acc = bf16_to_f64(a_bits) @ dequant_fp4(b_packed, sfb).T
+    acc32 = acc.astype(np.float32)
+    if not np.array_equal(acc32.astype(np.float64), acc):
+        raise ValueError("dot products are not exact in FP32")
+    prod = np.float32(scale_2) * acc32        # one IEEE single multiply, RNE
+    return f32_to_bf16(prod.astype(np.float32))

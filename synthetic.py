@@ -18,7 +18,9 @@ pages measure:
     n = 17408) and dense_gemm_router (router at M = 4510 and 2255, [M,2048] x
     [2048,256]);
   - kernelbot NVFP4 GEMM page (submission 123329), "SCALE FACTORS" section:
-    E2M1 elements with one E4M3 scale per 16 K elements.
+    E2M1 elements with one E4M3 scale per 16 K elements;
+  - gemm_dense.rs page, w4a16_gemm doc comments: BF16 activations times NVFP4
+    weights, measured at the qkvz projection (K = 2048, N = 12288, ISL 1016).
 """
 from __future__ import annotations
 
@@ -139,3 +141,19 @@ def fp4_gemm(seed: int = 4, m: int = 4096, n: int = 4096, k: int = 8192):
     sfa = e4m3_uniform(m, k // 16, 2.0 ** -4, 2.0 ** 4, seed, TID_SFA)
     sfb = e4m3_uniform(n, k // 16, 2.0 ** -4, 2.0 ** 4, seed, TID_SFB)
     return a, sfa, b, sfb
+
+
+# Per-tensor FP32 scale of the W4A16 weights (an arbitrary non-power-of-two
+# value of the size an NVFP4 global scale takes).
+W4A16_SCALE_2 = 0.0123
+
+
+def w4a16_gemm(seed: int = 5, m: int = 1016, n: int = 12288, k: int = 2048):
+    """W4A16: BF16 activations A[m,k] ~ N(0,1); NVFP4 weights B[n,k/2]
+    (uniform bytes) with E4M3FN scales U(2^-4, 2^4) per 16 K elements, and the
+    per-tensor FP32 scale W4A16_SCALE_2. Default shape: the gemm_dense.rs
+    page's qkvz projection (K = 2048, N = 12288) at ISL = 1016."""
+    a = normal_bf16((m, k), 1.0, seed, TID_A)
+    b = fp4_packed(n, k, seed, TID_B)
+    sfb = e4m3_uniform(n, k // 16, 2.0 ** -4, 2.0 ** 4, seed, TID_SFB)
+    return a, b, sfb, W4A16_SCALE_2

@@ -325,3 +325,95 @@ def test_fp4_power_of_two_scales_exact_in_fp32():
     ref = oracle.gemm_fp4_ref(a, sfa, b, sfb)
     assert np.array_equal(ref, ref.astype(np.float32).astype(np.float64))
     assert np.array_equal(ref * 4, np.round(ref * 4))
+
+
+# ---------------------------------------------------------------------------
+# W4A16 (BF16 activations x NVFP4 weights with a per-tensor scale)
+# ---------------------------------------------------------------------------
+
+def _e4m3_exact(byte: int) -> Fraction:
+    """E4M3FN from its bit fields (bias 7, subnormal m * 2^-9); finite codes only."""
+    s, e, m = byte >> 7, (byte >> 3) & 15, byte & 7
+    v = Fraction(m, 8) * Fraction(2) ** -6 if e == 0 else Fraction(8 + m, 8) * Fraction(2) ** (e - 7)
+    return -v if s else v
+
+
+def test_w4a16_brute_force_exact_rationals():
+    tab = _e2m1_table()
+    m, n, k = 3, 5, 48
+    a = rand_bf16((m, k), 90)
+    b = synthetic.fp4_packed(n, k, 90, 1)
+    sfb = synthetic.e4m3_uniform(n, k // 16, 2 ** -4, 2 ** 4, 90, 5)
+    s2 = 0.0123
+    s2_exact = Fraction(struct.unpack("<f", struct.pack("<f", s2))[0])
+    got = oracle.gemm_w4a16_ref(a, b, sfb, s2)
+    for i in range(m):
+        for j in range(n):
+            dot = Fraction(0)
+            for kk in range(k):
+                byte = int(b[j, kk // 2])
+                code = byte & 0xF if kk % 2 == 0 else byte >> 4
+                dot += bf16_exact(int(a[i, kk])) * tab[code] * _e4m3_exact(int(sfb[j, kk // 16]))
+            exact = s2_exact * dot
+            # the FP64 dot product is exact here; only the final product rounds
+            assert abs(Fraction(got[i, j]) - exact) <= abs(exact) * Fraction(2) ** -52
+
+
+def test_w4a16_identity_weights_with_group_scales():
+    """B = identity (code 0x2 = 1.0 on the diagonal), scale 2 on even 16-groups
+    of each row and 1 on odd ones: C[:, j] = s2 * A[:, j] * (2 if (j // 16) even)."""
+    k = n = 64
+    a = rand_bf16((7, k), 91)
+    codes = np.zeros((n, k), np.uint8)
+    codes[np.arange(n), np.arange(n)] = 0x2
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    sfb = np.where((np.arange(k // 16)[None, :] % 2) == 0, 0x40, 0x38).astype(np.uint8).repeat(n, 0)
+    s2 = 0.75
+    got = oracle.gemm_w4a16_ref(a, packed, sfb, s2)
+    af = oracle.bf16_to_f64(a)
+    factor = np.where((np.arange(n) // 16) % 2 == 0, 2.0, 1.0)
+    assert np.array_equal(got, 0.75 * af * factor[None, :])
+
+
+def test_w4a16_exact_output_rounds_once_in_fp32_then_bf16():
+    """Grid activations and scales in {1, 2}: every dot product is exact in FP32,
+    so C = bf16(fl32(s2 * acc)) is unique; checked by exact rationals and a
+    pure-Python single-precision multiply."""
+    tab = _e2m1_table()
+    m, n, k = 4, 6, 256
+    a = synthetic.grid_bf16((m, k), -8, 8, -5, 92, 0)
+    b = synthetic.fp4_packed(n, k, 92, 1)
+    sfb = synthetic.e4m3_choice(n, k // 16, [0x38, 0x40], 92, 5)
+    for s2 in (0.0123, 1.0, 3.0, -0.3):
+        got = oracle.gemm_w4a16_exact(a, b, sfb, s2)
+        s2f = struct.unpack("<f", struct.pack("<f", s2))[0]
+        for i in range(m):
+            for j in range(n):
+                dot = Fraction(0)
+                for kk in range(k):
+                    byte = int(b[j, kk // 2])
+                    code = byte & 0xF if kk % 2 == 0 else byte >> 4
+                    dot += bf16_exact(int(a[i, kk])) * tab[code] * _e4m3_exact(int(sfb[j, kk // 16]))
+                prod = f32r(float(Fraction(s2f) * dot))      # exact in a double, one FP32 rounding
+                want = torch_bf16_bits(np.array([prod], np.float32))[0]
+                assert int(got[i, j]) == int(want)
+
+
+def test_w4a16_exact_rejects_inexact_sums():
+    a = rand_bf16((2, 64), 93)
+    b = synthetic.fp4_packed(3, 64, 93, 1)
+    sfb = synthetic.e4m3_uniform(3, 4, 2 ** -4, 2 ** 4, 93, 5)
+    with pytest.raises(ValueError):
+        oracle.gemm_w4a16_exact(a, b, sfb, 1.0)
+
+
+def test_w4a16_on_dequantized_activations_equals_fp4_times_scale():
+    """With A holding exact FP4 values (unit scales), W4A16 is the FP4 GEMM times s2."""
+    m, n, k = 5, 4, 64
+    qa = synthetic.fp4_packed(m, k, 94, 0)
+    one = np.full((m, k // 16), 0x38, np.uint8)
+    tab = np.array([float(_e2m1_table()[c]) for c in range(16)], np.float32)
+    a = torch_bf16_bits(tab[oracle.unpack_e2m1(qa)])
+    b = synthetic.fp4_packed(n, k, 94, 1)
+    sfb = synthetic.e4m3_uniform(n, k // 16, 2 ** -4, 2 ** 4, 94, 5)
+    assert np.array_equal(oracle.gemm_w4a16_ref(a, b, sfb, 0.5), 0.5 * oracle.gemm_fp4_ref(qa, one, b, sfb))
