@@ -6,8 +6,9 @@ and raises BlockGemmError on a non-OK status. All arithmetic runs in the HIP
 kernels of the shared library; there is no fallback path. PyTorch provides
 device memory and streams.
 
-Importing this module fails if the library has not been built
-(`python -m block_scaled_fp4_gemm_amd.build`, or __graft_entry__.build()).
+Importing this module fails if the library has not been built, or was built
+from older sources (`python block_scaled_fp4_gemm_amd/build.py`, or
+__graft_entry__.build()).
 """
 from __future__ import annotations
 
@@ -18,9 +19,10 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libblockgemm.so")
 
+_REBUILD = "python block_scaled_fp4_gemm_amd/build.py"
+
 if not os.path.exists(_LIB_PATH):
-    raise ImportError(
-        f"{_LIB_PATH} is missing: build it with `python -m block_scaled_fp4_gemm_amd.build`")
+    raise ImportError(f"{_LIB_PATH} is missing: build it with `{_REBUILD}`")
 
 lib = ctypes.CDLL(_LIB_PATH)
 
@@ -32,10 +34,15 @@ _SIGS = {
     "gemm_bf16_ordered": [_p, _p, _p, _u32, _u32, _u32, _p],
     "gemm_bf16_ordered_f32": [_p, _p, _p, _u32, _u32, _u32, _p],
     "gemm_fp4_blockscaled": [_p, _p, _p, _p, _p, _u32, _u32, _u32, _p],
+    "gemm_w4a16": [_p, _p, _p, _f32, _p, _u32, _u32, _u32, _p],
     "bf16_scaled_add": [_p, _p, _sz, _f32, _p],
 }
 for _name, _args in _SIGS.items():
-    _fn = getattr(lib, _name)
+    try:
+        _fn = getattr(lib, _name)
+    except AttributeError as _e:
+        raise ImportError(f"{_LIB_PATH} lacks {_name} (built from older sources): rebuild it with "
+                          f"`{_REBUILD}`") from _e
     _fn.argtypes = _args
     _fn.restype = ctypes.c_int
 lib.gemm_bf16_splitk_workspace_bytes.argtypes = [_u32, _u32, _u32]
@@ -161,6 +168,23 @@ def gemm_fp4_blockscaled(a: torch.Tensor, sfa: torch.Tensor, b: torch.Tensor, sf
         out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
     _check(lib.gemm_fp4_blockscaled(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(out), m, n, k,
                                     _stream(stream)), "gemm_fp4_blockscaled")
+    return out
+
+
+def gemm_w4a16(a: torch.Tensor, b: torch.Tensor, sfb: torch.Tensor, scale_2: float,
+               out: torch.Tensor | None = None, stream=None):
+    """C = bf16(scale_2 * (A @ deq(B)^T)): A [M,K] bf16, B [N,K/2] packed e2m1, SFB [N,K/16] e4m3fn."""
+    for t in (b, sfb):
+        if t.element_size() != 1:
+            raise TypeError("packed FP4 weights and scales are byte tensors")
+    m, k = _bits16(a).shape
+    n = b.shape[0]
+    if b.shape[1] * 2 != k:
+        raise ValueError("B must be [N, K/2] bytes for A [M, K]")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    _check(lib.gemm_w4a16(_ptr(a), _ptr(b), _ptr(sfb), float(scale_2), _ptr(out), m, n, k, _stream(stream)),
+           "gemm_w4a16")
     return out
 
 

@@ -198,6 +198,29 @@ bg_status gemm_fp4_blockscaled(const uint8_t* A, const uint8_t* SFA, const uint8
     return launched(bg::launch_fp4(p, (hipStream_t)stream));
 }
 
+bg_status gemm_w4a16(const uint16_t* A, const uint8_t* B, const uint8_t* SFB, float scale_2,
+                     uint16_t* C, uint32_t M, uint32_t N, uint32_t K, void* stream) {
+    if (!dims_ok(M, N, K) || (K % 16) != 0) return BG_ERR_SHAPE;
+    if (M == 0 || N == 0) return BG_OK;
+    const uint64_t a_bytes = (uint64_t)M * K * 2;
+    const uint64_t b_bytes = (uint64_t)N * (K / 2), sb_bytes = (uint64_t)N * (K / 16);
+    const uint64_t c_bytes = (uint64_t)M * N * 2;
+    if (missing(A, a_bytes) || missing(B, b_bytes) || missing(SFB, sb_bytes) || missing(C, c_bytes))
+        return BG_ERR_NULL;
+    if (misaligned(A, a_bytes) || misaligned(B, b_bytes) || misaligned(SFB, sb_bytes) ||
+        misaligned(C, c_bytes))
+        return BG_ERR_ALIGN;
+    const Range rc = range_of(C, c_bytes);
+    if (overlap(rc, range_of(A, a_bytes)) || overlap(rc, range_of(B, b_bytes)) ||
+        overlap(rc, range_of(SFB, sb_bytes)))
+        return BG_ERR_ALIAS;
+    uint32_t cus = 0;
+    bg_status s = check_device(&cus);
+    if (s != BG_OK) return s;
+    bg::W4a16Problem p{A, B, SFB, C, M, N, K, scale_2, cus};
+    return launched(bg::launch_w4a16(p, (hipStream_t)stream));
+}
+
 bg_status bf16_scaled_add(uint16_t* out, const uint16_t* delta, size_t count, float scale,
                           void* stream) {
     if (count == 0) return BG_OK;

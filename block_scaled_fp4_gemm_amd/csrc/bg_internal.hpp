@@ -15,6 +15,7 @@ enum Epilogue : int {
     EPI_STORE_BF16 = 0,   // C = bf16(acc)
     EPI_SCALED_ACC = 1,   // out = bf16(out + scale * bf16(acc)), in place
     EPI_STORE_F32 = 2,    // plane[blockIdx.z] = acc (split-K partials)
+    EPI_SCALE_BF16 = 3,   // C = bf16(fl32(scale * acc))  (W4A16 per-tensor scale)
 };
 
 struct DenseProblem {
@@ -37,11 +38,22 @@ struct Fp4Problem {
     uint32_t M, N, K;
 };
 
+struct W4a16Problem {
+    const uint16_t* A;   // [M, K] bf16 activations
+    const uint8_t* B;    // [N, K/2] packed e2m1 weights
+    const uint8_t* SFB;  // [N, K/16] e4m3fn
+    uint16_t* C;         // [M, N] bf16
+    uint32_t M, N, K;
+    float scale_2;       // per-tensor weight scale
+    uint32_t cus;        // compute units of the current device (tile choice)
+};
+
 // Kernel launchers (defined in the .hip files). They enqueue on `stream` and
 // return hipGetLastError() of the launch. Shapes are already validated and
 // non-empty (M > 0, N > 0).
 hipError_t launch_dense(const DenseProblem& p, Epilogue epi, hipStream_t stream);
 hipError_t launch_fp4(const Fp4Problem& p, hipStream_t stream);
+hipError_t launch_w4a16(const W4a16Problem& p, hipStream_t stream);
 hipError_t launch_ordered(const uint16_t* A, const uint16_t* B, void* C, bool f32_out,
                           uint32_t M, uint32_t N, uint32_t K, hipStream_t stream);
 hipError_t launch_splitk_reduce(const float* ws, uint16_t* C, uint32_t M, uint32_t N,

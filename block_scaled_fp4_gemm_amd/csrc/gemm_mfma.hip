@@ -41,13 +41,22 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BK = 64;       // K elements per pipeline step
 constexpr int GROUP_M = 8;   // tile-rows per group in the grouped order
 
-enum Source : int { SRC_BF16_VEC = 0, SRC_BF16_SCALAR = 1, SRC_FP4 = 2 };
+// Operand sources. A kernel's SRC names both operands: SRC_W4A16 is BF16 A
+// (SRC_BF16_VEC staging) with FP4 B dequantized to BF16 (SRC_FP4_BF16).
+enum Source : int {
+    SRC_BF16_VEC = 0,
+    SRC_BF16_SCALAR = 1,
+    SRC_FP4 = 2,        // both operands FP4, dequantized to FP16
+    SRC_W4A16 = 3,
+    SRC_FP4_BF16 = 4,   // staging only: FP4 dequantized to BF16
+};
 
 struct KParams {
     const uint16_t* A;     // bf16 [M,K]            (SRC_BF16_*)
@@ -207,15 +216,16 @@ struct Stager<ROWS, NT, SRC_BF16_SCALAR, BKS> {
 };
 
 // Block-scaled FP4: a unit is one 16-element scale group of one row (8 packed
-// bytes + 1 scale byte); it is dequantized exactly to FP16 while being written
-// to LDS as two 16-byte chunks, for the FP16 MFMA. Every e2m1 value and every
-// e4m3 scale is exact in FP16, and so is their product: at most 6 significant
-// bits, magnitude between 2^-10 and 2688 (or zero, or NaN from a NaN scale).
-// So the packed FP16 multiply rounds nothing, and the operands the MFMA sees
-// are exactly the dequantized values: one conversion and half a packed
-// multiply per element.
-template <int ROWS, int NT>
-struct Stager<ROWS, NT, SRC_FP4, BK> {
+// bytes + 1 scale byte); it is dequantized exactly while being written to LDS
+// as two 16-byte chunks. Every e2m1 value, every e4m3 scale and their product
+// (at most 6 significant bits, magnitude between 2^-10 and 2688, or zero, or
+// NaN from a NaN scale) is exact in FP16 and in BF16.
+//  - F16OUT (both operands FP4, FP16 MFMA): FP16 convert, then half a packed
+//    FP16 multiply per element; the multiply rounds nothing.
+//  - BF16 (W4A16 weights next to BF16 activations, BF16 MFMA): FP32 convert,
+//    FP32 multiply (exact), BF16 pack (exact).
+template <int ROWS, int NT, bool F16OUT>
+struct Fp4Stager {
     static constexpr int PER = ROWS * (BK / 16) / NT;
     static_assert(PER * NT == ROWS * (BK / 16), "tile not divisible among threads");
     u32x2 w[PER];
@@ -240,18 +250,29 @@ struct Stager<ROWS, NT, SRC_FP4, BK> {
         }
     }
 
-    // Two e2m1 values (byte `byte` of word: low nibble first) times the scale
-    // in the low half of sc2, as packed FP16.
-    __device__ __forceinline__ static uint32_t deq2(uint32_t word, f16x2 sc2, int byte) {
-        f16x2 v;
-        switch (byte) {   // byte select must be an immediate
-            case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0); break;
-            case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1); break;
-            case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2); break;
-            default: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3); break;
+    // Two e2m1 values (byte `byte` of word: low nibble first) times the
+    // scale, as two packed 16-bit values.
+    __device__ __forceinline__ static uint32_t deq2(uint32_t word, f16x2 sc16, float sc32, int byte) {
+        if constexpr (F16OUT) {
+            f16x2 v;
+            switch (byte) {   // byte select must be an immediate
+                case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0); break;
+                case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1); break;
+                case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2); break;
+                default: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3); break;
+            }
+            const f16x2 sc = {sc16.x, sc16.x};
+            return __builtin_bit_cast(uint32_t, v * sc);   // v_pk_mul_f16, exact
+        } else {
+            f32x2 v;
+            switch (byte) {
+                case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0); break;
+                case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1); break;
+                case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2); break;
+                default: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3); break;
+            }
+            return pack_bf16x2(v.x * sc32, v.y * sc32);
         }
-        const f16x2 sc = {sc2.x, sc2.x};
-        return __builtin_bit_cast(uint32_t, v * sc);   // v_pk_mul_f16, exact
     }
 
     __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
@@ -261,16 +282,30 @@ struct Stager<ROWS, NT, SRC_FP4, BK> {
             const int row = u >> 2, g = u & 3;
             const bool in = (valid >> i) & 1u;
             const uint32_t wx = in ? w[i].x : 0u, wy = in ? w[i].y : 0u;
-            // e4m3fn byte -> FP16 (exact, NaN stays NaN); a unit past the K
-            // range gets scale 0 and zero data
-            const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(in ? s[i] : 0u, 1.0f, false);
-            const u32x4 lo = {deq2(wx, sc, 0), deq2(wx, sc, 1), deq2(wx, sc, 2), deq2(wx, sc, 3)};
-            const u32x4 hi = {deq2(wy, sc, 0), deq2(wy, sc, 1), deq2(wy, sc, 2), deq2(wy, sc, 3)};
+            // e4m3fn byte -> FP16 or FP32 (exact, NaN stays NaN); a unit past
+            // the K range gets scale 0 and zero data
+            const uint32_t sb = in ? s[i] : 0u;
+            f16x2 sc16 = {};
+            float sc32 = 0.0f;
+            if constexpr (F16OUT)
+                sc16 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
+            else
+                sc32 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sb, 1.0f, false)[0];
+            const u32x4 lo = {deq2(wx, sc16, sc32, 0), deq2(wx, sc16, sc32, 1), deq2(wx, sc16, sc32, 2),
+                              deq2(wx, sc16, sc32, 3)};
+            const u32x4 hi = {deq2(wy, sc16, sc32, 0), deq2(wy, sc16, sc32, 1), deq2(wy, sc16, sc32, 2),
+                              deq2(wy, sc16, sc32, 3)};
             *reinterpret_cast<u32x4*>(lds + row * BK + chunk_slot<8>(row, 2 * g) * 8) = lo;
             *reinterpret_cast<u32x4*>(lds + row * BK + chunk_slot<8>(row, 2 * g + 1) * 8) = hi;
         }
     }
 };
+
+template <int ROWS, int NT>
+struct Stager<ROWS, NT, SRC_FP4, BK> : Fp4Stager<ROWS, NT, true> {};
+
+template <int ROWS, int NT>
+struct Stager<ROWS, NT, SRC_FP4_BF16, BK> : Fp4Stager<ROWS, NT, false> {};
 
 // ---------------------------------------------------------------------------
 // Direct global -> LDS staging (gfx950 global_load_lds_dwordx4) for BF16 rows
@@ -379,72 +414,6 @@ __device__ __forceinline__ void mfma_block(const bf16x8 (&fa)[FM], const bf16x8 
         }
 }
 
-// acc[i][j][4g + e] is C[m][n + e] with
-//   m = m0 + wm*TM + i*32 + lane%32,  n = n0 + wn*TN + j*32 + 8g + 4*(lane/32).
-template <int EPI, int FM, int FN, int TM, int TN>
-__device__ __forceinline__ void epilogue(const KParams& p, const f32x16 (&acc)[FM][FN], int m0,
-                                         int n0, int wm, int wn, int lane, int split) {
-    const int M = p.M, N = p.N, ldc = p.ldc;
-    const bool vec_ok = (N & 3) == 0 && (ldc & 3) == 0;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int m = m0 + wm * TM + i * 32 + (lane & 31);
-        if (m >= M) continue;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * TN + j * 32 + g * 8 + (lane >> 5) * 4;
-                const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
-                const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-                const int64_t off = (int64_t)m * ldc + n;
-                if constexpr (EPI == EPI_STORE_F32) {
-                    float* plane = reinterpret_cast<float*>(p.C) + (int64_t)split * M * ldc;
-                    if (vec_ok && n + 3 < N) {
-                        *reinterpret_cast<f32x4*>(plane + off) = f32x4{v0, v1, v2, v3};
-                    } else {
-                        const float v[4] = {v0, v1, v2, v3};
-                        for (int e = 0; e < 4; ++e)
-                            if (n + e < N) plane[off + e] = v[e];
-                    }
-                } else if constexpr (EPI == EPI_STORE_BF16) {
-                    uint16_t* C = reinterpret_cast<uint16_t*>(p.C);
-                    const uint32_t w0 = pack_bf16x2(v0, v1), w1 = pack_bf16x2(v2, v3);
-                    if (vec_ok && n + 3 < N) {
-                        *reinterpret_cast<u32x2*>(C + off) = u32x2{w0, w1};
-                    } else {
-                        const uint16_t h[4] = {(uint16_t)w0, (uint16_t)(w0 >> 16), (uint16_t)w1,
-                                               (uint16_t)(w1 >> 16)};
-                        for (int e = 0; e < 4; ++e)
-                            if (n + e < N) C[off + e] = h[e];
-                    }
-                } else {  // EPI_SCALED_ACC: out = bf16(out + scale * bf16(delta))
-                    uint16_t* O = reinterpret_cast<uint16_t*>(p.C);
-                    const uint32_t d0 = pack_bf16x2(v0, v1), d1 = pack_bf16x2(v2, v3);
-                    const float s = p.scale;
-                    if (vec_ok && n + 3 < N) {
-                        const u32x2 o = *reinterpret_cast<const u32x2*>(O + off);
-                        const float r0 = bf16_lo(o.x) + s * bf16_lo(d0);
-                        const float r1 = bf16_hi(o.x) + s * bf16_hi(d0);
-                        const float r2 = bf16_lo(o.y) + s * bf16_lo(d1);
-                        const float r3 = bf16_hi(o.y) + s * bf16_hi(d1);
-                        *reinterpret_cast<u32x2*>(O + off) = u32x2{pack_bf16x2(r0, r1), pack_bf16x2(r2, r3)};
-                    } else {
-                        const float d[4] = {bf16_lo(d0), bf16_hi(d0), bf16_lo(d1), bf16_hi(d1)};
-                        for (int e = 0; e < 4; ++e) {
-                            if (n + e < N) {
-                                const float o = __builtin_bit_cast(float, (uint32_t)O[off + e] << 16);
-                                const float r = o + s * d[e];
-                                O[off + e] = (uint16_t)pack_bf16x2(r, 0.0f);
-                            }
-                        }
-                    }
-                }
-            }
-        }
-    }
-}
-
 // Scheduling groups for one sub-step: NM MFMAs, ND LDS reads and NV direct
 // (VMEM) loads, issued as MFMA, LDS read, VMEM, MFMA, ... until the memory
 // instructions run out, then the remaining MFMAs.
@@ -504,6 +473,10 @@ __device__ __forceinline__ void staged_epilogue(const KParams& p, const f32x16 (
                     const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
                     if constexpr (EPI == EPI_STORE_F32) {
                         *reinterpret_cast<f32x4*>(lds + slot(row, n_local >> 2)) = f32x4{v0, v1, v2, v3};
+                    } else if constexpr (EPI == EPI_SCALE_BF16) {
+                        const float sc = p.scale;   // one FP32 multiply, then the BF16 rounding
+                        *reinterpret_cast<u32x2*>(lds + slot(row, n_local >> 3) + (lane >> 5) * 8) =
+                            u32x2{pack_bf16x2(v0 * sc, v1 * sc), pack_bf16x2(v2 * sc, v3 * sc)};
                     } else {
                         *reinterpret_cast<u32x2*>(lds + slot(row, n_local >> 3) + (lane >> 5) * 8) =
                             u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
@@ -533,7 +506,7 @@ __device__ __forceinline__ void staged_epilogue(const KParams& p, const f32x16 (
                     const uint32_t e4[4] = {w.x, w.y, w.z, w.w};
                     for (int e = 0; e < 4 && n + e < N; ++e) plane[off + e] = __builtin_bit_cast(float, e4[e]);
                 }
-            } else if constexpr (EPI == EPI_STORE_BF16) {
+            } else if constexpr (EPI == EPI_STORE_BF16 || EPI == EPI_SCALE_BF16) {
                 uint16_t* C = reinterpret_cast<uint16_t*>(p.C);
                 if (full) {
                     *reinterpret_cast<u32x4*>(C + off) = w;
@@ -622,11 +595,16 @@ gemm_mfma_kernel(KParams p) {
     f32x16 acc[FM][FN];
     zero_acc(acc);
 
-    Stager<BM, NT, SRC> sa0, sa1;
-    Stager<BN, NT, SRC> sb0, sb1;
+    constexpr int SRC_A = SRC == SRC_W4A16 ? SRC_BF16_VEC : SRC;
+    constexpr int SRC_B = SRC == SRC_W4A16 ? SRC_FP4_BF16 : SRC;
+    Stager<BM, NT, SRC_A> sa0, sa1;
+    Stager<BN, NT, SRC_B> sb0, sb1;
     auto load = [&](auto& sa, auto& sb, int k0) {
         if constexpr (SRC == SRC_FP4) {
             sa.load(p.Aq, p.SFA, m0, p.M, p.K, k0, ke, tid);
+            sb.load(p.Bq, p.SFB, n0, p.N, p.K, k0, ke, tid);
+        } else if constexpr (SRC == SRC_W4A16) {
+            sa.load(p.A, m0, p.M, p.K, k0, ke, tid);
             sb.load(p.Bq, p.SFB, n0, p.N, p.K, k0, ke, tid);
         } else {
             sa.load(p.A, m0, p.M, p.K, k0, ke, tid);
@@ -1109,8 +1087,41 @@ hipError_t launch_dense(const DenseProblem& p, Epilogue epi, hipStream_t stream)
         case EPI_STORE_F32:
             return vec ? launch_dense_src<EPI_STORE_F32, SRC_BF16_VEC>(kp, splits, stream)
                        : launch_dense_src<EPI_STORE_F32, SRC_BF16_SCALAR>(kp, splits, stream);
+        case EPI_SCALE_BF16:   // W4A16 only (launch_w4a16)
+            break;
     }
     return hipErrorInvalidValue;
+}
+
+// W4A16 tile choices (register-staged kernel; BLOCKGEMM_W4A16_TILE, a tuning
+// hook, forces one). The estimate is rounds x blocks per CU x tile area /
+// measured rate, as for the BF16 tiles.
+struct W4a16Choice {
+    int cfg, bm, bn, occ;
+    double rate;
+};
+constexpr W4a16Choice kW4a16Choices[] = {
+    {0, 256, 256, 1, 985.0},
+    {4, 128, 384, 1, 760.0},   // 1016 x 12288: 256 tiles, exactly one round
+    {1, 128, 256, 1, 850.0},
+    {2, 128, 128, 2, 800.0},
+};
+
+int choose_w4a16(int M, int N, int cus) {
+    int best = 0;
+    double best_t = 1e300;
+    for (const W4a16Choice& c : kW4a16Choices) {
+        const double tiles = (double)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+        const double slots = (double)cus * c.occ;
+        const double rounds = tiles <= cus ? 1.0 : (double)(int64_t)((tiles + slots - 1) / slots);
+        const double occ = tiles <= cus ? 1.0 : c.occ;
+        const double t = rounds * occ * c.bm * c.bn / c.rate;
+        if (t < best_t) {
+            best_t = t;
+            best = c.cfg;
+        }
+    }
+    return best;
 }
 
 hipError_t launch_fp4(const Fp4Problem& p, hipStream_t stream) {
@@ -1132,6 +1143,30 @@ hipError_t launch_fp4(const Fp4Problem& p, hipStream_t stream) {
         case 2: return launch_cfg<128, 128, 2, 2, EPI_STORE_BF16, SRC_FP4, 2>(kp, 1, stream);
         case 3: return launch_cfg<256, 256, 2, 2, EPI_STORE_BF16, SRC_FP4, 1>(kp, 1, stream);
         default: return launch_cfg<256, 256, 2, 4, EPI_STORE_BF16, SRC_FP4, 1>(kp, 1, stream);
+    }
+}
+
+hipError_t launch_w4a16(const W4a16Problem& p, hipStream_t stream) {
+    KParams kp{};
+    kp.A = p.A;
+    kp.Bq = p.B;
+    kp.SFB = p.SFB;
+    kp.C = p.C;
+    kp.M = (int)p.M;
+    kp.N = (int)p.N;
+    kp.K = (int)p.K;
+    kp.ldc = (int)p.N;
+    kp.k_chunk = (int)p.K;
+    kp.scale = p.scale_2;
+    int cfg = env_int("BLOCKGEMM_W4A16_TILE");
+    if (cfg < 0) cfg = choose_w4a16(kp.M, kp.N, p.cus > 0 ? (int)p.cus : 256);
+    switch (cfg) {
+        case 1: return launch_cfg<128, 256, 2, 4, EPI_SCALE_BF16, SRC_W4A16, 1>(kp, 1, stream);
+        case 2: return launch_cfg<128, 128, 2, 2, EPI_SCALE_BF16, SRC_W4A16, 2>(kp, 1, stream);
+        case 3: return launch_cfg<256, 256, 2, 2, EPI_SCALE_BF16, SRC_W4A16, 1>(kp, 1, stream);
+        case 4: return launch_cfg<128, 384, 2, 4, EPI_SCALE_BF16, SRC_W4A16, 1>(kp, 1, stream);
+        case 5: return launch_cfg<256, 192, 2, 3, EPI_SCALE_BF16, SRC_W4A16, 1>(kp, 1, stream);
+        default: return launch_cfg<256, 256, 2, 4, EPI_SCALE_BF16, SRC_W4A16, 1>(kp, 1, stream);
     }
 }
 

@@ -142,8 +142,8 @@ bg_status gemm_bf16_ordered_f32(const uint16_t* A, const uint16_t* B, float* C32
  * kernelbot NVFP4 GEMM page (submission 123329): the "SCALE FACTORS" loop
  * (one scale per 16 K elements, plain [rows, K/16] layout) applied to both
  * operands, followed by a block-scaled dot product with FP32 accumulation.
- * Each dequantized element is exact in BF16 (at most 6 significant bits) and
- * is fed to BF16 matrix cores.
+ * Each dequantized element is exact in FP16 (at most 6 significant bits,
+ * magnitude 2^-10..2688) and is fed to FP16 matrix cores.
  *
  *  A:   [M, K/2] bytes, two E2M1 codes per byte, element 2t in the LOW nibble
  *       of byte t (sign bit 3, exponent bits 2..1, mantissa bit 0).
@@ -155,6 +155,30 @@ bg_status gemm_bf16_ordered_f32(const uint16_t* A, const uint16_t* B, float* C32
 bg_status gemm_fp4_blockscaled(const uint8_t* A, const uint8_t* SFA,
                                const uint8_t* B, const uint8_t* SFB, uint16_t* C,
                                uint32_t M, uint32_t N, uint32_t K, void* stream);
+
+/*
+ * gemm_w4a16: C[i,j] = bf16( fl32( s2 * sum_k A[i,k] * w[j,k] ) ), FP32
+ *   accumulation, w[j,k] = e2m1(B nibble [j,k]) * e4m3fn(SFB[j, k/16]),
+ *   s2 = scale_2.
+ *
+ * gemm_dense.rs page, doc comments of w4a16_gemm and its lossless BF16-MMA
+ * variant: BF16 activations times NVFP4 weights (E2M1 values, one FP8 E4M3
+ * scale per 16 K elements, one FP32 per-tensor scale). Each weight is
+ * dequantized exactly (it is exact in BF16) and fed with A to BF16 matrix
+ * cores; the per-tensor scale multiplies the FP32 dot product once, before
+ * the BF16 rounding of C.
+ *
+ *  A:   [M, K] BF16 activations, row-major.
+ *  B:   [N, K/2] bytes, two E2M1 codes per byte, element 2t in the LOW nibble
+ *       of byte t (the weight rows, K contiguous).
+ *  SFB: [N, K/16] E4M3FN bytes.
+ *  scale_2: the per-tensor FP32 weight scale (any finite value).
+ *  C:   [M, N] BF16, written.
+ *  K must be a multiple of 16 (BG_ERR_SHAPE otherwise); C must not overlap
+ *  A, B or SFB (BG_ERR_ALIAS).
+ */
+bg_status gemm_w4a16(const uint16_t* A, const uint8_t* B, const uint8_t* SFB, float scale_2,
+                     uint16_t* C, uint32_t M, uint32_t N, uint32_t K, void* stream);
 
 /*
  * bf16_scaled_add: out[i] = bf16( f32(out[i]) + fl32(scale * f32(delta[i])) )

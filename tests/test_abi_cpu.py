@@ -57,6 +57,7 @@ def test_empty_problems_are_ok_without_pointers():
     assert L.gemm_bf16_scaled_acc(None, None, None, 0, 0, 0, 1.0, None) == bg.BG_OK
     assert L.gemm_bf16_ordered(None, None, None, 0, 3, 3, None) == bg.BG_OK
     assert L.gemm_fp4_blockscaled(None, None, None, None, None, 0, 4, 32, None) == bg.BG_OK
+    assert L.gemm_w4a16(None, None, None, 1.0, None, 3, 0, 32, None) == bg.BG_OK
     assert L.bf16_scaled_add(None, None, 0, 1.0, None) == bg.BG_OK
     assert L.gemm_bf16_splitk(None, None, None, None, 0, 0, 4, 64, 4, None) == bg.BG_OK
 
@@ -68,6 +69,8 @@ def test_null_pointers():
     assert L.gemm_bf16(A, B, None, 4, 4, 4, None) == bg.BG_ERR_NULL
     assert L.gemm_bf16_ordered_f32(A, B, None, 4, 4, 4, None) == bg.BG_ERR_NULL
     assert L.gemm_fp4_blockscaled(A, None, B, S2, C, 4, 4, 32, None) == bg.BG_ERR_NULL
+    assert L.gemm_w4a16(A, B, None, 1.0, C, 4, 4, 32, None) == bg.BG_ERR_NULL
+    assert L.gemm_w4a16(None, B, S2, 1.0, C, 4, 4, 32, None) == bg.BG_ERR_NULL
     assert L.bf16_scaled_add(None, B, 8, 1.0, None) == bg.BG_ERR_NULL
 
 
@@ -77,6 +80,8 @@ def test_misaligned_pointers():
     assert L.gemm_bf16(A, B, C + 8, 4, 4, 8, None) == bg.BG_ERR_ALIGN
     assert L.gemm_bf16_scaled_acc(A, B + 4, C, 4, 4, 8, 2.0, None) == bg.BG_ERR_ALIGN
     assert L.gemm_fp4_blockscaled(A, S1 + 1, B, S2, C, 4, 4, 32, None) == bg.BG_ERR_ALIGN
+    assert L.gemm_w4a16(A, B + 8, S2, 1.0, C, 4, 4, 32, None) == bg.BG_ERR_ALIGN
+    assert L.gemm_w4a16(A, B, S2, 1.0, C + 2, 4, 4, 32, None) == bg.BG_ERR_ALIGN
     assert L.gemm_bf16_splitk(A, B, C, W + 4, 1 << 20, 4, 4, 128, 2, None) == bg.BG_ERR_ALIGN
 
 
@@ -90,6 +95,9 @@ def test_aliasing_outputs():
     assert L.gemm_bf16_splitk(A, B, C, C, 1 << 20, 4, 4, 128, 2, None) == bg.BG_ERR_ALIAS
     # FP4 C overlaps a scale tensor
     assert L.gemm_fp4_blockscaled(A, S1, B, S2, S1, 4, 4, 32, None) == bg.BG_ERR_ALIAS
+    # W4A16 C overlaps the activations or the weight scales
+    assert L.gemm_w4a16(A, B, S2, 1.0, A + 64, 4, 4, 32, None) == bg.BG_ERR_ALIAS
+    assert L.gemm_w4a16(A, B, S2, 1.0, S2, 4, 4, 32, None) == bg.BG_ERR_ALIAS
     assert L.bf16_scaled_add(A, A + 16, 64, 1.0, None) == bg.BG_ERR_ALIAS
     # adjacent but disjoint ranges are fine up to the device check
     if torch.cuda.device_count() == 0:
@@ -99,6 +107,8 @@ def test_aliasing_outputs():
 def test_shape_rules():
     L = bg.lib
     assert L.gemm_fp4_blockscaled(A, S1, B, S2, C, 4, 4, 40, None) == bg.BG_ERR_SHAPE   # K % 16
+    assert L.gemm_w4a16(A, B, S2, 1.0, C, 4, 4, 40, None) == bg.BG_ERR_SHAPE             # K % 16
+    assert L.gemm_w4a16(A, B, S2, 1.0, C, 4, 1 << 31, 32, None) == bg.BG_ERR_SHAPE
     assert L.gemm_bf16_splitk(A, B, C, W, 1 << 30, 4, 4, 128, 0, None) == bg.BG_ERR_SHAPE
     assert L.gemm_bf16_splitk(A, B, C, W, 1 << 30, 4, 4, 128, 65, None) == bg.BG_ERR_SHAPE
     assert L.gemm_bf16(A, B, C, 1 << 31, 4, 4, None) == bg.BG_ERR_SHAPE
@@ -116,6 +126,7 @@ def test_valid_arguments_reach_the_device_check():
     L = bg.lib
     assert L.gemm_bf16(A, B, C, 4, 4, 8, None) == bg.BG_ERR_DEVICE
     assert L.gemm_bf16_splitk(A, B, C, None, 0, 4, 4, 8, 1, None) == bg.BG_ERR_DEVICE
+    assert L.gemm_w4a16(A, B, S2, 0.5, C, 4, 4, 32, None) == bg.BG_ERR_DEVICE
 
 
 def test_python_binding_raises_on_status():

@@ -1,0 +1,85 @@
+"""GPU parity of gemm_w4a16 (BF16 activations x NVFP4 weights, per-tensor scale)."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp4_gemm_amd as bg
+import oracle
+import synthetic
+from gpu_util import assert_bits_equal, bits_of, check_close, to_dev_bf16, to_dev_u8
+
+pytestmark = pytest.mark.gpu
+
+S2 = synthetic.W4A16_SCALE_2
+
+
+def _run(a, b, sfb, s2):
+    c = bg.gemm_w4a16(to_dev_bf16(a), to_dev_u8(b), to_dev_u8(sfb), s2)
+    torch.cuda.synchronize()
+    return bits_of(c)
+
+
+def _check(a, b, sfb, s2, rows=None, what=""):
+    got = _run(a, b, sfb, s2)
+    k = a.shape[1]
+    sel = slice(None) if rows is None else rows
+    ref = oracle.gemm_w4a16_ref(a[sel], b, sfb, s2)
+    sig_b = oracle.rms(oracle.dequant_fp4(b, sfb)) * abs(float(np.float32(s2)))
+    check_close(got[sel], ref, k, oracle.rms(oracle.bf16_to_f64(a)), sig_b, what)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 16), (65, 129, 48), (7, 300, 64), (130, 66, 272),
+                                   (257, 255, 1040), (33, 17, 528), (300, 520, 2048)])
+def test_w4a16_edge_shapes(m, n, k):
+    print(f"w4a16 edge m={m} n={n} k={k}", flush=True)
+    a = synthetic.normal_bf16((m, k), 1.0, 100 + m, 0)
+    b = synthetic.fp4_packed(n, k, 100 + n, 1)
+    sfb = synthetic.e4m3_uniform(n, k // 16, 2 ** -4, 2 ** 4, 100, 5)
+    _check(a, b, sfb, S2, what=f"w4a16 {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("s2", [S2, 1.0, -3.0, 2.0 ** -20])
+@pytest.mark.parametrize("m,n,k", [(96, 80, 3008), (257, 131, 512), (5, 600, 64)])
+def test_w4a16_exactly_summable_bit_exact(m, n, k, s2):
+    """Grid activations and weight scales in {1, 2}: the FP32 dot products are
+    exact in any order, so C = bf16(fl32(s2 * acc)) is unique."""
+    a = synthetic.grid_bf16((m, k), -8, 8, -5, 101, 0)
+    b = synthetic.fp4_packed(n, k, 101, 1)
+    sfb = synthetic.e4m3_choice(n, k // 16, [0x38, 0x40], 101, 5)
+    assert_bits_equal(_run(a, b, sfb, s2), oracle.gemm_w4a16_exact(a, b, sfb, s2), f"w4a16 exact s2={s2}")
+
+
+def test_w4a16_qkvz_workload_all_rows():
+    print("w4a16 1016x12288x2048", flush=True)
+    a, b, sfb, s2 = synthetic.w4a16_gemm()
+    _check(a, b, sfb, s2, what="w4a16 qkvz")
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5])
+def test_every_w4a16_tile_config(cfg, monkeypatch):
+    """Each W4A16 tile variant (BLOCKGEMM_W4A16_TILE, a tuning hook) on ragged shapes."""
+    monkeypatch.setenv("BLOCKGEMM_W4A16_TILE", str(cfg))
+    for m, n, k in [(1, 1, 16), (65, 129, 48), (257, 255, 1040), (300, 520, 208)]:
+        a = synthetic.normal_bf16((m, k), 1.0, 110 + cfg, 0)
+        b = synthetic.fp4_packed(n, k, 110 + cfg, 1)
+        sfb = synthetic.e4m3_uniform(n, k // 16, 2 ** -4, 2 ** 4, 110, 5)
+        _check(a, b, sfb, S2, what=f"w4a16 cfg {cfg} {m}x{n}x{k}")
+        ga = synthetic.grid_bf16((m, k), -8, 8, -5, 111, 0)
+        eb = synthetic.e4m3_choice(n, k // 16, [0x38, 0x40], 111, 5)
+        assert_bits_equal(_run(ga, b, eb, 0.75), oracle.gemm_w4a16_exact(ga, b, eb, 0.75),
+                          f"w4a16 cfg {cfg} exact {m}x{n}x{k}")
+
+
+def test_w4a16_equals_fp4_gemm_on_fp4_valued_activations():
+    """A holding exact E2M1 values (unit scales) and s2 = 1: both entry points
+    compute the same exact sums, so their outputs agree bit for bit."""
+    m, n, k = 200, 136, 512
+    qa = synthetic.fp4_packed(m, k, 112, 0)
+    one = np.full((m, k // 16), 0x38, np.uint8)
+    a = oracle.f32_to_bf16(oracle.dequant_fp4(qa, one).astype(np.float32))
+    b = synthetic.fp4_packed(n, k, 112, 1)
+    sfb = synthetic.e4m3_choice(n, k // 16, [0x38, 0x40], 112, 5)
+    w = _run(a, b, sfb, 1.0)
+    c = bg.gemm_fp4_blockscaled(to_dev_u8(qa), to_dev_u8(one), to_dev_u8(b), to_dev_u8(sfb))
+    torch.cuda.synchronize()
+    assert_bits_equal(w, bits_of(c), "w4a16 vs fp4")
