@@ -9,8 +9,10 @@ HBM before timing starts. `value` = 3 * 2*M*N*K flops per step / step time.
 
 Every other row of the hot path is timed in the same run and reported under
 "rows": attention projections, the fused LoRA fold (HBM roofline), the
-order-preserving router GEMM (FP32 VALU roofline), the block-scaled FP4 GEMM
-and the small dense case, each warm and after a 1 GiB cache flush.
+order-preserving router GEMM (FP32 VALU roofline), the block-scaled FP4 GEMM,
+W4A16 and the small dense case, each warm and after a 1 GiB cache flush
+(median with p20/p80), each with the oracle timed beside it on a bounded
+sample of its rows (`oracle_*` fields, extrapolated to the full problem).
 
 Output: one JSON line on stdout; progress goes to stderr.
 """
@@ -50,6 +52,8 @@ def parse():
     p.add_argument("--no-rows", action="store_true", help="skip the per-row table")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--row-oracle-seconds", type=float, default=1.0,
+                   help="oracle time budget per row (0 skips the per-row oracle timings)")
     p.add_argument("--calib-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return p.parse_args()
@@ -199,7 +203,7 @@ def main():
     }
 
     if not args.no_rows:
-        result["rows"] = measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream)
+        result["rows"] = measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream, args.row_oracle_seconds)
 
     del X, Wg, Wu, H, Wd, G, U, D, WS
     torch.cuda.empty_cache()
@@ -227,14 +231,34 @@ def traffic_for_current_kernel():
         return None
 
 
-def measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream):
+def oracle_timing(fn_rows, total_rows, block, seconds):
+    """Runs the oracle on consecutive row blocks [r0, r1) until `seconds` of
+    wall time (at least one block) and extrapolates to all rows."""
+    if seconds <= 0:
+        return {}
+    t0 = time.time()
+    done = 0
+    while done < total_rows and (done == 0 or time.time() - t0 < seconds):
+        r1 = min(total_rows, done + block)
+        fn_rows(done, r1)
+        done = r1
+    dt = time.time() - t0
+    return {"oracle_us_extrapolated": round(dt / done * total_rows * 1e6, 1),
+            "oracle_sample": f"{done} of {total_rows} rows in {dt:.2f} s"}
+
+
+def measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream, oracle_seconds):
+    import oracle
+
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    spread = {}
 
     def timed(fn, reps=20):
-        """Median per-call time in us, warm and cold. Calls are enqueued
-        back to back (no host synchronisation between them), each inside its
-        own pair of events on the stream; cold calls are preceded by a 1 GiB
-        write that evicts the L2s and the 256 MB Infinity Cache."""
+        """Median per-call time in us, warm and cold (p20/p80 kept in
+        `spread`). Calls are enqueued back to back (no host synchronisation
+        between them), each inside its own pair of events on the stream; cold
+        calls are preceded by a 1 GiB write that evicts the L2s and the
+        256 MB Infinity Cache."""
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
@@ -251,8 +275,15 @@ def measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream):
                 e.record(stream)
                 pairs.append((s, e))
             torch.cuda.synchronize()
-            res[mode] = float(np.median([a.elapsed_time(b) * 1e3 for a, b in pairs]))
+            us = [a.elapsed_time(b) * 1e3 for a, b in pairs]
+            res[mode] = float(np.median(us))
+            spread[mode] = [round(float(np.percentile(us, 20)), 2), round(float(np.percentile(us, 80)), 2)]
         return res["warm"], res["cold"]
+
+    def with_spread(d):
+        d["us_warm_p20_p80"] = spread["warm"]
+        d["us_cold_p20_p80"] = spread["cold"]
+        return d
 
     rows = {}
 
@@ -261,9 +292,10 @@ def measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream):
         C = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         w, c = timed(lambda: bg.gemm_bf16(A, B, out=C))
         fl = 2.0 * m * n * k
-        rows[name] = {"shape": [m, n, k], "us_warm": round(w, 2), "us_cold": round(c, 2),
-                      "tflops_warm": round(fl / w / 1e6, 1), "tflops_cold": round(fl / c / 1e6, 1),
-                      "frac_bf16_peak_warm": round(fl / w / 1e6 / BF16_PEAK_TFLOPS, 4)}
+        rows[name] = with_spread({"shape": [m, n, k], "us_warm": round(w, 2), "us_cold": round(c, 2),
+                                  "tflops_warm": round(fl / w / 1e6, 1), "tflops_cold": round(fl / c / 1e6, 1),
+                                  "frac_bf16_peak_warm": round(fl / w / 1e6 / BF16_PEAK_TFLOPS, 4)})
+        rows[name].update(oracle_timing(lambda r0, r1: oracle.gemm_bf16_ref(a[r0:r1], b), m, 32, oracle_seconds))
         log(name, rows[name])
 
     a, b = synthetic.dense_small()
@@ -282,21 +314,31 @@ def measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream):
     fl = 2.0 * 5120 * 2048 * 11008
     for ks in (1, 2, 4, 8):
         w, c = timed(lambda: bg.gemm_bf16_splitk(H, WD, ks, workspace=WS, out=D))
-        rows[f"mlp_down_5120x2048x11008_k{ks}"] = {
+        rows[f"mlp_down_5120x2048x11008_k{ks}"] = with_spread({
             "us_warm": round(w, 2), "us_cold": round(c, 2), "tflops_warm": round(fl / w / 1e6, 1),
             "tflops_cold": round(fl / c / 1e6, 1), "frac_bf16_peak_warm": round(fl / w / 1e6 / BF16_PEAK_TFLOPS, 4),
-            "workspace_bytes": ks * 5120 * 2048 * 4 if ks > 1 else 0}
+            "workspace_bytes": ks * 5120 * 2048 * 4 if ks > 1 else 0})
         log(f"down k{ks}", rows[f"mlp_down_5120x2048x11008_k{ks}"])
+    # the oracle's split-K definition: FP64 planes, then the ascending FP32 reduce
+    rows["mlp_down_5120x2048x11008_k8"].update(oracle_timing(
+        lambda r0, r1: oracle.splitk_reduce(oracle.gemm_splitk_planes_ref(h[r0:r1], wd, 8).astype(np.float32)),
+        5120, 16, oracle_seconds))
     del H, WD, D, WS
 
     out, x, bl, scale = synthetic.lora_fold()
     O, X, BL = up16(out), up16(x), up16(bl)
     w, c = timed(lambda: bg.gemm_bf16_scaled_acc(X, BL, O, scale))
     byts = 2 * 2048 * 17408 * 2 + (2048 + 17408) * 64 * 2
-    rows["lora_fold_2048x17408x64"] = {"us_warm": round(w, 2), "us_cold": round(c, 2),
-                                       "gbs_warm": round(byts / w / 1e3, 1), "gbs_cold": round(byts / c / 1e3, 1),
-                                       "frac_hbm_cold": round(byts / c / 1e3 / HBM_PEAK_GBS, 4),
-                                       "algorithmic_bytes": byts}
+    rows["lora_fold_2048x17408x64"] = with_spread({
+        "us_warm": round(w, 2), "us_cold": round(c, 2),
+        "gbs_warm": round(byts / w / 1e3, 1), "gbs_cold": round(byts / c / 1e3, 1),
+        "frac_hbm_warm": round(byts / w / 1e3 / HBM_PEAK_GBS, 4), "frac_hbm_cold": round(byts / c / 1e3 / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes": byts})
+    # the oracle's fold: FP64 delta, BF16 rounding, then the FP32 epilogue
+    rows["lora_fold_2048x17408x64"].update(oracle_timing(
+        lambda r0, r1: oracle.scaled_acc_epilogue(
+            out[r0:r1], oracle.f32_to_bf16(oracle.gemm_bf16_ref(x[r0:r1], bl).astype(np.float32)), scale),
+        2048, 16, oracle_seconds))
     log("lora", rows["lora_fold_2048x17408x64"])
     del O, X, BL
 
@@ -306,9 +348,12 @@ def measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream):
         C = torch.empty((m, 256), dtype=torch.bfloat16, device=dev)
         w, c = timed(lambda: bg.gemm_bf16_ordered(X, W, out=C))
         fl = 2.0 * m * 256 * 2048
-        rows[f"router_ordered_{m}x256x2048"] = {
+        rows[f"router_ordered_{m}x256x2048"] = with_spread({
             "us_warm": round(w, 2), "us_cold": round(c, 2), "tflops_warm": round(fl / w / 1e6, 2),
-            "frac_valu_nofma_peak": round(fl / w / 1e6 / VALU_NOFMA_PEAK_TFLOPS, 4)}
+            "frac_valu_nofma_peak": round(fl / w / 1e6 / VALU_NOFMA_PEAK_TFLOPS, 4)})
+        # the strict FP32 recurrence of the oracle
+        rows[f"router_ordered_{m}x256x2048"].update(oracle_timing(
+            lambda r0, r1: oracle.gemm_ordered(x[r0:r1], wr), m, 16, oracle_seconds))
         log(f"router {m}", rows[f"router_ordered_{m}x256x2048"])
 
     a4, sfa, b4, sfb = synthetic.fp4_gemm()
@@ -316,11 +361,27 @@ def measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream):
     C = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
     w, c = timed(lambda: bg.gemm_fp4_blockscaled(A4, SA, B4, SB, out=C))
     fl = 2.0 * 4096 * 4096 * 8192
-    rows["fp4_4096x4096x8192"] = {"us_warm": round(w, 2), "us_cold": round(c, 2),
-                                  "tflops_warm": round(fl / w / 1e6, 1),
-                                  "frac_bf16_peak_warm": round(fl / w / 1e6 / BF16_PEAK_TFLOPS, 4),
-                                  "frac_fp4_peak_warm": round(fl / w / 1e6 / FP4_PEAK_TFLOPS, 4)}
+    rows["fp4_4096x4096x8192"] = with_spread({
+        "us_warm": round(w, 2), "us_cold": round(c, 2), "tflops_warm": round(fl / w / 1e6, 1),
+        "tflops_cold": round(fl / c / 1e6, 1),
+        "frac_bf16_peak_warm": round(fl / w / 1e6 / BF16_PEAK_TFLOPS, 4),
+        "frac_fp4_peak_warm": round(fl / w / 1e6 / FP4_PEAK_TFLOPS, 4)})
+    rows["fp4_4096x4096x8192"].update(oracle_timing(
+        lambda r0, r1: oracle.gemm_fp4_ref(a4[r0:r1], sfa[r0:r1], b4, sfb), 4096, 16, oracle_seconds))
     log("fp4", rows["fp4_4096x4096x8192"])
+    del A4, SA, B4, SB, C
+
+    aw, bw, sw, s2 = synthetic.w4a16_gemm()
+    AW, BW, SW = up16(aw), u8(bw), u8(sw)
+    C = torch.empty((1016, 12288), dtype=torch.bfloat16, device=dev)
+    w, c = timed(lambda: bg.gemm_w4a16(AW, BW, SW, s2, out=C))
+    fl = 2.0 * 1016 * 12288 * 2048
+    rows["w4a16_1016x12288x2048"] = with_spread({
+        "us_warm": round(w, 2), "us_cold": round(c, 2), "tflops_warm": round(fl / w / 1e6, 1),
+        "tflops_cold": round(fl / c / 1e6, 1), "frac_bf16_peak_warm": round(fl / w / 1e6 / BF16_PEAK_TFLOPS, 4)})
+    rows["w4a16_1016x12288x2048"].update(oracle_timing(
+        lambda r0, r1: oracle.gemm_w4a16_ref(aw[r0:r1], bw, sw, s2), 1016, 16, oracle_seconds))
+    log("w4a16", rows["w4a16_1016x12288x2048"])
     del flush
     return rows
 
