@@ -29,6 +29,7 @@ lib = ctypes.CDLL(_LIB_PATH)
 _p, _u32, _f32, _sz = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_float, ctypes.c_size_t
 _SIGS = {
     "gemm_bf16": [_p, _p, _p, _u32, _u32, _u32, _p],
+    "gemm_bf16_strided": [_p, _u32, _p, _u32, _p, _u32, _u32, _u32, _u32, _p],
     "gemm_bf16_scaled_acc": [_p, _p, _p, _u32, _u32, _u32, _f32, _p],
     "gemm_bf16_splitk": [_p, _p, _p, _p, _sz, _u32, _u32, _u32, _u32, _p],
     "gemm_bf16_ordered": [_p, _p, _p, _u32, _u32, _u32, _p],
@@ -102,6 +103,27 @@ def gemm_bf16(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None,
     if out is None:
         out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
     _check(lib.gemm_bf16(_ptr(a), _ptr(b), _ptr(out), m, n, k, _stream(stream)), "gemm_bf16")
+    return out
+
+
+def _rows(t: torch.Tensor, what: str):
+    """(rows, cols, row stride) of a 2-D tensor whose rows are contiguous."""
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{what} must be 2-D with contiguous rows")
+    return t.shape[0], t.shape[1], t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
+
+
+def gemm_bf16_strided(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor, stream=None):
+    """C = bf16(A @ B^T) on row-strided views (each row contiguous, any row stride)."""
+    m, k, lda = _rows(a, "A")
+    n, kb, ldb = _rows(b, "B")
+    mc, nc, ldc = _rows(out, "C")
+    if kb != k or (mc, nc) != (m, n):
+        raise ValueError("shapes must be A [M,K], B [N,K], C [M,N]")
+    for t in (a, b, out):
+        _bits16(t)
+    _check(lib.gemm_bf16_strided(a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc, m, n, k,
+                                 _stream(stream)), "gemm_bf16_strided")
     return out
 
 

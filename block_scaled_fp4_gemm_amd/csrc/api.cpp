@@ -108,7 +108,28 @@ bg_status gemm_bf16(const uint16_t* A, const uint16_t* B, uint16_t* C, uint32_t 
     if (s != BG_OK || M == 0 || N == 0) return s;
     uint32_t cus = 0;
     if ((s = check_device(&cus)) != BG_OK) return s;
-    bg::DenseProblem p{A, B, C, M, N, K, K, 1, 0.0f, cus};
+    bg::DenseProblem p{A, B, C, M, N, K, K, K, N, K, 1, 0.0f, cus};
+    return launched(bg::launch_dense(p, bg::EPI_STORE_BF16, (hipStream_t)stream));
+}
+
+bg_status gemm_bf16_strided(const uint16_t* A, uint32_t lda, const uint16_t* B, uint32_t ldb,
+                            uint16_t* C, uint32_t ldc, uint32_t M, uint32_t N, uint32_t K,
+                            void* stream) {
+    if (!dims_ok(M, N, K) || lda > kMaxDim || ldb > kMaxDim || ldc > kMaxDim) return BG_ERR_SHAPE;
+    if (lda < K || ldb < K || ldc < N) return BG_ERR_SHAPE;
+    if (M == 0 || N == 0) return BG_OK;
+    // bytes spanned: every row but the last is a full stride
+    const uint64_t a_bytes = K == 0 ? 0 : ((uint64_t)(M - 1) * lda + K) * 2;
+    const uint64_t b_bytes = K == 0 ? 0 : ((uint64_t)(N - 1) * ldb + K) * 2;
+    const uint64_t c_bytes = ((uint64_t)(M - 1) * ldc + N) * 2;
+    if (missing(A, a_bytes) || missing(B, b_bytes) || missing(C, c_bytes)) return BG_ERR_NULL;
+    if (misaligned(A, a_bytes) || misaligned(B, b_bytes) || misaligned(C, c_bytes)) return BG_ERR_ALIGN;
+    const Range rc = range_of(C, c_bytes);
+    if (overlap(rc, range_of(A, a_bytes)) || overlap(rc, range_of(B, b_bytes))) return BG_ERR_ALIAS;
+    uint32_t cus = 0;
+    bg_status s = check_device(&cus);
+    if (s != BG_OK) return s;
+    bg::DenseProblem p{A, B, C, M, N, K, lda, ldb, ldc, K, 1, 0.0f, cus};
     return launched(bg::launch_dense(p, bg::EPI_STORE_BF16, (hipStream_t)stream));
 }
 
@@ -118,7 +139,7 @@ bg_status gemm_bf16_scaled_acc(const uint16_t* X, const uint16_t* B, uint16_t* o
     if (s != BG_OK || M == 0 || N == 0) return s;
     uint32_t cus = 0;
     if ((s = check_device(&cus)) != BG_OK) return s;
-    bg::DenseProblem p{X, B, out, M, N, K, K, 1, scale, cus};
+    bg::DenseProblem p{X, B, out, M, N, K, K, K, N, K, 1, scale, cus};
     return launched(bg::launch_dense(p, bg::EPI_SCALED_ACC, (hipStream_t)stream));
 }
 
@@ -149,10 +170,10 @@ bg_status gemm_bf16_splitk(const uint16_t* A, const uint16_t* B, uint16_t* C, fl
     if ((s = check_device(&cus)) != BG_OK) return s;
     const hipStream_t st = (hipStream_t)stream;
     if (k_splits == 1) {
-        bg::DenseProblem p{A, B, C, M, N, K, K, 1, 0.0f, cus};
+        bg::DenseProblem p{A, B, C, M, N, K, K, K, N, K, 1, 0.0f, cus};
         return launched(bg::launch_dense(p, bg::EPI_STORE_BF16, st));
     }
-    bg::DenseProblem p{A, B, workspace, M, N, K, chunk, k_splits, 0.0f, cus};
+    bg::DenseProblem p{A, B, workspace, M, N, K, K, K, N, chunk, k_splits, 0.0f, cus};
     hipError_t e = bg::launch_dense(p, bg::EPI_STORE_F32, st);
     if (e != hipSuccess) return BG_ERR_LAUNCH;
     return launched(bg::launch_splitk_reduce(workspace, C, M, N, k_splits, st));

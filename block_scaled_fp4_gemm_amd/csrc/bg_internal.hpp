@@ -23,6 +23,8 @@ struct DenseProblem {
     const uint16_t* B;   // [N, K] bf16
     void* C;             // [M, N] bf16, or [splits][M][N] f32 planes
     uint32_t M, N, K;
+    uint32_t lda, ldb;   // elements between rows of A and of B (>= K)
+    uint32_t ldc;        // elements between rows of C (>= N; N for split-K planes)
     uint32_t k_chunk;    // K elements per split (multiple of 64, or K)
     uint32_t splits;
     float scale;

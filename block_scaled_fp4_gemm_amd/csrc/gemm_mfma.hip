@@ -67,6 +67,7 @@ struct KParams {
     const uint8_t* SFB;
     void* C;               // bf16 [M,N] or f32 planes [splits][M][N], rows ldc elements apart
     int M, N, K;
+    int lda, ldb;          // elements between consecutive rows of A and B (BF16 operands; >= K)
     int ldc;               // elements between consecutive rows of C (N, or more for a column range)
     int k_chunk;           // K elements per split (blockIdx.y)
     int tiles_m, tiles_n;
@@ -152,7 +153,8 @@ struct Stager<ROWS, NT, SRC_BF16_VEC, BKS> {
     static constexpr int PER = (ROWS * CPR + NT - 1) / NT;
     u32x4 r[PER];
 
-    __device__ __forceinline__ void load(const uint16_t* base, int row0, int nrows, int K,
+    // ld: elements between consecutive rows (a multiple of 8)
+    __device__ __forceinline__ void load(const uint16_t* base, int row0, int nrows, int ld,
                                          int k0, int k_end, int tid) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
@@ -162,7 +164,7 @@ struct Stager<ROWS, NT, SRC_BF16_VEC, BKS> {
             const int grow = min(row0 + row, nrows - 1);
             const int gk = k0 + c * 8;
             if (gk < k_end)
-                r[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)grow * K + gk);
+                r[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)grow * ld + gk);
             else
                 r[i] = u32x4{0u, 0u, 0u, 0u};
         }
@@ -185,7 +187,7 @@ struct Stager<ROWS, NT, SRC_BF16_SCALAR, BKS> {
     static constexpr int PER = (ROWS * CPR + NT - 1) / NT;
     u32x4 r[PER];
 
-    __device__ __forceinline__ void load(const uint16_t* base, int row0, int nrows, int K,
+    __device__ __forceinline__ void load(const uint16_t* base, int row0, int nrows, int ld,
                                          int k0, int k_end, int tid) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
@@ -193,7 +195,7 @@ struct Stager<ROWS, NT, SRC_BF16_SCALAR, BKS> {
             if (PER * NT != ROWS * CPR && q >= ROWS * CPR) break;
             const int row = q / CPR, c = q % CPR;
             const int grow = min(row0 + row, nrows - 1);
-            const uint16_t* src = base + (int64_t)grow * K;
+            const uint16_t* src = base + (int64_t)grow * ld;
             uint32_t h[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -329,7 +331,7 @@ struct DirectStager {
     static constexpr int PER = (SEGS + NW - 1) / NW;
     static_assert(SEGS * RPS == ROWS && RPS * CPR == 64, "whole 1 KB segments");
 
-    __device__ __forceinline__ static void issue(const uint16_t* base, int row0, int nrows, int K,
+    __device__ __forceinline__ static void issue(const uint16_t* base, int row0, int nrows, int ld,
                                                  int k0, uint16_t* lds_tile, int wave, int lane) {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
@@ -337,7 +339,7 @@ struct DirectStager {
             const int row = seg * RPS + lane / CPR;
             const int c = chunk_slot<CPR>(row, lane % CPR);
             const int grow = min(row0 + row, nrows - 1);
-            const uint16_t* g = base + (int64_t)grow * K + k0 + c * 8;
+            const uint16_t* g = base + (int64_t)grow * ld + k0 + c * 8;
             const uint32_t l = (uint32_t)(uintptr_t)(
                 (__attribute__((address_space(3))) uint16_t*)(lds_tile + seg * 512));
             // Emitted as inline assembly on purpose: the compiler's wait
@@ -604,11 +606,11 @@ gemm_mfma_kernel(KParams p) {
             sa.load(p.Aq, p.SFA, m0, p.M, p.K, k0, ke, tid);
             sb.load(p.Bq, p.SFB, n0, p.N, p.K, k0, ke, tid);
         } else if constexpr (SRC == SRC_W4A16) {
-            sa.load(p.A, m0, p.M, p.K, k0, ke, tid);
+            sa.load(p.A, m0, p.M, p.lda, k0, ke, tid);
             sb.load(p.Bq, p.SFB, n0, p.N, p.K, k0, ke, tid);
         } else {
-            sa.load(p.A, m0, p.M, p.K, k0, ke, tid);
-            sb.load(p.B, n0, p.N, p.K, k0, ke, tid);
+            sa.load(p.A, m0, p.M, p.lda, k0, ke, tid);
+            sb.load(p.B, n0, p.N, p.ldb, k0, ke, tid);
         }
     };
     auto store = [&](auto& sa, auto& sb, uint16_t* buf) {
@@ -724,8 +726,8 @@ __device__ __forceinline__ void direct_mainloop(const KParams& p, uint16_t* smem
     const int nsteps = (ke - kb) / BKS + (ragged ? 1 : 0);
 
     auto issue = [&](int k0, uint16_t* buf) {
-        DirectStager<BM, NT, BKS>::issue(p.A, m0, p.M, p.K, k0, buf, wave, lane);
-        DirectStager<BN, NT, BKS>::issue(p.B, n0, p.N, p.K, k0, buf + BM * BKS, wave, lane);
+        DirectStager<BM, NT, BKS>::issue(p.A, m0, p.M, p.lda, k0, buf, wave, lane);
+        DirectStager<BN, NT, BKS>::issue(p.B, n0, p.N, p.ldb, k0, buf + BM * BKS, wave, lane);
     };
 
     // Direct loads are issued at a uniform rate: STAGES stages in the
@@ -739,8 +741,8 @@ __device__ __forceinline__ void direct_mainloop(const KParams& p, uint16_t* smem
     if (ragged) {
         Stager<BM, NT, SRC_BF16_VEC, BKS> sa;
         Stager<BN, NT, SRC_BF16_VEC, BKS> sb;
-        sa.load(p.A, m0, p.M, p.K, kb, kb + ragged, tid);
-        sb.load(p.B, n0, p.N, p.K, kb, kb + ragged, tid);
+        sa.load(p.A, m0, p.M, p.lda, kb, kb + ragged, tid);
+        sb.load(p.B, n0, p.N, p.ldb, kb, kb + ragged, tid);
         sa.store(smem, tid);
         sb.store(smem + BM * BKS, tid);
         k_next = kb + ragged;
@@ -1049,7 +1051,7 @@ hipError_t launch_dense_vec(const KParams& kp, int splits, hipStream_t stream) {
     hipError_t e = launch_tile_cfg<EPI>(left, splits, sch.cfg, stream);
     if (e != hipSuccess) return e;
     KParams right = kp;
-    right.B = kp.B + (int64_t)sch.n1 * kp.K;
+    right.B = kp.B + (int64_t)sch.n1 * kp.ldb;
     right.C = reinterpret_cast<uint16_t*>(kp.C) + sch.n1;
     right.N = kp.N - sch.n1;
     return launch_tile_cfg<EPI>(right, splits, sch.cfg2, stream);
@@ -1071,11 +1073,14 @@ hipError_t launch_dense(const DenseProblem& p, Epilogue epi, hipStream_t stream)
     kp.M = (int)p.M;
     kp.N = (int)p.N;
     kp.K = (int)p.K;
-    kp.ldc = (int)p.N;
+    kp.lda = (int)p.lda;
+    kp.ldb = (int)p.ldb;
+    kp.ldc = (int)p.ldc;
     kp.k_chunk = (int)p.k_chunk;
     kp.scale = p.scale;
     kp.cus = p.cus > 0 ? (int)p.cus : 256;
-    const bool vec = (p.K % 8) == 0;
+    // whole 16-byte chunks on 16-byte-aligned rows (the base pointers are)
+    const bool vec = (p.K % 8) == 0 && (p.lda % 8) == 0 && (p.ldb % 8) == 0;
     const int splits = (int)p.splits;
     switch (epi) {
         case EPI_STORE_BF16:
@@ -1134,6 +1139,7 @@ hipError_t launch_fp4(const Fp4Problem& p, hipStream_t stream) {
     kp.M = (int)p.M;
     kp.N = (int)p.N;
     kp.K = (int)p.K;
+    kp.lda = kp.ldb = (int)p.K;
     kp.ldc = (int)p.N;
     kp.k_chunk = (int)p.K;
     const char* e = getenv("BLOCKGEMM_FP4_TILE");   // tuning only
@@ -1155,6 +1161,7 @@ hipError_t launch_w4a16(const W4a16Problem& p, hipStream_t stream) {
     kp.M = (int)p.M;
     kp.N = (int)p.N;
     kp.K = (int)p.K;
+    kp.lda = kp.ldb = (int)p.K;
     kp.ldc = (int)p.N;
     kp.k_chunk = (int)p.K;
     kp.scale = p.scale_2;

@@ -68,6 +68,29 @@ bg_status gemm_bf16(const uint16_t* A, const uint16_t* B, uint16_t* C,
                     uint32_t M, uint32_t N, uint32_t K, void* stream);
 
 /*
+ * gemm_bf16_strided: gemm_bf16 on operands and an output that are row ranges
+ * of larger row-major buffers. Row i of A starts lda elements after row i-1,
+ * row j of B ldb elements after row j-1, row i of C ldc elements after row
+ * i-1; only the first K (A, B) or N (C) elements of each row are read or
+ * written, and C's padding elements are left untouched.
+ *
+ * gemm_dense.rs page, doc comments of w4a16_gemm_n128_ldb and
+ * w4a16_gemm_n128_m128_bf16_ldb: the weight rows are addressed through an
+ * explicit row stride, so that padded or sub-matrix operands (the odd vocab
+ * N of lm_head) are neither copied nor misaddressed. Strides that are not a
+ * multiple of 8 elements (16 bytes) are legal and take a guarded
+ * element-wise load path; they never fault.
+ *
+ *  lda >= K, ldb >= K, ldc >= N (BG_ERR_SHAPE otherwise); all at most 2^31-1.
+ *  Base pointers 16-byte aligned (BG_ERR_ALIGN). C's spanned bytes
+ *  [C, C + 2*((M-1)*ldc + N)) must not overlap A's or B's (BG_ERR_ALIAS).
+ *  With lda = ldb = K and ldc = N this is exactly gemm_bf16.
+ */
+bg_status gemm_bf16_strided(const uint16_t* A, uint32_t lda, const uint16_t* B, uint32_t ldb,
+                            uint16_t* C, uint32_t ldc, uint32_t M, uint32_t N, uint32_t K,
+                            void* stream);
+
+/*
  * gemm_bf16_scaled_acc: fused LoRA expand+fold, in place on `out`:
  *   out[i,j] = bf16( f32(out[i,j]) + fl32( scale * f32(bf16(delta[i,j])) ) ),
  *   delta = X * B^T accumulated in FP32.

@@ -54,6 +54,7 @@ def test_empty_problems_are_ok_without_pointers():
     L = bg.lib
     assert L.gemm_bf16(None, None, None, 0, 5, 7, None) == bg.BG_OK
     assert L.gemm_bf16(None, None, None, 5, 0, 7, None) == bg.BG_OK
+    assert L.gemm_bf16_strided(None, 9, None, 9, None, 3, 0, 3, 7, None) == bg.BG_OK
     assert L.gemm_bf16_scaled_acc(None, None, None, 0, 0, 0, 1.0, None) == bg.BG_OK
     assert L.gemm_bf16_ordered(None, None, None, 0, 3, 3, None) == bg.BG_OK
     assert L.gemm_fp4_blockscaled(None, None, None, None, None, 0, 4, 32, None) == bg.BG_OK
@@ -67,6 +68,7 @@ def test_null_pointers():
     assert L.gemm_bf16(None, B, C, 4, 4, 4, None) == bg.BG_ERR_NULL
     assert L.gemm_bf16(A, None, C, 4, 4, 4, None) == bg.BG_ERR_NULL
     assert L.gemm_bf16(A, B, None, 4, 4, 4, None) == bg.BG_ERR_NULL
+    assert L.gemm_bf16_strided(A, 8, B, 8, None, 8, 4, 4, 4, None) == bg.BG_ERR_NULL
     assert L.gemm_bf16_ordered_f32(A, B, None, 4, 4, 4, None) == bg.BG_ERR_NULL
     assert L.gemm_fp4_blockscaled(A, None, B, S2, C, 4, 4, 32, None) == bg.BG_ERR_NULL
     assert L.gemm_w4a16(A, B, None, 1.0, C, 4, 4, 32, None) == bg.BG_ERR_NULL
@@ -78,6 +80,7 @@ def test_misaligned_pointers():
     L = bg.lib
     assert L.gemm_bf16(A + 2, B, C, 4, 4, 8, None) == bg.BG_ERR_ALIGN
     assert L.gemm_bf16(A, B, C + 8, 4, 4, 8, None) == bg.BG_ERR_ALIGN
+    assert L.gemm_bf16_strided(A, 9, B + 2, 9, C, 4, 4, 4, 8, None) == bg.BG_ERR_ALIGN
     assert L.gemm_bf16_scaled_acc(A, B + 4, C, 4, 4, 8, 2.0, None) == bg.BG_ERR_ALIGN
     assert L.gemm_fp4_blockscaled(A, S1 + 1, B, S2, C, 4, 4, 32, None) == bg.BG_ERR_ALIGN
     assert L.gemm_w4a16(A, B + 8, S2, 1.0, C, 4, 4, 32, None) == bg.BG_ERR_ALIGN
@@ -91,6 +94,8 @@ def test_aliasing_outputs():
     assert L.gemm_bf16(A, B, A + 16, 4, 4, 64, None) == bg.BG_ERR_ALIAS
     # out overlaps B
     assert L.gemm_bf16_scaled_acc(A, B, B, 4, 4, 64, 2.0, None) == bg.BG_ERR_ALIAS
+    # strided C spans (M-1)*ldc + N elements; the B operand lies inside that span
+    assert L.gemm_bf16_strided(A, 64, B - 4 * 100 * 2 + 16, 64, B - 4 * 100 * 2, 100, 5, 4, 64, None) == bg.BG_ERR_ALIAS
     # split-K workspace overlaps C
     assert L.gemm_bf16_splitk(A, B, C, C, 1 << 20, 4, 4, 128, 2, None) == bg.BG_ERR_ALIAS
     # FP4 C overlaps a scale tensor
@@ -112,6 +117,10 @@ def test_shape_rules():
     assert L.gemm_bf16_splitk(A, B, C, W, 1 << 30, 4, 4, 128, 0, None) == bg.BG_ERR_SHAPE
     assert L.gemm_bf16_splitk(A, B, C, W, 1 << 30, 4, 4, 128, 65, None) == bg.BG_ERR_SHAPE
     assert L.gemm_bf16(A, B, C, 1 << 31, 4, 4, None) == bg.BG_ERR_SHAPE
+    assert L.gemm_bf16_strided(A, 7, B, 8, C, 4, 4, 4, 8, None) == bg.BG_ERR_SHAPE    # lda < K
+    assert L.gemm_bf16_strided(A, 8, B, 7, C, 4, 4, 4, 8, None) == bg.BG_ERR_SHAPE    # ldb < K
+    assert L.gemm_bf16_strided(A, 8, B, 8, C, 3, 4, 4, 8, None) == bg.BG_ERR_SHAPE    # ldc < N
+    assert L.gemm_bf16_strided(A, 1 << 31, B, 8, C, 4, 4, 4, 8, None) == bg.BG_ERR_SHAPE
 
 
 def test_workspace_rules():
@@ -127,6 +136,7 @@ def test_valid_arguments_reach_the_device_check():
     assert L.gemm_bf16(A, B, C, 4, 4, 8, None) == bg.BG_ERR_DEVICE
     assert L.gemm_bf16_splitk(A, B, C, None, 0, 4, 4, 8, 1, None) == bg.BG_ERR_DEVICE
     assert L.gemm_w4a16(A, B, S2, 0.5, C, 4, 4, 32, None) == bg.BG_ERR_DEVICE
+    assert L.gemm_bf16_strided(A, 13, B, 8, C, 5, 4, 4, 8, None) == bg.BG_ERR_DEVICE
 
 
 def test_python_binding_raises_on_status():
