@@ -17,12 +17,14 @@ from .codecs import (  # noqa: F401
     e2m1_to_f64,
     e4m3fn_to_f64,
     f32_to_bf16,
+    scales_from_blocked,
     unpack_e2m1,
 )
 from .gemm import (  # noqa: F401
     bf16_in_closed_range,
     gemm_bf16_ref,
     gemm_fp4_ref,
+    gemm_fp4_splitk_planes_ref,
     gemm_ordered,
     gemm_ordered_f32,
     gemm_scaled_acc_exact,

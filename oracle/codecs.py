@@ -96,3 +96,30 @@ def dequant_fp4(packed, scales) -> np.ndarray:
     vals = e2m1_to_f64(codes)
     per_elem = np.repeat(e4m3fn_to_f64(sc), 16, axis=-1)
     return vals * per_elem
+
+
+def scales_from_blocked(blocked, rows: int, k_groups: int, batch: int = 1) -> np.ndarray:
+    """Plain [L, rows, K/16] E4M3 scale bytes from NVIDIA's blocked layout.
+
+    kernelbot NVFP4 GEMM page, "SCALE FACTORS": the hardware layout has shape
+    [32, 4, rest_m, 4, rest_k, L] (dims g_m, i_m, tile_m, i_k, tile_k, l) and
+    is stored in memory in the order l, tile_m, tile_k, g_m, i_m, i_k. Plain
+    row i = tile_m*128 + i_m*32 + g_m and group j = tile_k*4 + i_k. `blocked`
+    is the flat byte buffer in that memory order; rows % 128 == 0 and
+    k_groups % 4 == 0.
+    """
+    tm, tk = rows // 128, k_groups // 4
+    assert tm * 128 == rows and tk * 4 == k_groups
+    src = np.asarray(blocked, dtype=np.uint8).reshape(-1)
+    assert src.size == batch * rows * k_groups
+    out = np.empty((batch, rows, k_groups), np.uint8)
+    pos = 0
+    for l in range(batch):
+        for tile_m in range(tm):
+            for tile_k in range(tk):
+                for g_m in range(32):
+                    for i_m in range(4):
+                        for i_k in range(4):
+                            out[l, tile_m * 128 + i_m * 32 + g_m, tile_k * 4 + i_k] = src[pos]
+                            pos += 1
+    return out

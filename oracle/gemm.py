@@ -237,3 +237,18 @@ def gemm_w4a16_exact(a_bits, b_packed, sfb, scale_2) -> np.ndarray:
         raise ValueError("dot products are not exact in FP32")
     prod = np.float32(scale_2) * acc32        # one IEEE single multiply, RNE
     return f32_to_bf16(prod.astype(np.float32))
+
+
+def gemm_fp4_splitk_planes_ref(a_packed, sfa, b_packed, sfb, k_splits: int) -> np.ndarray:
+    """FP64 partial sums per K chunk of the FP4 GEMM (chunk rule of
+    splitk_chunk): planes[s] = sum over k in chunk s of deq(A) * deq(B).
+    Each plane is the FP4 definition (gemm_fp4_ref) on its own K range."""
+    a = dequant_fp4(a_packed, sfa)
+    b = dequant_fp4(b_packed, sfb)
+    k = a.shape[1]
+    kc = splitk_chunk(k, k_splits)
+    planes = np.zeros((k_splits, a.shape[0], b.shape[0]), np.float64)
+    for s in range(k_splits):
+        lo, hi = min(k, s * kc), min(k, (s + 1) * kc)
+        planes[s] = a[:, lo:hi] @ b[:, lo:hi].T
+    return planes

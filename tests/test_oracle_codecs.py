@@ -123,3 +123,28 @@ def test_e2m1_times_e4m3_is_exact_in_bf16():
 def test_oracle_does_not_import_the_library():
     src = open(codecs.__file__).read() + open(oracle.gemm.__file__).read()
     assert "block_scaled_fp4_gemm_amd" not in src
+
+
+# NVIDIA blocked scale layout (kernelbot NVFP4 page, "SCALE FACTORS")
+
+@pytest.mark.parametrize("rows,k_groups,batch", [(128, 4, 1), (256, 12, 1), (384, 8, 3)])
+def test_scales_from_blocked_matches_grouped_reshape(rows, k_groups, batch):
+    """The element loop equals the page's grouping
+    'g_m i_m tile_m i_k tile_k l -> (tile_m i_m g_m) (tile_k i_k) l' applied to
+    the stored order (l, tile_m, tile_k, g_m, i_m, i_k) by reshape/transpose."""
+    rng = np.random.default_rng(rows + k_groups + batch)
+    flat = rng.integers(0, 256, size=batch * rows * k_groups, dtype=np.uint8)
+    tm, tk = rows // 128, k_groups // 4
+    stored = flat.reshape(batch, tm, tk, 32, 4, 4)             # l tile_m tile_k g_m i_m i_k
+    grouped = stored.transpose(0, 1, 4, 3, 2, 5).reshape(batch, rows, k_groups)
+    assert np.array_equal(oracle.scales_from_blocked(flat, rows, k_groups, batch), grouped)
+
+
+def test_scales_from_blocked_closed_form_positions():
+    """One 128 x 4 block whose bytes hold their own offset g_m*16 + i_m*4 + i_k:
+    plain[i, j] = (i % 32)*16 + (i // 32)*4 + j, from i = i_m*32 + g_m, j = i_k."""
+    flat = np.arange(512, dtype=np.int64).astype(np.uint8)     # offsets mod 256
+    got = oracle.scales_from_blocked(flat, 128, 4, 1)[0]
+    i = np.arange(128)[:, None]
+    j = np.arange(4)[None, :]
+    assert np.array_equal(got, ((i % 32) * 16 + (i // 32) * 4 + j).astype(np.uint8))

@@ -417,3 +417,25 @@ def test_w4a16_on_dequantized_activations_equals_fp4_times_scale():
     b = synthetic.fp4_packed(n, k, 94, 1)
     sfb = synthetic.e4m3_uniform(n, k // 16, 2 ** -4, 2 ** 4, 94, 5)
     assert np.array_equal(oracle.gemm_w4a16_ref(a, b, sfb, 0.5), 0.5 * oracle.gemm_fp4_ref(qa, one, b, sfb))
+
+
+@pytest.mark.parametrize("k,ks", [(1024, 4), (4096, 8), (160, 3)])
+def test_fp4_splitk_planes_sum_and_slices(k, ks):
+    """FP4 split-K planes: each is the FP4 definition on its K slice of the
+    packed bytes and scales, and they sum exactly to the full FP4 result."""
+    m, n = 3, 5
+    a = synthetic.fp4_packed(m, k, 95, 0)
+    b = synthetic.fp4_packed(n, k, 95, 1)
+    sfa = synthetic.e4m3_choice(m, k // 16, [0x38, 0x40, 0x30], 95, 4)
+    sfb = synthetic.e4m3_choice(n, k // 16, [0x38, 0x40, 0x30], 95, 5)
+    planes = oracle.gemm_fp4_splitk_planes_ref(a, sfa, b, sfb, ks)
+    kc = oracle.splitk_chunk(k, ks)
+    for s in range(ks):
+        lo, hi = min(k, s * kc), min(k, (s + 1) * kc)
+        if hi == lo:
+            assert not planes[s].any()
+            continue
+        want = oracle.gemm_fp4_ref(a[:, lo // 2:hi // 2], sfa[:, lo // 16:hi // 16],
+                                   b[:, lo // 2:hi // 2], sfb[:, lo // 16:hi // 16])
+        assert np.array_equal(planes[s], want)
+    assert np.array_equal(planes.sum(axis=0), oracle.gemm_fp4_ref(a, sfa, b, sfb))
