@@ -9,8 +9,8 @@ HBM before timing starts. `value` = 3 * 2*M*N*K flops per step / step time.
 
 Every other row of the hot path is timed in the same run and reported under
 "rows": attention projections, the fused LoRA fold (HBM roofline), the
-order-preserving router GEMM (FP32 VALU roofline), the block-scaled FP4 GEMM,
-W4A16 and the small dense case, each warm and after a 1 GiB cache flush
+order-preserving router GEMM (FP32 VALU roofline), the block-scaled FP4 GEMM
+(and its M = 128 decode shapes through split-K), W4A16 and the small dense case, each warm and after a 1 GiB cache flush
 (median with p20/p80), each with the oracle timed beside it on a bounded
 sample of its rows (`oracle_*` fields, extrapolated to the full problem).
 
@@ -370,6 +370,36 @@ def measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream, oracle_seconds
         lambda r0, r1: oracle.gemm_fp4_ref(a4[r0:r1], sfa[r0:r1], b4, sfb), 4096, 16, oracle_seconds))
     log("fp4", rows["fp4_4096x4096x8192"])
     del A4, SA, B4, SB, C
+
+    # the kernelbot page's decode shapes (M = 128) through FP4 split-K, best
+    # k_splits of 4/8/16. Bounds: the 16-bit MFMA rate (exact dequantization)
+    # and HBM for the algorithmic bytes (A, B, scales read once, C written once).
+    for m, n, k in ((128, 7168, 16384), (128, 4096, 7168)):
+        ad, sad, bd, sbd = synthetic.fp4_decode(m=m, n=n, k=k)
+        AD, SAD, BD, SBD = u8(ad), u8(sad), u8(bd), u8(sbd)
+        C = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        WS = torch.empty((16, m, n), dtype=torch.float32, device=dev)
+        best = None
+        for ks in (4, 8, 16):
+            w, c = timed(lambda: bg.gemm_fp4_blockscaled_splitk(AD, SAD, BD, SBD, ks, workspace=WS[:ks], out=C))
+            if best is None or w < best[1]:
+                best = (ks, w, c, dict(spread))
+        ks, w, c, sp = best
+        fl = 2.0 * m * n * k
+        byts = m * k // 2 + n * k // 2 + (m + n) * k // 16 + m * n * 2
+        key = f"fp4_decode_{m}x{n}x{k}"
+        rows[key] = {"us_warm": round(w, 2), "us_cold": round(c, 2), "k_splits": ks,
+                     "us_warm_p20_p80": sp["warm"], "us_cold_p20_p80": sp["cold"],
+                     "tflops_warm": round(fl / w / 1e6, 1), "frac_bf16_peak_warm": round(fl / w / 1e6 / BF16_PEAK_TFLOPS, 4),
+                     "gbs_cold": round(byts / c / 1e3, 1), "frac_hbm_cold": round(byts / c / 1e3 / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes": byts,
+                     "bound_us": {"mfma_16bit": round(fl / BF16_PEAK_TFLOPS / 1e6, 2),
+                                  "hbm": round(byts / HBM_PEAK_GBS / 1e3, 2)}}
+        rows[key].update(oracle_timing(lambda r0, r1: oracle.gemm_fp4_ref(ad, sad, bd[r0:r1], sbd[r0:r1]),
+                                       n, 64, oracle_seconds))
+        rows[key]["oracle_sample"] += " (output columns)"
+        log("fp4 decode", rows[key])
+        del AD, SAD, BD, SBD, C, WS
 
     aw, bw, sw, s2 = synthetic.w4a16_gemm()
     AW, BW, SW = up16(aw), u8(bw), u8(sw)

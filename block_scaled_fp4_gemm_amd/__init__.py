@@ -36,6 +36,9 @@ _SIGS = {
     "gemm_bf16_ordered_f32": [_p, _p, _p, _u32, _u32, _u32, _p],
     "gemm_fp4_blockscaled": [_p, _p, _p, _p, _p, _u32, _u32, _u32, _p],
     "gemm_w4a16": [_p, _p, _p, _f32, _p, _u32, _u32, _u32, _p],
+    "gemm_fp4_blockscaled_batched": [_p, _p, _p, _p, _p, _u32, _u32, _u32, _u32, _p],
+    "gemm_fp4_blockscaled_splitk": [_p, _p, _p, _p, _p, _p, _sz, _u32, _u32, _u32, _u32, _p],
+    "fp4_scales_from_blocked": [_p, _p, _u32, _u32, _u32, _p],
     "bf16_scaled_add": [_p, _p, _sz, _f32, _p],
 }
 for _name, _args in _SIGS.items():
@@ -190,6 +193,50 @@ def gemm_fp4_blockscaled(a: torch.Tensor, sfa: torch.Tensor, b: torch.Tensor, sf
         out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
     _check(lib.gemm_fp4_blockscaled(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(out), m, n, k,
                                     _stream(stream)), "gemm_fp4_blockscaled")
+    return out
+
+
+def gemm_fp4_blockscaled_batched(a: torch.Tensor, sfa: torch.Tensor, b: torch.Tensor, sfb: torch.Tensor,
+                                 out: torch.Tensor | None = None, stream=None):
+    """C[l] = bf16(deq(A[l]) @ deq(B[l])^T) for A [L,M,K/2], SFA [L,M,K/16], B [L,N,K/2], SFB [L,N,K/16]."""
+    for t in (a, sfa, b, sfb):
+        if t.element_size() != 1 or t.dim() != 3:
+            raise TypeError("batched FP4 operands and scales are 3-D byte tensors")
+    l, m, kh = a.shape
+    n = b.shape[1]
+    if out is None:
+        out = torch.empty((l, m, n), dtype=torch.bfloat16, device=a.device)
+    _check(lib.gemm_fp4_blockscaled_batched(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(out), m, n, 2 * kh, l,
+                                            _stream(stream)), "gemm_fp4_blockscaled_batched")
+    return out
+
+
+def gemm_fp4_blockscaled_splitk(a: torch.Tensor, sfa: torch.Tensor, b: torch.Tensor, sfb: torch.Tensor,
+                                k_splits: int, workspace: torch.Tensor | None = None,
+                                out: torch.Tensor | None = None, stream=None):
+    """FP4 GEMM through k_splits FP32 planes (workspace of k_splits*M*N floats, allocated if None)."""
+    m, kh = a.shape
+    n = b.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    if workspace is None and k_splits > 1:
+        workspace = torch.empty((k_splits, m, n), dtype=torch.float32, device=a.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * 4
+    _check(lib.gemm_fp4_blockscaled_splitk(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(out), _ptr(workspace),
+                                           ws_bytes, m, n, 2 * kh, k_splits, _stream(stream)),
+           "gemm_fp4_blockscaled_splitk")
+    return out
+
+
+def fp4_scales_from_blocked(blocked: torch.Tensor, rows: int, k_groups: int, batch: int = 1,
+                            out: torch.Tensor | None = None, stream=None):
+    """Plain [batch, rows, k_groups] scale bytes from the blocked (l, tile_m, tile_k, 32, 4, 4) layout."""
+    if blocked.element_size() != 1:
+        raise TypeError("scales are byte tensors")
+    if out is None:
+        out = torch.empty((batch, rows, k_groups), dtype=torch.uint8, device=blocked.device)
+    _check(lib.fp4_scales_from_blocked(_ptr(blocked), _ptr(out), rows, k_groups, batch, _stream(stream)),
+           "fp4_scales_from_blocked")
     return out
 
 

@@ -84,6 +84,28 @@ bg_status check_dense(const void* A, const void* B, const void* out, uint32_t M,
     return BG_OK;
 }
 
+// Common checks of an FP4 problem with `batch` problems stored one after
+// another: A [M,K/2], SFA [M,K/16], B [N,K/2], SFB [N,K/16], out of
+// out_bytes per problem.
+bg_status check_fp4(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
+                    const void* out, uint64_t out_bytes, uint32_t M, uint32_t N, uint32_t K,
+                    uint32_t batch) {
+    const uint64_t a_bytes = (uint64_t)batch * M * (K / 2), sa_bytes = (uint64_t)batch * M * (K / 16);
+    const uint64_t b_bytes = (uint64_t)batch * N * (K / 2), sb_bytes = (uint64_t)batch * N * (K / 16);
+    const uint64_t c_bytes = (uint64_t)batch * out_bytes;
+    if (missing(A, a_bytes) || missing(SFA, sa_bytes) || missing(B, b_bytes) || missing(SFB, sb_bytes) ||
+        missing(out, c_bytes))
+        return BG_ERR_NULL;
+    if (misaligned(A, a_bytes) || misaligned(SFA, sa_bytes) || misaligned(B, b_bytes) ||
+        misaligned(SFB, sb_bytes) || misaligned(out, c_bytes))
+        return BG_ERR_ALIGN;
+    const Range rc = range_of(out, c_bytes);
+    if (overlap(rc, range_of(A, a_bytes)) || overlap(rc, range_of(SFA, sa_bytes)) ||
+        overlap(rc, range_of(B, b_bytes)) || overlap(rc, range_of(SFB, sb_bytes)))
+        return BG_ERR_ALIAS;
+    return BG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -198,25 +220,65 @@ bg_status gemm_bf16_ordered_f32(const uint16_t* A, const uint16_t* B, float* C32
 bg_status gemm_fp4_blockscaled(const uint8_t* A, const uint8_t* SFA, const uint8_t* B,
                                const uint8_t* SFB, uint16_t* C, uint32_t M, uint32_t N, uint32_t K,
                                void* stream) {
+    return gemm_fp4_blockscaled_batched(A, SFA, B, SFB, C, M, N, K, 1, stream);
+}
+
+bg_status gemm_fp4_blockscaled_batched(const uint8_t* A, const uint8_t* SFA, const uint8_t* B,
+                                       const uint8_t* SFB, uint16_t* C, uint32_t M, uint32_t N,
+                                       uint32_t K, uint32_t L, void* stream) {
+    if (!dims_ok(M, N, K) || (K % 16) != 0 || L > 65535) return BG_ERR_SHAPE;
+    if (M == 0 || N == 0 || L == 0) return BG_OK;
+    bg_status s = check_fp4(A, SFA, B, SFB, C, (uint64_t)M * N * 2, M, N, K, L);
+    if (s != BG_OK) return s;
+    if ((s = check_device()) != BG_OK) return s;
+    bg::Fp4Problem p{A, SFA, B, SFB, C, M, N, K, K, 1, L};
+    return launched(bg::launch_fp4(p, (hipStream_t)stream));
+}
+
+bg_status gemm_fp4_blockscaled_splitk(const uint8_t* A, const uint8_t* SFA, const uint8_t* B,
+                                      const uint8_t* SFB, uint16_t* C, float* workspace,
+                                      size_t workspace_bytes, uint32_t M, uint32_t N, uint32_t K,
+                                      uint32_t k_splits, void* stream) {
+    if (k_splits == 0 || k_splits > kMaxSplits) return BG_ERR_SHAPE;
     if (!dims_ok(M, N, K) || (K % 16) != 0) return BG_ERR_SHAPE;
     if (M == 0 || N == 0) return BG_OK;
-    const uint64_t a_bytes = (uint64_t)M * (K / 2), sa_bytes = (uint64_t)M * (K / 16);
-    const uint64_t b_bytes = (uint64_t)N * (K / 2), sb_bytes = (uint64_t)N * (K / 16);
-    const uint64_t c_bytes = (uint64_t)M * N * 2;
-    if (missing(A, a_bytes) || missing(SFA, sa_bytes) || missing(B, b_bytes) ||
-        missing(SFB, sb_bytes) || missing(C, c_bytes))
-        return BG_ERR_NULL;
-    if (misaligned(A, a_bytes) || misaligned(SFA, sa_bytes) || misaligned(B, b_bytes) ||
-        misaligned(SFB, sb_bytes) || misaligned(C, c_bytes))
-        return BG_ERR_ALIGN;
-    const Range rc = range_of(C, c_bytes);
-    if (overlap(rc, range_of(A, a_bytes)) || overlap(rc, range_of(SFA, sa_bytes)) ||
-        overlap(rc, range_of(B, b_bytes)) || overlap(rc, range_of(SFB, sb_bytes)))
+    bg_status s = check_fp4(A, SFA, B, SFB, C, (uint64_t)M * N * 2, M, N, K, 1);
+    if (s != BG_OK) return s;
+    if (k_splits == 1) {
+        if ((s = check_device()) != BG_OK) return s;
+        bg::Fp4Problem p{A, SFA, B, SFB, C, M, N, K, K, 1, 1};
+        return launched(bg::launch_fp4(p, (hipStream_t)stream));
+    }
+    const uint64_t per = ((uint64_t)K + k_splits - 1) / k_splits;
+    const uint32_t chunk = (uint32_t)((per + 63) / 64 * 64);
+    const uint64_t need = (uint64_t)k_splits * M * N * 4;
+    if (workspace == nullptr || workspace_bytes < need) return BG_ERR_WORKSPACE;
+    if (misaligned(workspace, need)) return BG_ERR_ALIGN;
+    const Range rw = range_of(workspace, need);
+    if (overlap(rw, range_of(A, (uint64_t)M * (K / 2))) || overlap(rw, range_of(SFA, (uint64_t)M * (K / 16))) ||
+        overlap(rw, range_of(B, (uint64_t)N * (K / 2))) || overlap(rw, range_of(SFB, (uint64_t)N * (K / 16))) ||
+        overlap(rw, range_of(C, (uint64_t)M * N * 2)))
         return BG_ERR_ALIAS;
+    if ((s = check_device()) != BG_OK) return s;
+    const hipStream_t st = (hipStream_t)stream;
+    bg::Fp4Problem p{A, SFA, B, SFB, workspace, M, N, K, chunk, k_splits, 1};
+    hipError_t e = bg::launch_fp4(p, st);
+    if (e != hipSuccess) return BG_ERR_LAUNCH;
+    return launched(bg::launch_splitk_reduce(workspace, C, M, N, k_splits, st));
+}
+
+bg_status fp4_scales_from_blocked(const uint8_t* blocked, uint8_t* plain, uint32_t rows,
+                                  uint32_t k_groups, uint32_t batch, void* stream) {
+    if (rows % 128 != 0 || k_groups % 4 != 0 || rows > kMaxDim || k_groups > kMaxDim || batch > 65535)
+        return BG_ERR_SHAPE;
+    const uint64_t bytes = (uint64_t)batch * rows * k_groups;
+    if (bytes == 0) return BG_OK;
+    if (missing(blocked, bytes) || missing(plain, bytes)) return BG_ERR_NULL;
+    if (misaligned(blocked, bytes) || misaligned(plain, bytes)) return BG_ERR_ALIGN;
+    if (overlap(range_of(blocked, bytes), range_of(plain, bytes))) return BG_ERR_ALIAS;
     bg_status s = check_device();
     if (s != BG_OK) return s;
-    bg::Fp4Problem p{A, SFA, B, SFB, C, M, N, K};
-    return launched(bg::launch_fp4(p, (hipStream_t)stream));
+    return launched(bg::launch_scales_from_blocked(blocked, plain, rows, k_groups, batch, (hipStream_t)stream));
 }
 
 bg_status gemm_w4a16(const uint16_t* A, const uint8_t* B, const uint8_t* SFB, float scale_2,

@@ -32,12 +32,15 @@ struct DenseProblem {
 };
 
 struct Fp4Problem {
-    const uint8_t* A;    // [M, K/2]
-    const uint8_t* SFA;  // [M, K/16]
-    const uint8_t* B;    // [N, K/2]
-    const uint8_t* SFB;  // [N, K/16]
-    uint16_t* C;         // [M, N] bf16
+    const uint8_t* A;    // [batch][M, K/2]
+    const uint8_t* SFA;  // [batch][M, K/16]
+    const uint8_t* B;    // [batch][N, K/2]
+    const uint8_t* SFB;  // [batch][N, K/16]
+    void* C;             // [batch][M, N] bf16, or [splits][M][N] f32 planes
     uint32_t M, N, K;
+    uint32_t k_chunk;    // K elements per split (multiple of 64, or K)
+    uint32_t splits;     // > 1: FP32 planes (batch must be 1)
+    uint32_t batch;
 };
 
 struct W4a16Problem {
@@ -55,6 +58,8 @@ struct W4a16Problem {
 // non-empty (M > 0, N > 0).
 hipError_t launch_dense(const DenseProblem& p, Epilogue epi, hipStream_t stream);
 hipError_t launch_fp4(const Fp4Problem& p, hipStream_t stream);
+hipError_t launch_scales_from_blocked(const uint8_t* src, uint8_t* dst, uint32_t rows, uint32_t k_groups,
+                                      uint32_t batch, hipStream_t stream);
 hipError_t launch_w4a16(const W4a16Problem& p, hipStream_t stream);
 hipError_t launch_ordered(const uint16_t* A, const uint16_t* B, void* C, bool f32_out,
                           uint32_t M, uint32_t N, uint32_t K, hipStream_t stream);

@@ -73,6 +73,9 @@ struct KParams {
     int tiles_m, tiles_n;
     float scale;
     int cus;               // compute units of the device (tile choice)
+    // batched FP4 (blockIdx.z = batch index): per-batch strides of Aq, SFA,
+    // Bq, SFB (bytes) and C (elements); zero for one problem
+    int64_t bs_a, bs_sa, bs_b, bs_sb, bs_c;
 };
 
 // Swizzled 16-byte chunk slot of logical chunk c in a tile row of CPR chunks
@@ -571,6 +574,14 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[FM][FN]) {
 template <int BM, int BN, int WM, int WN, int EPI, int SRC, int RSETS = 2>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_mfma_kernel(KParams p) {
+    if constexpr (SRC == SRC_FP4) {
+        const int64_t l = blockIdx.z;   // batch index (0 for one problem)
+        p.Aq += l * p.bs_a;
+        p.SFA += l * p.bs_sa;
+        p.Bq += l * p.bs_b;
+        p.SFB += l * p.bs_sb;
+        p.C = reinterpret_cast<uint16_t*>(p.C) + l * p.bs_c;
+    }
     constexpr int NT = WM * WN * 64;
     constexpr int TM = BM / WM, TN = BN / WN;   // wave sub-tile
     constexpr int FM = TM / 32, FN = TN / 32;   // 32x32 MFMA blocks per wave
@@ -868,11 +879,11 @@ gemm_mfma_direct_kernel(KParams p) {
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, int SRC, int RSETS = 2>
-hipError_t launch_cfg(const KParams& kp, int splits, hipStream_t stream) {
+hipError_t launch_cfg(const KParams& kp, int splits, hipStream_t stream, int batch = 1) {
     KParams q = kp;
     q.tiles_m = (kp.M + BM - 1) / BM;
     q.tiles_n = (kp.N + BN - 1) / BN;
-    dim3 grid((unsigned)(q.tiles_m * q.tiles_n), (unsigned)splits, 1);
+    dim3 grid((unsigned)(q.tiles_m * q.tiles_n), (unsigned)splits, (unsigned)batch);
     hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, EPI, SRC, RSETS>), grid, dim3(WM * WN * 64), 0,
                        stream, q);
     return hipGetLastError();
@@ -1141,15 +1152,65 @@ hipError_t launch_fp4(const Fp4Problem& p, hipStream_t stream) {
     kp.K = (int)p.K;
     kp.lda = kp.ldb = (int)p.K;
     kp.ldc = (int)p.N;
-    kp.k_chunk = (int)p.K;
-    const char* e = getenv("BLOCKGEMM_FP4_TILE");   // tuning only
-    const int cfg = e ? atoi(e) : 0;
-    switch (cfg) {
-        case 1: return launch_cfg<256, 256, 2, 4, EPI_STORE_BF16, SRC_FP4, 2>(kp, 1, stream);
-        case 2: return launch_cfg<128, 128, 2, 2, EPI_STORE_BF16, SRC_FP4, 2>(kp, 1, stream);
-        case 3: return launch_cfg<256, 256, 2, 2, EPI_STORE_BF16, SRC_FP4, 1>(kp, 1, stream);
-        default: return launch_cfg<256, 256, 2, 4, EPI_STORE_BF16, SRC_FP4, 1>(kp, 1, stream);
+    kp.k_chunk = (int)p.k_chunk;
+    const int splits = (int)p.splits, batch = (int)p.batch;
+    if (batch > 1) {
+        kp.bs_a = (int64_t)p.M * (p.K / 2);
+        kp.bs_sa = (int64_t)p.M * (p.K / 16);
+        kp.bs_b = (int64_t)p.N * (p.K / 2);
+        kp.bs_sb = (int64_t)p.N * (p.K / 16);
+        kp.bs_c = (int64_t)p.M * p.N;
     }
+    // FP32 planes (split-K) for the small-M decode shapes
+    if (splits > 1) {
+        int sk = env_int("BLOCKGEMM_FP4_SK_TILE");   // tuning only
+        if (sk < 0) sk = p.M <= 192 ? 3 : 2;
+        switch (sk) {
+            case 0: return launch_cfg<128, 128, 2, 2, EPI_STORE_F32, SRC_FP4, 2>(kp, splits, stream);
+            case 1: return launch_cfg<128, 256, 2, 4, EPI_STORE_F32, SRC_FP4, 1>(kp, splits, stream);
+            case 3: return launch_cfg<128, 256, 2, 4, EPI_STORE_F32, SRC_FP4, 2>(kp, splits, stream);
+            default: return launch_cfg<256, 256, 2, 4, EPI_STORE_F32, SRC_FP4, 1>(kp, splits, stream);
+        }
+    }
+    int cfg = env_int("BLOCKGEMM_FP4_TILE");   // tuning only
+    if (cfg < 0) cfg = p.M <= 192 ? 2 : 0;
+    switch (cfg) {
+        case 1: return launch_cfg<256, 256, 2, 4, EPI_STORE_BF16, SRC_FP4, 2>(kp, 1, stream, batch);
+        case 2: return launch_cfg<128, 128, 2, 2, EPI_STORE_BF16, SRC_FP4, 2>(kp, 1, stream, batch);
+        case 3: return launch_cfg<256, 256, 2, 2, EPI_STORE_BF16, SRC_FP4, 1>(kp, 1, stream, batch);
+        default: return launch_cfg<256, 256, 2, 4, EPI_STORE_BF16, SRC_FP4, 1>(kp, 1, stream, batch);
+    }
+}
+
+// Blocked (NVIDIA hardware) scale layout -> plain [L, rows, k_groups]: the
+// stored order is (l, tile_m, tile_k, g_m[32], i_m[4], i_k[4]); thread q
+// moves the 4 bytes of one (l, tile_m, tile_k, g_m, i_m) to plain row
+// tile_m*128 + i_m*32 + g_m, groups tile_k*4 .. tile_k*4 + 3.
+__global__ void __launch_bounds__(256)
+scales_from_blocked_kernel(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst, int rows,
+                           int k_groups, int64_t words) {
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= words) return;
+    const int tk = k_groups / 4, tm = rows / 128;
+    const int i_m = (int)(q & 3);
+    const int g_m = (int)((q >> 2) & 31);
+    int64_t r = q >> 7;                      // (l, tile_m, tile_k)
+    const int tile_k = (int)(r % tk);
+    r /= tk;
+    const int tile_m = (int)(r % tm);
+    const int64_t l = r / tm;
+    const int row = tile_m * 128 + i_m * 32 + g_m;
+    dst[(l * rows + row) * tk + tile_k] = src[q];
+}
+
+hipError_t launch_scales_from_blocked(const uint8_t* src, uint8_t* dst, uint32_t rows, uint32_t k_groups,
+                                      uint32_t batch, hipStream_t stream) {
+    const int64_t words = (int64_t)batch * rows * (k_groups / 4);
+    const int64_t blocks = (words + 255) / 256;
+    hipLaunchKernelGGL(scales_from_blocked_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const uint32_t*>(src), reinterpret_cast<uint32_t*>(dst), (int)rows,
+                       (int)k_groups, words);
+    return hipGetLastError();
 }
 
 hipError_t launch_w4a16(const W4a16Problem& p, hipStream_t stream) {

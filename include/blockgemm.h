@@ -180,6 +180,62 @@ bg_status gemm_fp4_blockscaled(const uint8_t* A, const uint8_t* SFA,
                                uint32_t M, uint32_t N, uint32_t K, void* stream);
 
 /*
+ * gemm_fp4_blockscaled_batched: L independent gemm_fp4_blockscaled problems
+ * of one shape, stored one after another (problem l of A at A + l*M*K/2, of
+ * SFA at SFA + l*M*K/16, of B and SFB likewise with N, of C at C + l*M*N).
+ *
+ * kernelbot NVFP4 GEMM page, custom_kernel docstring: a, b, the scales and c
+ * carry a batch dimension l, and the tensors are allocated l-major. The
+ * page's kernel asserts L == 1; the method does not need it.
+ *
+ *  L <= 65535 (BG_ERR_SHAPE otherwise); L == 0 is a no-op. Other rules as
+ *  gemm_fp4_blockscaled, over all L problems' bytes.
+ */
+bg_status gemm_fp4_blockscaled_batched(const uint8_t* A, const uint8_t* SFA,
+                                       const uint8_t* B, const uint8_t* SFB, uint16_t* C,
+                                       uint32_t M, uint32_t N, uint32_t K, uint32_t L,
+                                       void* stream);
+
+/*
+ * gemm_fp4_blockscaled_splitk: gemm_fp4_blockscaled through k_splits FP32
+ * partial planes, for shapes with few output tiles (the kernelbot page's
+ * decode-sized problems, M = 128).
+ *
+ *  Phase 1: workspace[s][i][j] = FP32 sum of deq(A)[i,k]*deq(B)[j,k] over
+ *           chunk s of K, chunks of ceil(K/k_splits) rounded up to 64.
+ *  Phase 2: C = bf16( ((ws[0] + ws[1]) + ...) ), planes added in ascending s.
+ *
+ * The split is gemm_dense.rs's dense_gemm_splitk (FP32 workspace of
+ * k_splits*M*N*4 bytes, then a BF16 reduce) applied to the block-scaled
+ * product. workspace_bytes >= k_splits*M*N*4 (gemm_bf16_splitk_workspace_bytes
+ * gives it) unless k_splits == 1, which writes C directly and ignores the
+ * workspace. 1 <= k_splits <= 64.
+ */
+bg_status gemm_fp4_blockscaled_splitk(const uint8_t* A, const uint8_t* SFA,
+                                      const uint8_t* B, const uint8_t* SFB, uint16_t* C,
+                                      float* workspace, size_t workspace_bytes,
+                                      uint32_t M, uint32_t N, uint32_t K, uint32_t k_splits,
+                                      void* stream);
+
+/*
+ * fp4_scales_from_blocked: plain [L, rows, k_groups] E4M3 scale bytes (the
+ * layout every FP4 entry point here takes) from NVIDIA's blocked hardware
+ * layout.
+ *
+ * kernelbot NVFP4 GEMM page, "SCALE FACTORS": the blocked tensor has shape
+ * [32, 4, rest_m, 4, rest_k, L] (dims g_m, i_m, tile_m, i_k, tile_k, l) and is
+ * stored in the order (l, tile_m, tile_k, g_m, i_m, i_k): 512-byte blocks of
+ * 128 rows x 4 groups. Plain row = tile_m*128 + i_m*32 + g_m, group =
+ * tile_k*4 + i_k.
+ *
+ *  blocked: batch*rows*k_groups bytes in that order (read).
+ *  plain:   [batch, rows, k_groups] bytes (written); must not overlap blocked.
+ *  rows % 128 == 0 and k_groups % 4 == 0 (BG_ERR_SHAPE otherwise).
+ */
+bg_status fp4_scales_from_blocked(const uint8_t* blocked, uint8_t* plain, uint32_t rows,
+                                  uint32_t k_groups, uint32_t batch, void* stream);
+
+/*
  * gemm_w4a16: C[i,j] = bf16( fl32( s2 * sum_k A[i,k] * w[j,k] ) ), FP32
  *   accumulation, w[j,k] = e2m1(B nibble [j,k]) * e4m3fn(SFB[j, k/16]),
  *   s2 = scale_2.

@@ -157,3 +157,9 @@ def w4a16_gemm(seed: int = 5, m: int = 1016, n: int = 12288, k: int = 2048):
     b = fp4_packed(n, k, seed, TID_B)
     sfb = e4m3_uniform(n, k // 16, 2.0 ** -4, 2.0 ** 4, seed, TID_SFB)
     return a, b, sfb, W4A16_SCALE_2
+
+
+def fp4_decode(seed: int = 6, m: int = 128, n: int = 7168, k: int = 16384):
+    """The kernelbot NVFP4 page's decode-sized problems (L=1, M=128; N, K =
+    7168, 16384 or 4096, 7168): operands and scales drawn as for fp4_gemm."""
+    return fp4_gemm(seed=seed, m=m, n=n, k=k)

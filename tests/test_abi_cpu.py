@@ -59,6 +59,9 @@ def test_empty_problems_are_ok_without_pointers():
     assert L.gemm_bf16_ordered(None, None, None, 0, 3, 3, None) == bg.BG_OK
     assert L.gemm_fp4_blockscaled(None, None, None, None, None, 0, 4, 32, None) == bg.BG_OK
     assert L.gemm_w4a16(None, None, None, 1.0, None, 3, 0, 32, None) == bg.BG_OK
+    assert L.gemm_fp4_blockscaled_batched(None, None, None, None, None, 4, 4, 32, 0, None) == bg.BG_OK
+    assert L.gemm_fp4_blockscaled_splitk(None, None, None, None, None, None, 0, 0, 4, 32, 4, None) == bg.BG_OK
+    assert L.fp4_scales_from_blocked(None, None, 128, 4, 0, None) == bg.BG_OK
     assert L.bf16_scaled_add(None, None, 0, 1.0, None) == bg.BG_OK
     assert L.gemm_bf16_splitk(None, None, None, None, 0, 0, 4, 64, 4, None) == bg.BG_OK
 
@@ -73,6 +76,8 @@ def test_null_pointers():
     assert L.gemm_fp4_blockscaled(A, None, B, S2, C, 4, 4, 32, None) == bg.BG_ERR_NULL
     assert L.gemm_w4a16(A, B, None, 1.0, C, 4, 4, 32, None) == bg.BG_ERR_NULL
     assert L.gemm_w4a16(None, B, S2, 1.0, C, 4, 4, 32, None) == bg.BG_ERR_NULL
+    assert L.gemm_fp4_blockscaled_batched(A, S1, B, None, C, 4, 4, 32, 2, None) == bg.BG_ERR_NULL
+    assert L.fp4_scales_from_blocked(S1, None, 128, 4, 1, None) == bg.BG_ERR_NULL
     assert L.bf16_scaled_add(None, B, 8, 1.0, None) == bg.BG_ERR_NULL
 
 
@@ -85,6 +90,8 @@ def test_misaligned_pointers():
     assert L.gemm_fp4_blockscaled(A, S1 + 1, B, S2, C, 4, 4, 32, None) == bg.BG_ERR_ALIGN
     assert L.gemm_w4a16(A, B + 8, S2, 1.0, C, 4, 4, 32, None) == bg.BG_ERR_ALIGN
     assert L.gemm_w4a16(A, B, S2, 1.0, C + 2, 4, 4, 32, None) == bg.BG_ERR_ALIGN
+    assert L.fp4_scales_from_blocked(S1 + 4, S2, 128, 4, 1, None) == bg.BG_ERR_ALIGN
+    assert L.gemm_fp4_blockscaled_splitk(A, S1, B, S2, C, W + 4, 1 << 20, 4, 4, 128, 2, None) == bg.BG_ERR_ALIGN
     assert L.gemm_bf16_splitk(A, B, C, W + 4, 1 << 20, 4, 4, 128, 2, None) == bg.BG_ERR_ALIGN
 
 
@@ -103,6 +110,10 @@ def test_aliasing_outputs():
     # W4A16 C overlaps the activations or the weight scales
     assert L.gemm_w4a16(A, B, S2, 1.0, A + 64, 4, 4, 32, None) == bg.BG_ERR_ALIAS
     assert L.gemm_w4a16(A, B, S2, 1.0, S2, 4, 4, 32, None) == bg.BG_ERR_ALIAS
+    # batched: the second problem's C (C + 4*4*2) runs into SFB placed right after the first
+    assert L.gemm_fp4_blockscaled_batched(A, S1, B, C + 32, C, 4, 4, 32, 2, None) == bg.BG_ERR_ALIAS
+    assert L.gemm_fp4_blockscaled_splitk(A, S1, B, S2, C, C, 1 << 20, 4, 4, 128, 2, None) == bg.BG_ERR_ALIAS
+    assert L.fp4_scales_from_blocked(S1, S1 + 256, 128, 4, 1, None) == bg.BG_ERR_ALIAS
     assert L.bf16_scaled_add(A, A + 16, 64, 1.0, None) == bg.BG_ERR_ALIAS
     # adjacent but disjoint ranges are fine up to the device check
     if torch.cuda.device_count() == 0:
@@ -114,6 +125,12 @@ def test_shape_rules():
     assert L.gemm_fp4_blockscaled(A, S1, B, S2, C, 4, 4, 40, None) == bg.BG_ERR_SHAPE   # K % 16
     assert L.gemm_w4a16(A, B, S2, 1.0, C, 4, 4, 40, None) == bg.BG_ERR_SHAPE             # K % 16
     assert L.gemm_w4a16(A, B, S2, 1.0, C, 4, 1 << 31, 32, None) == bg.BG_ERR_SHAPE
+    assert L.gemm_fp4_blockscaled_batched(A, S1, B, S2, C, 4, 4, 40, 2, None) == bg.BG_ERR_SHAPE
+    assert L.gemm_fp4_blockscaled_batched(A, S1, B, S2, C, 4, 4, 32, 70000, None) == bg.BG_ERR_SHAPE
+    assert L.gemm_fp4_blockscaled_splitk(A, S1, B, S2, C, W, 1 << 20, 4, 4, 40, 2, None) == bg.BG_ERR_SHAPE
+    assert L.gemm_fp4_blockscaled_splitk(A, S1, B, S2, C, W, 1 << 20, 4, 4, 32, 0, None) == bg.BG_ERR_SHAPE
+    assert L.fp4_scales_from_blocked(S1, S2, 100, 4, 1, None) == bg.BG_ERR_SHAPE      # rows % 128
+    assert L.fp4_scales_from_blocked(S1, S2, 128, 6, 1, None) == bg.BG_ERR_SHAPE      # k_groups % 4
     assert L.gemm_bf16_splitk(A, B, C, W, 1 << 30, 4, 4, 128, 0, None) == bg.BG_ERR_SHAPE
     assert L.gemm_bf16_splitk(A, B, C, W, 1 << 30, 4, 4, 128, 65, None) == bg.BG_ERR_SHAPE
     assert L.gemm_bf16(A, B, C, 1 << 31, 4, 4, None) == bg.BG_ERR_SHAPE
@@ -128,6 +145,8 @@ def test_workspace_rules():
     need = 2 * 4 * 4 * 4
     assert L.gemm_bf16_splitk(A, B, C, None, need, 4, 4, 128, 2, None) == bg.BG_ERR_WORKSPACE
     assert L.gemm_bf16_splitk(A, B, C, W, need - 1, 4, 4, 128, 2, None) == bg.BG_ERR_WORKSPACE
+    assert L.gemm_fp4_blockscaled_splitk(A, S1, B, S2, C, W, need - 1, 4, 4, 128, 2, None) == bg.BG_ERR_WORKSPACE
+    assert L.gemm_fp4_blockscaled_splitk(A, S1, B, S2, C, None, need, 4, 4, 128, 2, None) == bg.BG_ERR_WORKSPACE
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="valid call would launch on fake pointers")

@@ -83,3 +83,130 @@ def test_every_fp4_tile_config(cfg, monkeypatch):
         eb = synthetic.e4m3_choice(n, k // 16, [0x38, 0x40], 71, 5)
         want = oracle.f32_to_bf16(oracle.gemm_fp4_ref(a, ea, b, eb).astype(np.float32))
         assert_bits_equal(_run(a, ea, b, eb), want, f"fp4 cfg {cfg} exact {m}x{n}x{k}")
+
+
+# ---------------------------------------------------------------------------
+# batched FP4, FP4 split-K (decode shapes) and the blocked-scale importer
+# ---------------------------------------------------------------------------
+
+def test_fp4_batched_equals_per_problem_calls():
+    L, m, n, k = 3, 130, 66, 272
+    a = np.stack([synthetic.fp4_packed(m, k, 130 + l, 0) for l in range(L)])
+    b = np.stack([synthetic.fp4_packed(n, k, 130 + l, 1) for l in range(L)])
+    sfa = np.stack([synthetic.e4m3_uniform(m, k // 16, 2 ** -4, 2 ** 4, 130 + l, 4) for l in range(L)])
+    sfb = np.stack([synthetic.e4m3_uniform(n, k // 16, 2 ** -4, 2 ** 4, 130 + l, 5) for l in range(L)])
+    c = bg.gemm_fp4_blockscaled_batched(to_dev_u8(a), to_dev_u8(sfa), to_dev_u8(b), to_dev_u8(sfb))
+    torch.cuda.synchronize()
+    got = bits_of(c)
+    for l in range(L):
+        one = _run(a[l], sfa[l], b[l], sfb[l])
+        assert_bits_equal(got[l], one, f"batch {l} vs single call")
+        check_close(got[l], oracle.gemm_fp4_ref(a[l], sfa[l], b[l], sfb[l]), k,
+                    oracle.rms(oracle.dequant_fp4(a[l], sfa[l])), oracle.rms(oracle.dequant_fp4(b[l], sfb[l])),
+                    f"batch {l}")
+
+
+@pytest.mark.parametrize("m,n,k,ks", [(128, 512, 4096, 4), (65, 300, 1040, 3), (128, 256, 16384, 16)])
+def test_fp4_splitk_planes_and_result(m, n, k, ks):
+    print(f"fp4 splitk m={m} n={n} k={k} ks={ks}", flush=True)
+    a, b = synthetic.fp4_packed(m, k, 140, 0), synthetic.fp4_packed(n, k, 140, 1)
+    sfa = synthetic.e4m3_uniform(m, k // 16, 2 ** -4, 2 ** 4, 140, 4)
+    sfb = synthetic.e4m3_uniform(n, k // 16, 2 ** -4, 2 ** 4, 140, 5)
+    ws = torch.full((ks, m, n), float("nan"), dtype=torch.float32, device="cuda")
+    c = bg.gemm_fp4_blockscaled_splitk(to_dev_u8(a), to_dev_u8(sfa), to_dev_u8(b), to_dev_u8(sfb), ks, workspace=ws)
+    torch.cuda.synchronize()
+    planes = ws.cpu().numpy()
+    ref_planes = oracle.gemm_fp4_splitk_planes_ref(a, sfa, b, sfb, ks)
+    kc = oracle.splitk_chunk(k, ks)
+    sa, sb = oracle.rms(oracle.dequant_fp4(a, sfa)), oracle.rms(oracle.dequant_fp4(b, sfb))
+    for s in range(ks):
+        klen = max(0, min(k, (s + 1) * kc) - min(k, s * kc))
+        assert (np.abs(planes[s] - ref_planes[s]) <= oracle.tolerance(ref_planes[s], klen, sa, sb)).all(), f"plane {s}"
+    assert_bits_equal(bits_of(c), oracle.splitk_reduce(planes), "reduce")
+    check_close(bits_of(c), oracle.gemm_fp4_ref(a, sfa, b, sfb), k, sa, sb, "fp4 splitk result")
+
+
+def test_fp4_splitk_power_of_two_scales_bit_exact():
+    m, n, k = 128, 384, 8192
+    a, b = synthetic.fp4_packed(m, k, 141, 0), synthetic.fp4_packed(n, k, 141, 1)
+    sfa = synthetic.e4m3_choice(m, k // 16, [0x38, 0x40], 141, 4)
+    sfb = synthetic.e4m3_choice(n, k // 16, [0x38, 0x40], 141, 5)
+    want = oracle.f32_to_bf16(oracle.gemm_fp4_ref(a, sfa, b, sfb).astype(np.float32))
+    for ks in (1, 2, 8):
+        c = bg.gemm_fp4_blockscaled_splitk(to_dev_u8(a), to_dev_u8(sfa), to_dev_u8(b), to_dev_u8(sfb), ks)
+        torch.cuda.synchronize()
+        assert_bits_equal(bits_of(c), want, f"fp4 splitk exact ks={ks}")
+
+
+@pytest.mark.parametrize("n,k", [(7168, 16384), (4096, 7168)])
+def test_fp4_decode_shapes_sampled_columns(n, k):
+    """The kernelbot page's decode shapes (M = 128): all rows, 512 sampled
+    output columns, plain call and split-K."""
+    print(f"fp4 decode 128x{n}x{k}", flush=True)
+    m = 128
+    a, b = synthetic.fp4_packed(m, k, 142, 0), synthetic.fp4_packed(n, k, 142, 1)
+    sfa = synthetic.e4m3_uniform(m, k // 16, 2 ** -4, 2 ** 4, 142, 4)
+    sfb = synthetic.e4m3_uniform(n, k // 16, 2 ** -4, 2 ** 4, 142, 5)
+    cols = synthetic.sample_rows(n, 512, 1030)
+    ref = oracle.gemm_fp4_ref(a, sfa, b[cols], sfb[cols])
+    sa, sb = oracle.rms(oracle.dequant_fp4(a, sfa)), oracle.rms(oracle.dequant_fp4(b[cols], sfb[cols]))
+    da, dsa, db, dsb = to_dev_u8(a), to_dev_u8(sfa), to_dev_u8(b), to_dev_u8(sfb)
+    for ks in (1, 8):
+        c = bg.gemm_fp4_blockscaled_splitk(da, dsa, db, dsb, ks)
+        torch.cuda.synchronize()
+        check_close(bits_of(c)[:, cols], ref, k, sa, sb, f"decode 128x{n}x{k} ks={ks}")
+
+
+@pytest.mark.parametrize("rows,k_groups,batch", [(128, 4, 1), (256, 512, 1), (384, 12, 2)])
+def test_scales_from_blocked_bit_exact(rows, k_groups, batch):
+    rng = np.random.default_rng(rows + k_groups)
+    blocked = rng.integers(0, 256, size=batch * rows * k_groups, dtype=np.uint8)
+    got = bg.fp4_scales_from_blocked(to_dev_u8(blocked), rows, k_groups, batch)
+    torch.cuda.synchronize()
+    want = oracle.scales_from_blocked(blocked, rows, k_groups, batch)
+    assert np.array_equal(got.cpu().numpy(), want)
+
+
+def test_gemm_on_imported_scales_equals_plain_scales():
+    """Scales handed over in the blocked layout, imported on the GPU, give
+    the same product as the plain scales (inverse layout written here from
+    the page's row/group formula)."""
+    m, n, k = 256, 384, 1024
+    a, b = synthetic.fp4_packed(m, k, 143, 0), synthetic.fp4_packed(n, k, 143, 1)
+    sfa = synthetic.e4m3_uniform(m, k // 16, 2 ** -4, 2 ** 4, 143, 4)
+    sfb = synthetic.e4m3_uniform(n, k // 16, 2 ** -4, 2 ** 4, 143, 5)
+
+    def to_blocked(plain):
+        rows, groups = plain.shape
+        out = np.empty(rows * groups, np.uint8)
+        pos = 0
+        for tile_m in range(rows // 128):
+            for tile_k in range(groups // 4):
+                for g_m in range(32):
+                    for i_m in range(4):
+                        for i_k in range(4):
+                            out[pos] = plain[tile_m * 128 + i_m * 32 + g_m, tile_k * 4 + i_k]
+                            pos += 1
+        return out
+
+    isa = bg.fp4_scales_from_blocked(to_dev_u8(to_blocked(sfa)), m, k // 16)[0]
+    isb = bg.fp4_scales_from_blocked(to_dev_u8(to_blocked(sfb)), n, k // 16)[0]
+    c1 = bg.gemm_fp4_blockscaled(to_dev_u8(a), isa, to_dev_u8(b), isb)
+    c2 = bg.gemm_fp4_blockscaled(to_dev_u8(a), to_dev_u8(sfa), to_dev_u8(b), to_dev_u8(sfb))
+    torch.cuda.synchronize()
+    assert_bits_equal(bits_of(c1), bits_of(c2), "imported vs plain scales")
+
+
+@pytest.mark.parametrize("tile", [0, 1, 2, 3])
+def test_every_fp4_splitk_tile(tile, monkeypatch):
+    """Each FP4 split-K tile (BLOCKGEMM_FP4_SK_TILE, a tuning hook): planes
+    summed in order equal the exact result on power-of-two scales."""
+    monkeypatch.setenv("BLOCKGEMM_FP4_SK_TILE", str(tile))
+    for m, n, k, ks in [(128, 384, 4096, 8), (65, 129, 1040, 3), (300, 520, 2048, 5)]:
+        a, b = synthetic.fp4_packed(m, k, 150 + tile, 0), synthetic.fp4_packed(n, k, 150 + tile, 1)
+        sfa = synthetic.e4m3_choice(m, k // 16, [0x38, 0x40], 150, 4)
+        sfb = synthetic.e4m3_choice(n, k // 16, [0x38, 0x40], 150, 5)
+        c = bg.gemm_fp4_blockscaled_splitk(to_dev_u8(a), to_dev_u8(sfa), to_dev_u8(b), to_dev_u8(sfb), ks)
+        torch.cuda.synchronize()
+        want = oracle.f32_to_bf16(oracle.gemm_fp4_ref(a, sfa, b, sfb).astype(np.float32))
+        assert_bits_equal(bits_of(c), want, f"fp4 splitk tile {tile} {m}x{n}x{k} ks={ks}")
