@@ -27,6 +27,7 @@
 // ("SCALE FACTORS": one E4M3 scale per 16 K elements multiplied into each
 // E2M1 element, then an FP32-accumulated dot product).
 #include <cstdlib>
+#include <type_traits>
 
 #include "bg_internal.hpp"
 
@@ -155,10 +156,16 @@ struct Stager<ROWS, NT, SRC_BF16_VEC, BKS> {
     static constexpr int CPR = BKS / 8;
     static constexpr int PER = (ROWS * CPR + NT - 1) / NT;
     u32x4 r[PER];
+    uint32_t valid;   // bit i: chunk i lies inside the K range (applied when storing)
 
-    // ld: elements between consecutive rows (a multiple of 8)
+    // ld: elements between consecutive rows (a multiple of 8). Every lane
+    // loads (a chunk past k_end re-reads the row's last chunk before k_end
+    // and is stored as zeros), so the load has no branch around it, nothing
+    // reads its result before the store, and the wait counts are exact.
+    // k_end >= 8 whenever a step exists.
     __device__ __forceinline__ void load(const uint16_t* base, int row0, int nrows, int ld,
                                          int k0, int k_end, int tid) {
+        valid = 0u;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int q = tid + i * NT;
@@ -166,21 +173,25 @@ struct Stager<ROWS, NT, SRC_BF16_VEC, BKS> {
             const int row = q / CPR, c = q % CPR;
             const int grow = min(row0 + row, nrows - 1);
             const int gk = k0 + c * 8;
-            if (gk < k_end)
-                r[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)grow * ld + gk);
-            else
-                r[i] = u32x4{0u, 0u, 0u, 0u};
+            const int gkc = gk < k_end ? gk : max(k_end - 8, 0);
+            r[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)grow * ld + gkc);
+            valid |= (gk < k_end ? 1u : 0u) << i;
         }
     }
-    __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
+    // writes the chunks with lo <= i < hi
+    __device__ __forceinline__ void store_units(uint16_t* lds, int tid, int lo, int hi) const {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
+            if (i < lo || i >= hi) continue;
             const int q = tid + i * NT;
             if (PER * NT != ROWS * CPR && q >= ROWS * CPR) break;
             const int row = q / CPR, c = q % CPR;
-            *reinterpret_cast<u32x4*>(lds + row * BKS + chunk_slot<CPR>(row, c) * 8) = r[i];
+            const bool in = (valid >> i) & 1u;
+            *reinterpret_cast<u32x4*>(lds + row * BKS + chunk_slot<CPR>(row, c) * 8) =
+                in ? r[i] : u32x4{0u, 0u, 0u, 0u};
         }
     }
+    __device__ __forceinline__ void store(uint16_t* lds, int tid) const { store_units(lds, tid, 0, PER); }
 };
 
 // BF16 rows with an unaligned pitch: element-wise guarded loads.
@@ -209,15 +220,17 @@ struct Stager<ROWS, NT, SRC_BF16_SCALAR, BKS> {
                          h[6] | (h[7] << 16)};
         }
     }
-    __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
+    __device__ __forceinline__ void store_units(uint16_t* lds, int tid, int lo, int hi) const {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
+            if (i < lo || i >= hi) continue;
             const int q = tid + i * NT;
             if (PER * NT != ROWS * CPR && q >= ROWS * CPR) break;
             const int row = q / CPR, c = q % CPR;
             *reinterpret_cast<u32x4*>(lds + row * BKS + chunk_slot<CPR>(row, c) * 8) = r[i];
         }
     }
+    __device__ __forceinline__ void store(uint16_t* lds, int tid) const { store_units(lds, tid, 0, PER); }
 };
 
 // Block-scaled FP4: a unit is one 16-element scale group of one row (8 packed
@@ -280,9 +293,13 @@ struct Fp4Stager {
         }
     }
 
-    __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
+    __device__ __forceinline__ void store(uint16_t* lds, int tid) const { store_units(lds, tid, 0, PER); }
+
+    // converts and writes the units with lo <= i < hi
+    __device__ __forceinline__ void store_units(uint16_t* lds, int tid, int lo, int hi) const {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
+            if (i < lo || i >= hi) continue;
             const int u = tid + i * NT;
             const int row = u >> 2, g = u & 3;
             const bool in = (valid >> i) & 1u;
@@ -434,6 +451,23 @@ __device__ __forceinline__ void interleave_mfma() {
     if (ND > NM) __builtin_amdgcn_sched_group_barrier(0x100, ND - NM, 0);
 }
 
+// Sub-step schedule with operand conversion: NM MFMAs, each followed by an
+// LDS read (while ND last), up to NV VALU and up to NW LDS writes (spread
+// evenly), so the conversion's VALU work issues under the matrix core's
+// busy cycles.
+template <int NM, int ND, int NV, int NW>
+__device__ __forceinline__ void interleave_mfma_cvt() {
+    constexpr int V = (NV + NM - 1) / NM, W = (NW + NM - 1) / NM;
+#pragma unroll
+    for (int q = 0; q < NM; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // MFMA
+        if (q < ND) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // LDS read
+        if (V > 0) __builtin_amdgcn_sched_group_barrier(0x002, V, 0);          // VALU
+        if (W > 0 && q * W < NW) __builtin_amdgcn_sched_group_barrier(0x200, W, 0);   // LDS write
+    }
+    if (ND > NM) __builtin_amdgcn_sched_group_barrier(0x100, ND - NM, 0);
+}
+
 // Epilogue through LDS: each wave writes its accumulator tile into LDS, then
 // the whole workgroup streams complete rows to memory, 16 contiguous bytes
 // per lane (a wave covers 1 KB of consecutive row bytes per store), instead
@@ -551,6 +585,15 @@ __device__ __forceinline__ void staged_epilogue(const KParams& p, const f32x16 (
     }
 }
 
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 in order.
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (N > 0) {
+        static_for<N - 1>(f);
+        f(std::integral_constant<int, N - 1>{});
+    }
+}
+
 template <int FM, int FN>
 __device__ __forceinline__ void zero_acc(f32x16 (&acc)[FM][FN]) {
 #pragma unroll
@@ -610,8 +653,12 @@ gemm_mfma_kernel(KParams p) {
 
     constexpr int SRC_A = SRC == SRC_W4A16 ? SRC_BF16_VEC : SRC;
     constexpr int SRC_B = SRC == SRC_W4A16 ? SRC_FP4_BF16 : SRC;
-    Stager<BM, NT, SRC_A> sa0, sa1;
-    Stager<BN, NT, SRC_B> sb0, sb1;
+    // RSETS register sets form a ring: set r holds the steps t with t % RSETS == r
+    constexpr int NSETS = RSETS > 1 ? RSETS : 1;
+    Stager<BM, NT, SRC_A> sa[NSETS];
+    Stager<BN, NT, SRC_B> sb[NSETS];
+    Stager<BM, NT, SRC_A>& sa0 = sa[0];
+    Stager<BN, NT, SRC_B>& sb0 = sb[0];
     auto load = [&](auto& sa, auto& sb, int k0) {
         if constexpr (SRC == SRC_FP4) {
             sa.load(p.Aq, p.SFA, m0, p.M, p.K, k0, ke, tid);
@@ -632,31 +679,54 @@ gemm_mfma_kernel(KParams p) {
     if (nsteps > 0) {
         load(sa0, sb0, kb);
         store(sa0, sb0, smem);
+        // the other sets are loaded even past the end (clamped, zero-masked
+        // loads), so the loop below is one basic block with exact waits
+#pragma unroll
+        for (int r = 1; r < NSETS; ++r) load(sa[r], sb[r], kb + r * BK);
     }
-    if (RSETS == 2 && nsteps > 1) load(sa1, sb1, kb + BK);
     lds_barrier();
 
     bf16x8 fa[2][FM], fb[2][FN];
     if (nsteps > 0) load_frags<FM, FN, TM, TN, BK>(smem, smem + BM * BK, wm, wn, lane, 0, fa[0], fb[0]);
 
-    // One K step. `held` carries step t+1 (loaded during step t-1), `next`
-    // receives step t+2.
+    // Conversion of the held set is spread over the KK-1 leading sub-steps:
+    // part kk covers units [U*kk/(KK-1), U*(kk+1)/(KK-1)) of the U = PA + PB
+    // units (A's first), interleaved with that sub-step's MFMAs.
+    constexpr int PA = Stager<BM, NT, SRC_A>::PER, PB = Stager<BN, NT, SRC_B>::PER, U = PA + PB;
+    // approximate VALU instructions and LDS writes per unit, for the schedule
+    constexpr int VU_A = SRC_A == SRC_FP4 ? 24 : 0;
+    constexpr int VU_B = SRC_B == SRC_FP4 ? 24 : SRC_B == SRC_FP4_BF16 ? 32 : 0;
+    constexpr int WU_A = SRC_A == SRC_FP4 ? 2 : 1, WU_B = SRC_B == SRC_BF16_VEC || SRC_B == SRC_BF16_SCALAR ? 1 : 2;
+    constexpr int CVT_VALU = (PA * VU_A + PB * VU_B + KK - 2) / (KK - 1);
+    constexpr int CVT_DSW = (PA * WU_A + PB * WU_B + KK - 2) / (KK - 1);
+    auto store_part = [&](auto& sa, auto& sb, uint16_t* buf, int part) {
+        const int lo = U * part / (KK - 1), hi = U * (part + 1) / (KK - 1);
+        sa.store_units(buf, tid, lo, min(hi, PA));
+        sb.store_units(buf + BM * BK, tid, max(lo - PA, 0), hi - PA);
+    };
+
+    // One K step. `held` carries step t+1 (loaded RSETS-1 steps ago), `next`
+    // (step t's set, converted during step t-1) receives step t+RSETS. Loads
+    // past the last step read clamped addresses and convert to zeros, so
+    // nothing here branches.
     auto step = [&](int t, auto& held_a, auto& held_b, auto& next_a, auto& next_b) {
         const uint16_t* sA = smem + (t & 1) * STAGE;
-        if (t + 2 < nsteps) load(next_a, next_b, kb + (t + 2) * BK);
+        uint16_t* dst = smem + ((t + 1) & 1) * STAGE;
+        load(next_a, next_b, kb + (t + NSETS) * BK);
+        __builtin_amdgcn_sched_barrier(0);   // the loads lead the step: a whole step covers their latency
 #pragma unroll
         for (int kk = 0; kk + 1 < KK; ++kk) {
             const int cur = kk & 1;
             load_frags<FM, FN, TM, TN, BK>(sA, sA + BM * BK, wm, wn, lane, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
+            store_part(held_a, held_b, dst, kk);
             mfma_block<FM, FN, SRC == SRC_FP4>(fa[cur], fb[cur], acc);
-            interleave_mfma<FM * FN, FM + FN, 0>();
-            if (kk == 0 && t + 1 < nsteps) store(held_a, held_b, smem + ((t + 1) & 1) * STAGE);
+            interleave_mfma_cvt<FM * FN, FM + FN, CVT_VALU, CVT_DSW>();
         }
-        if (t + 1 < nsteps) {
-            lds_barrier();   // step t+1 is in LDS for every wave; step t's buffer is free
-            const uint16_t* nA = smem + ((t + 1) & 1) * STAGE;
-            load_frags<FM, FN, TM, TN, BK>(nA, nA + BM * BK, wm, wn, lane, 0, fa[LAST ^ 1], fb[LAST ^ 1]);
-        }
+        // step t+1 is in LDS for every wave; step t's buffer is free. Past the
+        // last step this reads a buffer of zeros (harmless).
+        lds_barrier();
+        const uint16_t* nA = smem + ((t + 1) & 1) * STAGE;
+        load_frags<FM, FN, TM, TN, BK>(nA, nA + BM * BK, wm, wn, lane, 0, fa[LAST ^ 1], fb[LAST ^ 1]);
         mfma_block<FM, FN, SRC == SRC_FP4>(fa[LAST], fb[LAST], acc);
         interleave_mfma<FM * FN, FM + FN, 0>();
     };
@@ -675,9 +745,17 @@ gemm_mfma_kernel(KParams p) {
         for (int kk = 0; kk + 1 < KK; ++kk) {
             const int cur = kk & 1;
             load_frags<FM, FN, TM, TN, BK>(sA, sA + BM * BK, wm, wn, lane, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
-            if (kk == KK - 2) store(sa0, sb0, smem + ((t + 1) & 1) * STAGE);
-            mfma_block<FM, FN, SRC == SRC_FP4>(fa[cur], fb[cur], acc);
-            interleave_mfma<FM * FN, FM + FN, 0>();
+            if (kk == KK - 2) {
+                // not earlier: hoisted conversions would wait for the loads
+                // just issued
+                __builtin_amdgcn_sched_barrier(0);
+                store(sa0, sb0, smem + ((t + 1) & 1) * STAGE);
+                mfma_block<FM, FN, SRC == SRC_FP4>(fa[cur], fb[cur], acc);
+                interleave_mfma_cvt<FM * FN, FM + FN, CVT_VALU * (KK - 1), CVT_DSW * (KK - 1)>();
+            } else {
+                mfma_block<FM, FN, SRC == SRC_FP4>(fa[cur], fb[cur], acc);
+                interleave_mfma<FM * FN, FM + FN, 0>();
+            }
         }
         if (t + 1 < nsteps) {
             lds_barrier();
@@ -688,11 +766,13 @@ gemm_mfma_kernel(KParams p) {
         interleave_mfma<FM * FN, FM + FN, 0>();
     };
 
-    if constexpr (RSETS == 2) {
-        for (int t = 0; t < nsteps; t += 2) {
-            step(t, sa1, sb1, sa0, sb0);
-            if (t + 1 < nsteps) step(t + 1, sa0, sb0, sa1, sb1);
-        }
+    if constexpr (RSETS > 1) {
+        // whole rounds of RSETS steps: steps past the end multiply zeros
+        for (int t = 0; t < nsteps; t += NSETS)
+            static_for<NSETS>([&](auto rc) {
+                constexpr int r = decltype(rc)::value;
+                step(t + r, sa[(r + 1) % NSETS], sb[(r + 1) % NSETS], sa[r], sb[r]);
+            });
     } else {
         for (int t = 0; t < nsteps; ++t) step1(t);
     }
@@ -1118,7 +1198,7 @@ struct W4a16Choice {
 };
 constexpr W4a16Choice kW4a16Choices[] = {
     {0, 256, 256, 1, 985.0},
-    {4, 128, 384, 1, 760.0},   // 1016 x 12288: 256 tiles, exactly one round
+    {6, 128, 384, 1, 810.0},   // 1016 x 12288: 256 tiles, exactly one round
     {1, 128, 256, 1, 850.0},
     {2, 128, 128, 2, 800.0},
 };
@@ -1169,6 +1249,9 @@ hipError_t launch_fp4(const Fp4Problem& p, hipStream_t stream) {
             case 0: return launch_cfg<128, 128, 2, 2, EPI_STORE_F32, SRC_FP4, 2>(kp, splits, stream);
             case 1: return launch_cfg<128, 256, 2, 4, EPI_STORE_F32, SRC_FP4, 1>(kp, splits, stream);
             case 3: return launch_cfg<128, 256, 2, 4, EPI_STORE_F32, SRC_FP4, 2>(kp, splits, stream);
+            case 4: return launch_cfg<128, 256, 2, 4, EPI_STORE_F32, SRC_FP4, 3>(kp, splits, stream);
+            case 5: return launch_cfg<128, 256, 2, 4, EPI_STORE_F32, SRC_FP4, 4>(kp, splits, stream);
+            case 6: return launch_cfg<128, 128, 2, 2, EPI_STORE_F32, SRC_FP4, 4>(kp, splits, stream);
             default: return launch_cfg<256, 256, 2, 4, EPI_STORE_F32, SRC_FP4, 1>(kp, splits, stream);
         }
     }
@@ -1178,6 +1261,11 @@ hipError_t launch_fp4(const Fp4Problem& p, hipStream_t stream) {
         case 1: return launch_cfg<256, 256, 2, 4, EPI_STORE_BF16, SRC_FP4, 2>(kp, 1, stream, batch);
         case 2: return launch_cfg<128, 128, 2, 2, EPI_STORE_BF16, SRC_FP4, 2>(kp, 1, stream, batch);
         case 3: return launch_cfg<256, 256, 2, 2, EPI_STORE_BF16, SRC_FP4, 1>(kp, 1, stream, batch);
+        case 5: return launch_cfg<128, 256, 2, 4, EPI_STORE_BF16, SRC_FP4, 2>(kp, 1, stream, batch);
+        case 6: return launch_cfg<256, 128, 4, 2, EPI_STORE_BF16, SRC_FP4, 2>(kp, 1, stream, batch);
+        case 7: return launch_cfg<128, 256, 2, 4, EPI_STORE_BF16, SRC_FP4, 3>(kp, 1, stream, batch);
+        case 8: return launch_cfg<256, 128, 4, 2, EPI_STORE_BF16, SRC_FP4, 3>(kp, 1, stream, batch);
+        case 9: return launch_cfg<128, 256, 2, 4, EPI_STORE_BF16, SRC_FP4, 4>(kp, 1, stream, batch);
         default: return launch_cfg<256, 256, 2, 4, EPI_STORE_BF16, SRC_FP4, 1>(kp, 1, stream, batch);
     }
 }
@@ -1234,6 +1322,9 @@ hipError_t launch_w4a16(const W4a16Problem& p, hipStream_t stream) {
         case 3: return launch_cfg<256, 256, 2, 2, EPI_SCALE_BF16, SRC_W4A16, 1>(kp, 1, stream);
         case 4: return launch_cfg<128, 384, 2, 4, EPI_SCALE_BF16, SRC_W4A16, 1>(kp, 1, stream);
         case 5: return launch_cfg<256, 192, 2, 3, EPI_SCALE_BF16, SRC_W4A16, 1>(kp, 1, stream);
+        case 6: return launch_cfg<128, 384, 2, 4, EPI_SCALE_BF16, SRC_W4A16, 2>(kp, 1, stream);
+        case 7: return launch_cfg<128, 256, 2, 4, EPI_SCALE_BF16, SRC_W4A16, 2>(kp, 1, stream);
+        case 9: return launch_cfg<128, 256, 2, 4, EPI_SCALE_BF16, SRC_W4A16, 3>(kp, 1, stream);
         default: return launch_cfg<256, 256, 2, 4, EPI_SCALE_BF16, SRC_W4A16, 1>(kp, 1, stream);
     }
 }

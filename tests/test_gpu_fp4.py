@@ -67,7 +67,7 @@ def test_fp4_config_sampled_rows():
                 oracle.rms(oracle.dequant_fp4(b, sfb)), "fp4 config")
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 5, 6, 7, 8, 9])
 def test_every_fp4_tile_config(cfg, monkeypatch):
     """Each FP4 tile variant (BLOCKGEMM_FP4_TILE, a tuning hook) on ragged shapes."""
     monkeypatch.setenv("BLOCKGEMM_FP4_TILE", str(cfg))
@@ -197,7 +197,7 @@ def test_gemm_on_imported_scales_equals_plain_scales():
     assert_bits_equal(bits_of(c1), bits_of(c2), "imported vs plain scales")
 
 
-@pytest.mark.parametrize("tile", [0, 1, 2, 3])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6])
 def test_every_fp4_splitk_tile(tile, monkeypatch):
     """Each FP4 split-K tile (BLOCKGEMM_FP4_SK_TILE, a tuning hook): planes
     summed in order equal the exact result on power-of-two scales."""

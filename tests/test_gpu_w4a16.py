@@ -55,7 +55,7 @@ def test_w4a16_qkvz_workload_all_rows():
     _check(a, b, sfb, s2, what="w4a16 qkvz")
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 6, 7, 9])
 def test_every_w4a16_tile_config(cfg, monkeypatch):
     """Each W4A16 tile variant (BLOCKGEMM_W4A16_TILE, a tuning hook) on ragged shapes."""
     monkeypatch.setenv("BLOCKGEMM_W4A16_TILE", str(cfg))
