@@ -116,22 +116,29 @@ def main():
     def down(ks):
         bg.gemm_bf16_splitk(H, Wd, ks, workspace=WS, out=D)
 
-    # choose the down-projection split during warm-up
+    # Choose the down-projection split during warm-up, in context: whole
+    # steps (gate, up, down) with each candidate, in interleaved rounds, so
+    # the clock state the down GEMM sees is the one of the timed loop.
+    def step_with(ks):
+        bg.gemm_bf16(X, Wg, out=G)
+        bg.gemm_bf16(X, Wu, out=U)
+        down(ks)
+
     if args.splitk == "auto":
-        best = None
-        for ks in (1, 2, 4, 8):
-            for _ in range(3):
-                down(ks)
-            s = ev()
-            for _ in range(10):
-                down(ks)
-            e = ev()
-            torch.cuda.synchronize()
-            t = s.elapsed_time(e) / 10
-            log(f"down k_splits={ks}: {t * 1e3:.1f} us")
-            if best is None or t < best[1]:
-                best = (ks, t)
-        ks_down = best[0]
+        cands = (1, 2, 4, 8)
+        times = {ks: [] for ks in cands}
+        for _ in range(3):
+            for ks in cands:
+                step_with(ks)
+                s = ev()
+                for _ in range(5):
+                    step_with(ks)
+                e = ev()
+                torch.cuda.synchronize()
+                times[ks].append(s.elapsed_time(e) / 5)
+        for ks in cands:
+            log(f"step with down k_splits={ks}: {np.median(times[ks]) * 1e3:.1f} us (median of 3 rounds)")
+        ks_down = min(cands, key=lambda k: float(np.median(times[k])))
     else:
         ks_down = int(args.splitk)
 

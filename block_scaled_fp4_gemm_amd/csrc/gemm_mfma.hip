@@ -1044,6 +1044,7 @@ hipError_t launch_tile_cfg(const KParams& kp, int splits, int cfg, hipStream_t s
         case 15: return launch_direct<160, 256, 64, 1, 8, 2, EPI>(kp, splits, stream);
         case 16: return launch_direct<320, 128, 64, 2, 2, 2, EPI>(kp, splits, stream);
         case 17: return launch_direct<160, 128, 64, 1, 4, 3, EPI>(kp, splits, stream);
+        case 23: return launch_direct<128, 128, 64, 2, 2, 3, EPI>(kp, splits, stream);
         default: return launch_direct<256, 128, 64, 4, 2, 3, EPI>(kp, splits, stream);   // 10
     }
 }
@@ -1059,16 +1060,20 @@ hipError_t launch_tile_cfg(const KParams& kp, int splits, int cfg, hipStream_t s
 // launch with the tile that finishes them fastest (usually one round of a
 // half-size tile). Every output is still produced by one tile walking K in
 // the same order, so the result is bit-identical to the unsplit launch.
+// `rate` holds with occ blocks on every CU; `rate1` with one block per CU
+// (problems of at most one tile per CU), lower for the two-block tiles,
+// whose latency the second block hides.
 struct TileChoice {
     int cfg, bm, bn, occ;
-    double rate;
+    double rate, rate1;
 };
 constexpr TileChoice kTileChoices[] = {
-    {2, 256, 256, 1, 1096.0},
-    {8, 160, 256, 1, 972.0},
-    {10, 256, 128, 1, 900.0},
-    {9, 160, 128, 2, 884.0},
-    {6, 128, 128, 2, 808.0},
+    {2, 256, 256, 1, 1096.0, 1096.0},
+    {8, 160, 256, 1, 972.0, 972.0},
+    {10, 256, 128, 1, 900.0, 900.0},
+    {9, 160, 128, 2, 884.0, 819.0},
+    {6, 128, 128, 2, 808.0, 671.0},
+    {23, 128, 128, 1, 763.0, 763.0},   // three stages: 5120 x 512, 160 tiles
 };
 constexpr double kLaunchGapUs = 2.0;   // second launch of a column split
 
@@ -1083,7 +1088,8 @@ double dp_us(const TileChoice& c, int M, int N, int K, int splits, int cus) {
     const double slots = (double)cus * c.occ;
     const double rounds = tiles <= cus ? 1.0 : (double)(int64_t)((tiles + slots - 1) / slots);
     const double occ = tiles <= cus ? 1.0 : c.occ;
-    return rounds * occ * 2.0 * c.bm * c.bn * ((double)K / splits) * cus / (c.rate * 1e6);
+    const double rate = tiles <= cus ? c.rate1 : c.rate;
+    return rounds * occ * 2.0 * c.bm * c.bn * ((double)K / splits) * cus / (rate * 1e6);
 }
 
 const TileChoice* best_single(int M, int N, int K, int splits, int cus, double* t_out) {
