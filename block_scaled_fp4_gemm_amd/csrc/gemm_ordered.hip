@@ -13,8 +13,8 @@
 // Design (CDNA4): a workgroup of 16x16 threads owns a (16*RM) x (16*RN)
 // output tile; each thread keeps an RM x RN block of accumulators. K is
 // walked in steps of KT; each step stages A and B rows as FP32 into LDS,
-// K-major ([k][row]). The per-output k order is untouched by the tiling:
-// tiles are visited in ascending k and, inside a tile, k ascends.
+// row-major with a padded pitch. The per-output k order is untouched by the
+// tiling: tiles are visited in ascending k and, inside a tile, k ascends.
 #include <cmath>
 #include <cstdlib>
 
@@ -39,10 +39,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
 }
 
 // Stage rows [row0, row0+ROWS) x k in [k0, k0+KT) of a [nrows, K] BF16 matrix
-// into lds[k][ROWS] as FP32. Positions with k >= K, or rows >= nrows, get 0.
-// A unit is 8 consecutive k of one row; consecutive threads take consecutive
-// rows, so the eight FP32 writes of a unit land in distinct banks.
-template <int ROWS, int NT, int LD>
+// into lds[row][LDK] as FP32 (row-major, LDK = KT + 4 floats per row).
+// Positions with k >= K, or rows >= nrows, get 0. A unit is 8 consecutive k
+// of one row, written as two 16-byte stores; consecutive threads take
+// consecutive rows.
+template <int ROWS, int NT, int LDK>
 __device__ __forceinline__ void stage(float* lds, const uint16_t* src, int row0, int nrows,
                                       int K, int k0, bool vec, int tid) {
     constexpr int UNITS = ROWS * (KT / 8);
@@ -62,26 +63,32 @@ __device__ __forceinline__ void stage(float* lds, const uint16_t* src, int row0,
             for (int x = 0; x < 8; ++x)
                 h[x] = (grow < nrows && gk + x < K) ? (uint32_t)src[(int64_t)grow * K + gk + x] : 0u;
         }
-#pragma unroll
-        for (int x = 0; x < 8; ++x) lds[(c * 8 + x) * LD + row] = bf16_bits_to_f32(h[x]);
+        float* dst = lds + row * LDK + c * 8;
+        *reinterpret_cast<f32x4*>(dst) = f32x4{bf16_bits_to_f32(h[0]), bf16_bits_to_f32(h[1]),
+                                               bf16_bits_to_f32(h[2]), bf16_bits_to_f32(h[3])};
+        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{bf16_bits_to_f32(h[4]), bf16_bits_to_f32(h[5]),
+                                                   bf16_bits_to_f32(h[6]), bf16_bits_to_f32(h[7])};
     }
 }
 
 // A workgroup of 16 x 16 threads owns a (16*RM) x (16*RN) output tile; thread
-// (tx, ty) keeps outputs rows ty + 16*i (i < RM) x cols tx*RN + j (j < RN).
-// A rows are read as broadcast 4-byte LDS loads (16 threads share one row
-// set), B columns as RN-wide loads. The register block size is chosen per
-// shape so the number of waves lands just below a multiple of the SIMD
-// count: the work is pure VALU, and a SIMD holding one wave more than the
-// others sets the runtime.
+// (tx, ty) keeps outputs rows ty + 16*i (i < RM) x cols tx + 16*j (j < RN).
+// Each 16-byte LDS read brings four consecutive k of one row, so a thread
+// reads RM + RN vectors per four k and then runs the 4*RM*RN multiply-add
+// pairs in ascending k. With a 36-float row pitch the 16 rows that the 16
+// lanes of a row group read start in 16 disjoint groups of four banks (A
+// rows are shared by 16 lanes and broadcast). The register block size is
+// chosen per shape so the number of waves lands just below a multiple of the
+// SIMD count: the work is pure VALU, and a SIMD holding one wave more than
+// the others sets the runtime.
 template <int RM, int RN, bool F32_OUT>
 __global__ void __launch_bounds__(256)
 gemm_ordered_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* C,
                     int M, int N, int K, int tiles_n) {
     constexpr int TM = 16 * RM, TN = 16 * RN;
-    constexpr int LDA = TM + (TM % 2 == 0 ? 1 : 0);   // odd stride: staging writes spread over banks
-    __shared__ __attribute__((aligned(16))) float sA[KT * LDA];
-    __shared__ __attribute__((aligned(16))) float sB[KT * TN];
+    constexpr int LDK = KT + 4;
+    __shared__ __attribute__((aligned(16))) float sA[TM * LDK];
+    __shared__ __attribute__((aligned(16))) float sB[TN * LDK];
 
     const int tid = threadIdx.x;
     const int tx = tid & 15, ty = tid >> 4;
@@ -97,30 +104,27 @@ gemm_ordered_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__
 
     for (int k0 = 0; k0 < K; k0 += KT) {
         __syncthreads();
-        stage<TM, 256, LDA>(sA, A, m0, M, K, k0, vec, tid);
-        stage<TN, 256, TN>(sB, B, n0, N, K, k0, vec, tid);
+        stage<TM, 256, LDK>(sA, A, m0, M, K, k0, vec, tid);
+        stage<TN, 256, LDK>(sB, B, n0, N, K, k0, vec, tid);
         __syncthreads();
+        // Groups of four k; past K the staged values are zero, and adding the
+        // product +0 leaves every accumulator unchanged (an accumulator that
+        // starts at +0 never becomes -0 under round to nearest).
         const int kn = min(KT, K - k0);
 #pragma unroll 2
-        for (int kk = 0; kk < kn; ++kk) {
-            float a[RM], b[RN];
+        for (int kc = 0; kc < kn; kc += 4) {
+            f32x4 a[RM], b[RN];
 #pragma unroll
-            for (int i = 0; i < RM; ++i) a[i] = sA[kk * LDA + ty + 16 * i];
-            if constexpr (RN == 4) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(&sB[kk * TN + tx * 4]);
-                b[0] = v.x; b[1] = v.y; b[2] = v.z; b[3] = v.w;
-            } else if constexpr (RN == 2) {
-                const float2 v = *reinterpret_cast<const float2*>(&sB[kk * TN + tx * 2]);
-                b[0] = v.x; b[1] = v.y;
-            } else {
+            for (int i = 0; i < RM; ++i) a[i] = *reinterpret_cast<const f32x4*>(&sA[(ty + 16 * i) * LDK + kc]);
 #pragma unroll
-                for (int j = 0; j < RN; ++j) b[j] = sB[kk * TN + tx * RN + j];
-            }
+            for (int j = 0; j < RN; ++j) b[j] = *reinterpret_cast<const f32x4*>(&sB[(tx + 16 * j) * LDK + kc]);
 #pragma unroll
-            for (int i = 0; i < RM; ++i)
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
-                for (int j = 0; j < RN; ++j)
-                    acc[i][j] = __fadd_rn(acc[i][j], __fmul_rn(a[i], b[j]));
+                for (int i = 0; i < RM; ++i)
+#pragma unroll
+                    for (int j = 0; j < RN; ++j)
+                        acc[i][j] = __fadd_rn(acc[i][j], __fmul_rn(a[i][q], b[j][q]));
         }
     }
 
@@ -130,7 +134,7 @@ gemm_ordered_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__
         if (m >= M) continue;
 #pragma unroll
         for (int j = 0; j < RN; ++j) {
-            const int n = n0 + tx * RN + j;
+            const int n = n0 + tx + 16 * j;
             if (n >= N) continue;
             if constexpr (F32_OUT)
                 reinterpret_cast<float*>(C)[(int64_t)m * N + n] = acc[i][j];
@@ -219,11 +223,12 @@ scaled_add_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ delta
 }  // namespace
 
 // Register-block choice, fitted to MI355X measurements of this kernel: the
-// VALU loop needs about three waves per SIMD to hide LDS and dependency
-// latency (one wave per SIMD runs at roughly half speed even when the waves
-// split evenly), two-column blocks read B most cheaply, and a larger block
-// reuses its operands better. Score = min(waves per SIMD, 3) x column factor
-// x (outputs per thread)^(1/4); the highest score wins.
+// VALU loop needs four to five waves per SIMD to hide LDS and dependency
+// latency (one wave per SIMD runs at roughly half speed), single-column
+// blocks amortize their A reads worst, and a larger block reuses its
+// operands better. Score = min(waves per SIMD, 4.5) x column factor x
+// (outputs per thread)^(1/4); the highest score wins. Measured: 4510 x 256 x
+// 2048 picks 2x2 (152 us), 2255 x 256 x 2048 picks 2x1 (111 us).
 namespace {
 struct OrdChoice {
     int rm, rn;
@@ -256,7 +261,7 @@ hipError_t launch_ordered(const uint16_t* A, const uint16_t* B, void* C, bool f3
             const double waves = 4.0 * ((M + 16 * rm - 1) / (16 * rm)) * (double)((N + 16 * rn - 1) / (16 * rn));
             const double per_simd = waves / simds;
             const double col = rn == 2 ? 1.0 : (rn == 4 ? 0.9 : 0.85);
-            const double score = (per_simd < 3.0 ? per_simd : 3.0) * col * std::sqrt(std::sqrt((double)(rm * rn)));
+            const double score = (per_simd < 4.5 ? per_simd : 4.5) * col * std::sqrt(std::sqrt((double)(rm * rn)));
             if (score > best) {
                 best = score;
                 pick = c;
