@@ -330,7 +330,7 @@ template <int ROWS, int NT>
 struct Stager<ROWS, NT, SRC_FP4_BF16, BK> : Fp4Stager<ROWS, NT, false> {};
 
 // ---------------------------------------------------------------------------
-// Direct global -> LDS staging (gfx950 global_load_lds_dwordx4) for BF16 rows
+// Direct global -> LDS staging (buffer_load_dwordx4 ... lds) for BF16 rows
 // with a 16-byte-multiple pitch. One instruction moves 64 lanes x 16 bytes
 // into one contiguous 1 KB LDS segment (lane i lands at byte 16*i), i.e.
 // 512/BKS tile rows of 2*BKS bytes. The XOR swizzle is applied on the global
@@ -351,24 +351,43 @@ struct DirectStager {
     static constexpr int PER = (SEGS + NW - 1) / NW;
     static_assert(SEGS * RPS == ROWS && RPS * CPR == 64, "whole 1 KB segments");
 
-    __device__ __forceinline__ static void issue(const uint16_t* base, int row0, int nrows, int ld,
-                                                 int k0, uint16_t* lds_tile, int wave, int lane) {
+    // Buffer form: the tile's rows are addressed through a buffer resource
+    // based at row row0, so each lane's offset (its row and swizzled chunk)
+    // is a 32-bit constant for the whole K walk and the K position is a
+    // scalar offset: no per-step vector address arithmetic. Needs
+    // ROWS * ld * 2 < 2^32 (checked by the host).
+    uint32_t voff[PER];
+    __amdgpu_buffer_rsrc_t rsrc;
+
+    __device__ __forceinline__ void init(const uint16_t* base, int row0, int nrows, int ld, int wave, int lane) {
+        rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + (int64_t)row0 * ld), (short)0,
+                                                 0x7FFFFFFF, 0x00020000);
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             const int seg = min(wave + j * NW, SEGS - 1);
             const int row = seg * RPS + lane / CPR;
             const int c = chunk_slot<CPR>(row, lane % CPR);
-            const int grow = min(row0 + row, nrows - 1);
-            const uint16_t* g = base + (int64_t)grow * ld + k0 + c * 8;
+            const int lrow = min(row0 + row, nrows - 1) - row0;
+            voff[j] = (uint32_t)(lrow * ld + c * 8) * 2u;
+        }
+    }
+
+    __device__ __forceinline__ void issue_buf(int k0, uint16_t* lds_tile, int wave) const {
+        const uint32_t soff = (uint32_t)k0 * 2u;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int seg = min(wave + j * NW, SEGS - 1);
             const uint32_t l = (uint32_t)(uintptr_t)(
                 (__attribute__((address_space(3))) uint16_t*)(lds_tile + seg * 512));
             // Emitted as inline assembly on purpose: the compiler's wait
             // insertion cannot tell the ring buffers apart and would make every
             // later LDS read wait for these loads. Their completion is tracked
             // explicitly with s_waitcnt vmcnt before each step barrier.
-            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(l));
+            asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff[j]), "s"(rsrc), "s"(soff),
+                         "{m0}"(l));
         }
     }
+
 };
 
 // ---------------------------------------------------------------------------
@@ -816,9 +835,13 @@ __device__ __forceinline__ void direct_mainloop(const KParams& p, uint16_t* smem
     const int ragged = (ke - kb) % BKS;
     const int nsteps = (ke - kb) / BKS + (ragged ? 1 : 0);
 
+    DirectStager<BM, NT, BKS> dsa;
+    DirectStager<BN, NT, BKS> dsb;
+    dsa.init(p.A, m0, p.M, p.lda, wave, lane);
+    dsb.init(p.B, n0, p.N, p.ldb, wave, lane);
     auto issue = [&](int k0, uint16_t* buf) {
-        DirectStager<BM, NT, BKS>::issue(p.A, m0, p.M, p.lda, k0, buf, wave, lane);
-        DirectStager<BN, NT, BKS>::issue(p.B, n0, p.N, p.ldb, k0, buf + BM * BKS, wave, lane);
+        dsa.issue_buf(k0, buf, wave);
+        dsb.issue_buf(k0, buf + BM * BKS, wave);
     };
 
     // Direct loads are issued at a uniform rate: STAGES stages in the
@@ -1176,8 +1199,11 @@ hipError_t launch_dense(const DenseProblem& p, Epilogue epi, hipStream_t stream)
     kp.k_chunk = (int)p.k_chunk;
     kp.scale = p.scale;
     kp.cus = p.cus > 0 ? (int)p.cus : 256;
-    // whole 16-byte chunks on 16-byte-aligned rows (the base pointers are)
-    const bool vec = (p.K % 8) == 0 && (p.lda % 8) == 0 && (p.ldb % 8) == 0;
+    // whole 16-byte chunks on 16-byte-aligned rows (the base pointers are),
+    // and row pitches whose largest tile (320 rows) spans less than 2 GB, the
+    // range of the direct kernels' 32-bit buffer offsets
+    const bool vec = (p.K % 8) == 0 && (p.lda % 8) == 0 && (p.ldb % 8) == 0 &&
+                     (int64_t)p.lda * 640 < (int64_t(1) << 31) && (int64_t)p.ldb * 640 < (int64_t(1) << 31);
     const int splits = (int)p.splits;
     switch (epi) {
         case EPI_STORE_BF16:
