@@ -373,9 +373,15 @@ struct DirectStager {
     }
 
     __device__ __forceinline__ void issue_buf(int k0, uint16_t* lds_tile, int wave) const {
+        issue_range(k0, lds_tile, wave, 0, PER);
+    }
+
+    // the loads j with lo <= j < hi (all of them: issue_buf)
+    __device__ __forceinline__ void issue_range(int k0, uint16_t* lds_tile, int wave, int lo, int hi) const {
         const uint32_t soff = (uint32_t)k0 * 2u;
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
+            if (j < lo || j >= hi) continue;
             const int seg = min(wave + j * NW, SEGS - 1);
             const uint32_t l = (uint32_t)(uintptr_t)(
                 (__attribute__((address_space(3))) uint16_t*)(lds_tile + seg * 512));
@@ -843,6 +849,16 @@ __device__ __forceinline__ void direct_mainloop(const KParams& p, uint16_t* smem
         dsa.issue_buf(k0, buf, wave);
         dsb.issue_buf(k0, buf + BM * BKS, wave);
     };
+    // Part q of KK of one stage's loads (A's first, then B's): a stage
+    // refilled inside the loop is issued over KK sub-steps instead of at once,
+    // which spreads the chip's L2 requests over the whole step.
+    constexpr int PA = DirectStager<BM, NT, BKS>::PER;
+    auto issue_part = [&](int k0, uint16_t* buf, int q) {
+        constexpr int NP = BKS / 16;
+        const int lo = L * q / NP, hi = L * (q + 1) / NP;
+        dsa.issue_range(k0, buf, wave, lo, min(hi, PA));
+        dsb.issue_range(k0, buf + BM * BKS, wave, max(lo - PA, 0), hi - PA);
+    };
 
     // Direct loads are issued at a uniform rate: STAGES stages in the
     // prologue and exactly one per loop iteration, so "stage t+1 has landed"
@@ -889,10 +905,18 @@ __device__ __forceinline__ void direct_mainloop(const KParams& p, uint16_t* smem
     bf16x8 fa[2][FM], fb[2][FN];
     if (nsteps > 0) load_frags<FM, FN, TM, TN, BKS>(smem, smem + BM * BKS, wm, wn, lane, 0, fa[0], fb[0]);
 
-    auto leading_substeps = [&](const uint16_t* sA) {
+    // The stage refilled after a step's barrier: part 0 right after the
+    // barrier, parts 1..KK-1 at the starts of the next step's leading
+    // sub-steps, all before that step's wait, so the wait count below still
+    // holds (every stage up to t+STAGES-1 fully issued at step t's wait).
+    bool pend = false;
+    int pk = 0;
+    uint16_t* pbuf = smem;
+    auto leading_substeps = [&](const uint16_t* sA, bool parts) {
 #pragma unroll
         for (int kk = 0; kk + 1 < KK; ++kk) {
             const int cur = kk & 1;
+            if (parts) issue_part(pk, pbuf, kk + 1);
             load_frags<FM, FN, TM, TN, BKS>(sA, sA + BM * BKS, wm, wn, lane, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
             mfma_block<FM, FN>(fa[cur], fb[cur], acc);
             interleave_mfma<FM * FN, FM + FN, 0>();
@@ -900,18 +924,23 @@ __device__ __forceinline__ void direct_mainloop(const KParams& p, uint16_t* smem
     };
 
     for (int t = 0; t + 1 < nsteps; ++t) {
-        leading_substeps(smem + (t % STAGES) * STAGE);
+        leading_substeps(smem + (t % STAGES) * STAGE, pend);
         wait_vmcnt<(STAGES >= 2 ? (STAGES - 2) * L : 0)>();   // stage t+1 landed for this wave
         lds_barrier();                    // ... and for every wave; stage t is free
-        issue(min(k_next, k_last), smem + (t % STAGES) * STAGE);
+        pend = true;
+        pk = min(k_next, k_last);
+        pbuf = smem + (t % STAGES) * STAGE;
         k_next += BKS;
+        issue_part(pk, pbuf, 0);
         const uint16_t* nA = smem + ((t + 1) % STAGES) * STAGE;
         load_frags<FM, FN, TM, TN, BKS>(nA, nA + BM * BKS, wm, wn, lane, 0, fa[LAST ^ 1], fb[LAST ^ 1]);
         mfma_block<FM, FN>(fa[LAST], fb[LAST], acc);
         interleave_mfma<FM * FN, FM + FN, 0>();
     }
     if (nsteps > 0) {
-        leading_substeps(smem + ((nsteps - 1) % STAGES) * STAGE);
+        // the stage pending here lies past the end (never read): its other
+        // parts are not issued
+        leading_substeps(smem + ((nsteps - 1) % STAGES) * STAGE, false);
         mfma_block<FM, FN>(fa[LAST], fb[LAST], acc);
     }
     wait_vmcnt<0>();   // drain the re-loads past the end before LDS is reused or the wave exits
