@@ -56,6 +56,8 @@ def parse():
                    help="oracle time budget per row (0 skips the per-row oracle timings)")
     p.add_argument("--calib-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (counter calibration) and exit")
+    p.add_argument("--profile-rows", action="store_true",
+                   help="only run every row's call 3 times, untimed (for counter passes), and exit")
     return p.parse_args()
 
 
@@ -93,6 +95,10 @@ def main():
 
     def u8(b):
         return torch.from_numpy(np.ascontiguousarray(b)).to(dev)
+
+    if args.profile_rows:
+        profile_rows(bg, synthetic, torch, up16, u8, dev)
+        return
 
     t_gen = time.time()
     x_np, wg_np = synthetic.mlp_gate_up()
@@ -174,6 +180,18 @@ def main():
     achieved = flops_gemm / (gu_avg * 1e-3) / 1e12
     log(f"step {ms_step * 1e3:.1f} us: gate/up {gu_avg * 1e3:.1f} us avg, down {np.mean(down_ms) * 1e3:.1f} us avg")
 
+    # GPU engine clock while the same step runs on (outside the timed region):
+    # the BF16 peak at the measured clock puts the achieved rate in context.
+    clocks = sample_sclk(lambda: step(), seconds=0.3, sync=torch.cuda.synchronize)
+    if clocks is not None:
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        peak_at = cus * 4096 * clocks["sclk_mhz_mean"] * 1e6 / 1e12
+        clocks["cus"] = cus
+        clocks["bf16_peak_at_sclk_tflops"] = round(peak_at, 1)
+        clocks["gate_up_frac_at_sclk"] = round(achieved / peak_at, 4)
+        log(f"sclk {clocks['sclk_mhz_mean']:.0f} MHz mean over {clocks['samples']} samples: "
+            f"BF16 peak at that clock {peak_at:.0f} TFLOP/s")
+
     roofline = {
         "bound": "mfma",
         "kernel": ("gemm_bf16 MLP gate/up call 5120x11008x2048 (per call): gemm_mfma_direct_kernel 256x256 "
@@ -207,6 +225,7 @@ def main():
         "gate_up_us": round(gu_avg * 1e3, 2),
         "down_us": round(float(np.mean(down_ms)) * 1e3, 2),
         "roofline": roofline,
+        "clocks": clocks,
     }
 
     if not args.no_rows:
@@ -220,6 +239,57 @@ def main():
             [("gate", x_np, wg_np), ("up", x_np, wu_np), ("down", h_np, wd_np)], args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
+
+
+def sample_sclk(run_once, seconds, sync):
+    """Runs run_once() back to back for about `seconds` while a thread reads
+    the active engine-clock level (the line marked '*' in the driver's
+    pp_dpm_sclk file) every 2 ms. Returns the mean MHz and the sample count,
+    or None when no such file is readable."""
+    import glob
+    import threading
+    paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+
+    def read(path):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if "*" in line:
+                        return float(line.split(":")[1].strip().lower().split("mhz")[0])
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    paths = [p for p in paths if read(p) is not None]
+    if not paths:
+        return None
+    samples = {p: [] for p in paths}
+    stop = threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            for p in paths:
+                v = read(p)
+                if v is not None:
+                    samples[p].append(v)
+            time.sleep(0.002)
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t_end = time.time() + seconds
+    while time.time() < t_end:
+        for _ in range(10):
+            run_once()
+        sync()
+    stop.set()
+    th.join()
+    # the GPU under load is the card whose clock ran highest
+    best = max(paths, key=lambda p: sum(samples[p]) / max(1, len(samples[p])))
+    v = samples[best]
+    if not v:
+        return None
+    return {"sclk_mhz_mean": round(sum(v) / len(v), 1), "sclk_mhz_min": min(v), "sclk_mhz_max": max(v),
+            "samples": len(v), "source": best}
 
 
 def traffic_for_current_kernel():
@@ -236,6 +306,47 @@ def traffic_for_current_kernel():
         return rec.get("traffic_bytes_per_launch")
     except (OSError, ValueError):
         return None
+
+
+def profile_rows(bg, synthetic, torch, up16, u8, dev):
+    """Every row's library call on its workload, three times each, in the
+    order of the per-row table (kernel names tell the rows apart in a
+    counter pass)."""
+    calls = []
+    a, b = synthetic.attn_proj()
+    A, B = up16(a), up16(b)
+    calls.append(("attn_qo", lambda: bg.gemm_bf16(A, B)))
+    a2, b2 = synthetic.attn_proj(n=512)
+    A2, B2 = up16(a2), up16(b2)
+    calls.append(("attn_kv", lambda: bg.gemm_bf16(A2, B2)))
+    x, w = synthetic.mlp_gate_up()
+    X, W = up16(x), up16(w)
+    calls.append(("mlp_gate_up", lambda: bg.gemm_bf16(X, W)))
+    h, wd = synthetic.mlp_down()
+    H, WD = up16(h), up16(wd)
+    calls.append(("mlp_down_k1", lambda: bg.gemm_bf16(H, WD)))
+    out, xl, bl, sc = synthetic.lora_fold()
+    O, XL, BL = up16(out), up16(xl), up16(bl)
+    calls.append(("lora_fold", lambda: bg.gemm_bf16_scaled_acc(XL, BL, O, sc)))
+    for m in (4510, 2255):
+        xr, wr = synthetic.router(m=m)
+        XR, WR = up16(xr), up16(wr)
+        calls.append((f"router_{m}", lambda XR=XR, WR=WR: bg.gemm_bf16_ordered(XR, WR)))
+    fa, fsa, fb, fsb = synthetic.fp4_gemm()
+    FA, FSA, FB, FSB = u8(fa), u8(fsa), u8(fb), u8(fsb)
+    calls.append(("fp4", lambda: bg.gemm_fp4_blockscaled(FA, FSA, FB, FSB)))
+    da, dsa, db, dsb = synthetic.fp4_decode()
+    DA, DSA, DB, DSB = u8(da), u8(dsa), u8(db), u8(dsb)
+    WS = torch.empty(8 * 128 * 7168, dtype=torch.float32, device=dev)
+    calls.append(("fp4_decode_k8", lambda: bg.gemm_fp4_blockscaled_splitk(DA, DSA, DB, DSB, 8, workspace=WS)))
+    wa, wb, wsb, s2 = synthetic.w4a16_gemm()
+    WA, WB, WSB = up16(wa), u8(wb), u8(wsb)
+    calls.append(("w4a16", lambda: bg.gemm_w4a16(WA, WB, WSB, s2)))
+    for name, fn in calls:
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        log(f"profiled row {name}")
 
 
 def oracle_timing(fn_rows, total_rows, block, seconds):
