@@ -92,7 +92,12 @@ gemm_ordered_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__
 
     const int tid = threadIdx.x;
     const int tx = tid & 15, ty = tid >> 4;
-    const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+    // Dispatch places workgroup b on XCD b % 8; renumbered so each XCD holds
+    // one contiguous range of tiles, the column tiles of a row block (which
+    // share its A rows) run on the same XCD and hit in its L2.
+    const int nb = gridDim.x, per = nb >> 3, rem = nb & 7, x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int logical = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + j;
+    const int tm = logical / tiles_n, tn = logical % tiles_n;
     const int m0 = tm * TM, n0 = tn * TN;
     const bool vec = (K & 7) == 0;
 
