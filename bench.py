@@ -535,30 +535,52 @@ def measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream, oracle_seconds
 
 
 def cpu_baseline(gemms, seconds):
-    """The oracle's FP64 GEMM (decode + numpy matmul) on the host, over row
-    blocks of the step's three GEMMs in turn, until `seconds` of wall time."""
+    """The plain C++ oracle's FP64 GEMM (oracle/cpu_oracle.cpp: decode, then
+    one ascending-k FP64 dot product per output, rows split over host
+    threads) on a bounded sample: for each of the step's three GEMMs, a run of
+    consecutive output rows sized to take about seconds/3 of wall time. The
+    numpy oracle (decode + BLAS FP64 matmul) is timed the same way for context."""
+    import numpy as np
     from threadpoolctl import threadpool_info
 
     import oracle
+    from oracle import cpp
 
-    t0 = time.time()
-    blk = 128
-    flops = 0.0
-    done = {name: 0 for name, _, _ in gemms}
-    i = 0
-    while time.time() - t0 < seconds:
-        name, a, w = gemms[i % len(gemms)]
-        r0 = (done[name] // blk * blk) % a.shape[0]
-        oracle.gemm_bf16_ref(a[r0:r0 + blk], w)
-        flops += 2.0 * min(blk, a.shape[0] - r0) * w.shape[0] * a.shape[1]
-        done[name] += blk
-        i += 1
-    dt = time.time() - t0
-    threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
-    parts = ", ".join(f"{n}: {done[n]} rows" for n, _, _ in gemms)
-    return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"gemm_bf16_ref (FP64 numpy) over 128-row blocks of the MLP step's GEMMs ({parts}; "
-                      f"{flops / 1e9:.0f} GFLOP in {dt:.1f} s wall)"}
+    threads = min(16, cpp.hardware_threads())   # the host share of one GPU
+
+    def rate(fn, a, w, budget):
+        rows, t, flops, done = 8, 0.0, 0.0, 0
+        while t < budget:
+            r = min(rows, a.shape[0])
+            t0 = time.time()
+            fn(a, w, r)
+            dt = time.time() - t0
+            t += dt
+            flops += 2.0 * r * w.shape[0] * a.shape[1]
+            done += r
+            rows = max(8, int(r * max(1.0, (budget - t) / max(dt, 1e-3)) * 0.9))
+        return flops, t, done
+
+    per = seconds / len(gemms)
+    tot_f, tot_t, parts = 0.0, 0.0, []
+    for name, a, w in gemms:
+        f, t, n = rate(lambda a_, w_, r: cpp.gemm_bf16_ref_rows(a_, w_, np.arange(r), threads), a, w, per)
+        tot_f, tot_t = tot_f + f, tot_t + t
+        parts.append(f"{name}: {n} rows")
+    res = {"value": round(tot_f / tot_t / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"C++ oracle orc_gemm_bf16_f64_rows (FP64, ascending k, {threads} threads) on leading rows "
+                     f"of the MLP step's GEMMs ({', '.join(parts)}; {tot_f / 1e9:.1f} GFLOP in {tot_t:.1f} s wall)"}
+
+    blas = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    nf, nt, nparts = 0.0, 0.0, []
+    for name, a, w in gemms:
+        f, t, n = rate(lambda a_, w_, r: oracle.gemm_bf16_ref(a_[:r], w_), a, w, min(per, 3.0))
+        nf, nt = nf + f, nt + t
+        nparts.append(f"{name}: {n} rows")
+    res["numpy_oracle"] = {"value": round(nf / nt / 1e12, 4), "unit": "TFLOP/s", "cores": int(blas),
+                           "sample": f"gemm_bf16_ref (decode + FP64 BLAS matmul) ({', '.join(nparts)}; "
+                                     f"{nf / 1e9:.0f} GFLOP in {nt:.1f} s wall)"}
+    return res
 
 
 if __name__ == "__main__":

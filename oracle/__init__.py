@@ -6,6 +6,11 @@ package. It shares no code, tables, constants or helpers with the HIP library
 (block_scaled_fp4_gemm_amd), and neither imports the other; both consume the
 same seeded bytes from the standalone `synthetic` module.
 
+Two independent implementations of the same definitions live here: the numpy
+modules (codecs, gemm) and a plain C++17 one (cpu_oracle.cpp, built with
+-O2 -ffp-contract=off and loaded through oracle.cpp). Each is pinned on its
+own, and the two are compared with each other.
+
 Every function is pinned by CPU tests against something other than itself
 (textbook format tables, library dtype conversions, exact rational brute
 force, closed-form identities and hand-worked rounding cases).

@@ -5,6 +5,7 @@ import torch
 
 import block_scaled_fp4_gemm_amd as bg
 import oracle
+from oracle import cpp
 import synthetic
 from gpu_util import assert_bits_equal, bits_of, check_close, empty_bf16, to_dev_bf16
 
@@ -167,6 +168,9 @@ def test_router_bit_exact(m):
     got32 = c32.cpu().numpy()
     assert_bits_equal(got32.view(np.uint32), want32.view(np.uint32), "fp32 sums")
     assert_bits_equal(bits_of(c), oracle.f32_to_bf16(want32), "bf16 out")
+    # the plain C++ oracle's strict FP32 recurrence gives the same bits
+    want16 = cpp.gemm_ordered(x, w, threads=16)
+    assert_bits_equal(bits_of(c), want16, "bf16 out vs C++ oracle")
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 1, 1), (65, 129, 33), (17, 7, 300), (130, 257, 64), (3, 70, 2049)])
