@@ -19,6 +19,7 @@ Output: one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -46,8 +47,8 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--splitk", default="auto", help="auto or a fixed k_splits for the down projection")
     p.add_argument("--no-rows", action="store_true", help="skip the per-row table")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -130,6 +131,13 @@ def main():
         bg.gemm_bf16(X, Wu, out=U)
         down(ks)
 
+    # The timed regions run with Python's cyclic garbage collector off (as
+    # timeit does): a collection during a long unsynchronised launch sequence
+    # was seen to block the host for tens of milliseconds while the queue
+    # drained, leaving the GPU idle inside the timed region.
+    gc.collect()
+    gc.disable()
+
     if args.splitk == "auto":
         cands = (1, 2, 4, 8)
         times = {ks: [] for ks in cands}
@@ -168,6 +176,7 @@ def main():
         step(rec)
     end = ev()
     torch.cuda.synchronize()
+    gc.enable()
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / args.steps
     flops_gemm = 2.0 * M * INTER * HID
@@ -381,6 +390,8 @@ def measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream, oracle_seconds
             fn()
         torch.cuda.synchronize()
         res = {}
+        gc.collect()
+        gc.disable()
         for mode in ("warm", "cold"):
             pairs = []
             for _ in range(reps):
@@ -396,6 +407,7 @@ def measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream, oracle_seconds
             us = [a.elapsed_time(b) * 1e3 for a, b in pairs]
             res[mode] = float(np.median(us))
             spread[mode] = [round(float(np.percentile(us, 20)), 2), round(float(np.percentile(us, 80)), 2)]
+        gc.enable()
         return res["warm"], res["cold"]
 
     def with_spread(d):

@@ -1121,7 +1121,9 @@ struct TileChoice {
 };
 constexpr TileChoice kTileChoices[] = {
     {2, 256, 256, 1, 1096.0, 1096.0},
-    {8, 160, 256, 1, 972.0, 972.0},
+    // three stages (159744 bytes of LDS): 6-8% ahead of two stages on the
+    // 5120x2048 outputs (down, Q/O) in interleaved same-GPU runs
+    {3, 160, 256, 1, 1050.0, 1050.0},
     {10, 256, 128, 1, 900.0, 900.0},
     {9, 160, 128, 2, 884.0, 819.0},
     {6, 128, 128, 2, 808.0, 671.0},
