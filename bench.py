@@ -2,7 +2,8 @@
 
 A step is the MLP block of a 2B-class decoder at one packed LoRA step (the
 sm121a_matmul.py page's shape list): gate and up projections
-A[5120,2048] x W[11008,2048]^T, then the down projection
+A[5120,2048] x W[11008,2048]^T (two separate products with their own weights
+and outputs, computed in one launch by gemm_bf16_dual), then the down projection
 H[5120,11008] x W[2048,11008]^T through split-K (best k_splits of 1/2/4/8,
 chosen during warm-up). Inputs are seeded synthetic BF16 tensors resident in
 HBM before timing starts. `value` = 3 * 2*M*N*K flops per step / step time.
@@ -126,9 +127,13 @@ def main():
     # Choose the down-projection split during warm-up, in context: whole
     # steps (gate, up, down) with each candidate, in interleaved rounds, so
     # the clock state the down GEMM sees is the one of the timed loop.
+    # gate and up: two products of X in one launch (gemm_bf16_dual), so their
+    # tiles share the rounds of one grid
+    def gate_up():
+        bg.gemm_bf16_dual(X, Wg, Wu, out0=G, out1=U)
+
     def step_with(ks):
-        bg.gemm_bf16(X, Wg, out=G)
-        bg.gemm_bf16(X, Wu, out=U)
+        gate_up()
         down(ks)
 
     # The timed regions run with Python's cyclic garbage collector off (as
@@ -158,13 +163,11 @@ def main():
 
     def step(rec=None):
         e0 = ev() if rec is not None else None
-        bg.gemm_bf16(X, Wg, out=G)
+        gate_up()
         e1 = ev() if rec is not None else None
-        bg.gemm_bf16(X, Wu, out=U)
-        e2 = ev() if rec is not None else None
         down(ks_down)
         if rec is not None:
-            rec.append((e0, e1, e2, ev()))
+            rec.append((e0, e1, ev()))
 
     for _ in range(args.warmup):
         step()
@@ -183,11 +186,12 @@ def main():
     flops_step = 3 * flops_gemm
     value = flops_step / (ms_step * 1e-3) / 1e12
 
-    gate_up_ms = [r[0].elapsed_time(r[1]) for r in rec] + [r[1].elapsed_time(r[2]) for r in rec]
-    down_ms = [r[2].elapsed_time(r[3]) for r in rec]
+    gate_up_ms = [r[0].elapsed_time(r[1]) for r in rec]
+    down_ms = [r[1].elapsed_time(r[2]) for r in rec]
     gu_avg = float(np.mean(gate_up_ms))
-    achieved = flops_gemm / (gu_avg * 1e-3) / 1e12
-    log(f"step {ms_step * 1e3:.1f} us: gate/up {gu_avg * 1e3:.1f} us avg, down {np.mean(down_ms) * 1e3:.1f} us avg")
+    achieved = 2 * flops_gemm / (gu_avg * 1e-3) / 1e12
+    log(f"step {ms_step * 1e3:.1f} us: gate+up (dual) {gu_avg * 1e3:.1f} us avg, "
+        f"down {np.mean(down_ms) * 1e3:.1f} us avg")
 
     # GPU engine clock while the same step runs on (outside the timed region):
     # the BF16 peak at the measured clock puts the achieved rate in context.
@@ -203,8 +207,8 @@ def main():
 
     roofline = {
         "bound": "mfma",
-        "kernel": ("gemm_bf16 MLP gate/up call 5120x11008x2048 (per call): gemm_mfma_direct_kernel 256x256 "
-                   "tiles over columns 0-9471, then 256x128 tiles over 9472-11007"),
+        "kernel": ("gemm_bf16_dual MLP gate+up call (two 5120x11008x2048 products of one X, per call): one "
+                   "dispatch of gemm_mfma_direct_kernel 256x256 tiles, 1720 tiles"),
         "achieved": round(achieved, 1),
         "peak": BF16_PEAK_TFLOPS,
         "unit": "TFLOP/s",
@@ -231,7 +235,7 @@ def main():
             "parallelism": "none (1 GPU)",
         },
         "pct_of_bf16_peak": round(100.0 * value / BF16_PEAK_TFLOPS, 2),
-        "gate_up_us": round(gu_avg * 1e3, 2),
+        "gate_up_dual_us": round(gu_avg * 1e3, 2),
         "down_us": round(float(np.mean(down_ms)) * 1e3, 2),
         "roofline": roofline,
         "clocks": clocks,
@@ -302,7 +306,7 @@ def sample_sclk(run_once, seconds, sync):
 
 
 def traffic_for_current_kernel():
-    """HBM bytes per gate/up call (both dispatches) from the committed counter
+    """HBM bytes per gate+up dual call from the committed counter
     summary, or None if the GEMM kernel source changed since the counters
     were taken."""
     path = os.path.join(ROOT, "profiles", "traffic_gate_up.json")
@@ -331,6 +335,8 @@ def profile_rows(bg, synthetic, torch, up16, u8, dev):
     x, w = synthetic.mlp_gate_up()
     X, W = up16(x), up16(w)
     calls.append(("mlp_gate_up", lambda: bg.gemm_bf16(X, W)))
+    W2 = up16(synthetic.normal_bf16((INTER, HID), 0.02, 2, synthetic.TID_B2 + 10))
+    calls.append(("mlp_gate_up_dual", lambda: bg.gemm_bf16_dual(X, W, W2)))
     h, wd = synthetic.mlp_down()
     H, WD = up16(h), up16(wd)
     calls.append(("mlp_down_k1", lambda: bg.gemm_bf16(H, WD)))
@@ -436,6 +442,19 @@ def measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream, oracle_seconds
     dense_row("attn_kv_5120x512x2048", 5120, 512, 2048, a, b)
     a, b = synthetic.mlp_gate_up()
     dense_row("mlp_gate_up_5120x11008x2048", 5120, 11008, 2048, a, b)
+    # both projections in one launch (the step's form)
+    A, B = up16(a), up16(b)
+    B2 = up16(synthetic.normal_bf16((INTER, HID), 0.02, 2, synthetic.TID_B2 + 10))
+    C1 = torch.empty((5120, 11008), dtype=torch.bfloat16, device=dev)
+    C2 = torch.empty((5120, 11008), dtype=torch.bfloat16, device=dev)
+    w, c = timed(lambda: bg.gemm_bf16_dual(A, B, B2, out0=C1, out1=C2))
+    fl = 2 * 2.0 * 5120 * 11008 * 2048
+    rows["mlp_gate_up_dual_2x5120x11008x2048"] = with_spread({
+        "shape": [5120, 11008, 2048], "products": 2, "us_warm": round(w, 2), "us_cold": round(c, 2),
+        "tflops_warm": round(fl / w / 1e6, 1), "tflops_cold": round(fl / c / 1e6, 1),
+        "frac_bf16_peak_warm": round(fl / w / 1e6 / BF16_PEAK_TFLOPS, 4)})
+    log("mlp_gate_up_dual", rows["mlp_gate_up_dual_2x5120x11008x2048"])
+    del A, B, B2, C1, C2
 
     h, wd = synthetic.mlp_down()
     H, WD = up16(h), up16(wd)

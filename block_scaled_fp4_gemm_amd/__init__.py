@@ -30,6 +30,7 @@ _p, _u32, _f32, _sz = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_float, ctypes.c
 _SIGS = {
     "gemm_bf16": [_p, _p, _p, _u32, _u32, _u32, _p],
     "gemm_bf16_strided": [_p, _u32, _p, _u32, _p, _u32, _u32, _u32, _u32, _p],
+    "gemm_bf16_dual": [_p, _p, _p, _p, _p, _u32, _u32, _u32, _p],
     "gemm_bf16_scaled_acc": [_p, _p, _p, _u32, _u32, _u32, _f32, _p],
     "gemm_bf16_splitk": [_p, _p, _p, _p, _sz, _u32, _u32, _u32, _u32, _p],
     "gemm_bf16_ordered": [_p, _p, _p, _u32, _u32, _u32, _p],
@@ -107,6 +108,22 @@ def gemm_bf16(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None,
         out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
     _check(lib.gemm_bf16(_ptr(a), _ptr(b), _ptr(out), m, n, k, _stream(stream)), "gemm_bf16")
     return out
+
+
+def gemm_bf16_dual(a: torch.Tensor, b0: torch.Tensor, b1: torch.Tensor, out0: torch.Tensor | None = None,
+                   out1: torch.Tensor | None = None, stream=None):
+    """C0 = bf16(A @ B0^T) and C1 = bf16(A @ B1^T) (same shapes) in one launch."""
+    m, k = _bits16(a).shape
+    n = _bits16(b0).shape[0]
+    if tuple(_bits16(b1).shape) != tuple(b0.shape):
+        raise ValueError("B0 and B1 must have the same shape")
+    if out0 is None:
+        out0 = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    if out1 is None:
+        out1 = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    _check(lib.gemm_bf16_dual(_ptr(a), _ptr(b0), _ptr(b1), _ptr(out0), _ptr(out1), m, n, k, _stream(stream)),
+           "gemm_bf16_dual")
+    return out0, out1
 
 
 def _rows(t: torch.Tensor, what: str):

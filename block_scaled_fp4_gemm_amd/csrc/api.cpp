@@ -134,6 +134,22 @@ bg_status gemm_bf16(const uint16_t* A, const uint16_t* B, uint16_t* C, uint32_t 
     return launched(bg::launch_dense(p, bg::EPI_STORE_BF16, (hipStream_t)stream));
 }
 
+bg_status gemm_bf16_dual(const uint16_t* A, const uint16_t* B0, const uint16_t* B1, uint16_t* C0,
+                         uint16_t* C1, uint32_t M, uint32_t N, uint32_t K, void* stream) {
+    bg_status s = check_dense(A, B0, C0, M, N, K, 2);
+    if (s != BG_OK) return s;
+    if ((s = check_dense(A, B1, C1, M, N, K, 2)) != BG_OK) return s;
+    if (M == 0 || N == 0) return BG_OK;
+    const uint64_t b_bytes = (uint64_t)N * K * 2, c_bytes = (uint64_t)M * N * 2;
+    const Range r0 = range_of(C0, c_bytes), r1 = range_of(C1, c_bytes);
+    if (overlap(r0, r1) || overlap(r0, range_of(B1, b_bytes)) || overlap(r1, range_of(B0, b_bytes)))
+        return BG_ERR_ALIAS;
+    uint32_t cus = 0;
+    if ((s = check_device(&cus)) != BG_OK) return s;
+    bg::DenseProblem p{A, B0, C0, M, N, K, K, K, N, K, 1, 0.0f, cus};
+    return launched(bg::launch_dense_dual(p, B1, C1, (hipStream_t)stream));
+}
+
 bg_status gemm_bf16_strided(const uint16_t* A, uint32_t lda, const uint16_t* B, uint32_t ldb,
                             uint16_t* C, uint32_t ldc, uint32_t M, uint32_t N, uint32_t K,
                             void* stream) {

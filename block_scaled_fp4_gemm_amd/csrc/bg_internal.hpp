@@ -57,6 +57,9 @@ struct W4a16Problem {
 // return hipGetLastError() of the launch. Shapes are already validated and
 // non-empty (M > 0, N > 0).
 hipError_t launch_dense(const DenseProblem& p, Epilogue epi, hipStream_t stream);
+// C0 = bf16(A * B^T) (the problem p, BF16 store) and C1 = bf16(A * B1^T) of the
+// same shape, in one launch when the direct kernels apply.
+hipError_t launch_dense_dual(const DenseProblem& p, const uint16_t* B1, uint16_t* C1, hipStream_t stream);
 hipError_t launch_fp4(const Fp4Problem& p, hipStream_t stream);
 hipError_t launch_scales_from_blocked(const uint8_t* src, uint8_t* dst, uint32_t rows, uint32_t k_groups,
                                       uint32_t batch, hipStream_t stream);

@@ -77,6 +77,12 @@ struct KParams {
     // batched FP4 (blockIdx.z = batch index): per-batch strides of Aq, SFA,
     // Bq, SFB (bytes) and C (elements); zero for one problem
     int64_t bs_a, bs_sa, bs_b, bs_sb, bs_c;
+    // two products of the same A in one launch (direct kernels, BF16 store):
+    // column tiles [dual_tiles_n, 2*dual_tiles_n) of the grid compute
+    // C1 = A * B1^T; 0 for a single problem
+    const uint16_t* B1;
+    void* C1;
+    int dual_tiles_n;
 };
 
 // Swizzled 16-byte chunk slot of logical chunk c in a tile row of CPR chunks
@@ -967,11 +973,19 @@ gemm_mfma_direct_kernel(KParams p) {
 
     int tm, tn;
     tile_of_block(p.tiles_m, p.tiles_n, tm, tn);
+    // the second problem of a dual launch: same A and shape, its own B and C
+    // (uniform per workgroup)
+    KParams q = p;
+    if (p.dual_tiles_n > 0 && tn >= p.dual_tiles_n) {
+        tn -= p.dual_tiles_n;
+        q.B = p.B1;
+        q.C = p.C1;
+    }
     const int m0 = tm * BM, n0 = tn * BN;
 
     const int split = blockIdx.y;
-    const int kb = (int)min((int64_t)p.K, (int64_t)split * p.k_chunk);
-    const int ke = (int)min((int64_t)p.K, (int64_t)kb + p.k_chunk);
+    const int kb = (int)min((int64_t)q.K, (int64_t)split * q.k_chunk);
+    const int ke = (int)min((int64_t)q.K, (int64_t)kb + q.k_chunk);
 
     f32x16 acc[FM][FN];
     zero_acc(acc);
@@ -988,26 +1002,26 @@ gemm_mfma_direct_kernel(KParams p) {
     static_assert(!PREF || NPRE * NT == BM * PCPR, "prefetch rounds cover the tile exactly");
     u32x4 pre[NPRE > 0 ? NPRE : 1];
     direct_mainloop<BM, BN, BKS, WM, WN, STAGES, NPRE>(
-        p, smem, m0, n0, kb, ke, wave, lane, tid, acc, [&]() {
+        q, smem, m0, n0, kb, ke, wave, lane, tid, acc, [&]() {
             if constexpr (PREF) {
-                const uint16_t* O = reinterpret_cast<const uint16_t*>(p.C);
-                const bool vec_ok = (p.N & 7) == 0 && (p.ldc & 7) == 0;
+                const uint16_t* O = reinterpret_cast<const uint16_t*>(q.C);
+                const bool vec_ok = (q.N & 7) == 0 && (q.ldc & 7) == 0;
 #pragma unroll
                 for (int it = 0; it < NPRE; ++it) {
-                    const int q = tid + it * NT;
-                    const int row = q / PCPR, chunk = q % PCPR;
+                    const int piece = tid + it * NT;
+                    const int row = piece / PCPR, chunk = piece % PCPR;
                     const int m = m0 + row, n = n0 + chunk * 8;
-                    if (m < p.M && vec_ok && n + 8 <= p.N)
-                        pre[it] = *reinterpret_cast<const u32x4*>(O + (int64_t)m * p.ldc + n);
+                    if (m < q.M && vec_ok && n + 8 <= q.N)
+                        pre[it] = *reinterpret_cast<const u32x4*>(O + (int64_t)m * q.ldc + n);
                 }
                 // edge tiles skip some prefetch loads: uniform per workgroup
-                return vec_ok && m0 + BM <= p.M && n0 + BN <= p.N;
+                return vec_ok && m0 + BM <= q.M && n0 + BN <= q.N;
             }
             return true;
         });
 
     staged_epilogue<EPI, BM, BN, WM, WN, FM, FN, NT, SMEM_ELEMS * 2, NPRE>(
-        p, acc, reinterpret_cast<uint8_t*>(smem), m0, n0, wm, wn, lane, tid, split, pre);
+        q, acc, reinterpret_cast<uint8_t*>(smem), m0, n0, wm, wn, lane, tid, split, pre);
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, int SRC, int RSETS = 2>
@@ -1030,6 +1044,11 @@ hipError_t launch_direct(const KParams& kp, int splits, hipStream_t stream) {
     KParams q = kp;
     q.tiles_m = (kp.M + BM - 1) / BM;
     q.tiles_n = (kp.N + BN - 1) / BN;
+    q.dual_tiles_n = 0;
+    if (kp.B1 != nullptr) {   // dual launch: the second product's tiles follow the first's
+        q.dual_tiles_n = q.tiles_n;
+        q.tiles_n *= 2;
+    }
     dim3 grid((unsigned)(q.tiles_m * q.tiles_n), (unsigned)splits, 1);
     hipLaunchKernelGGL((gemm_mfma_direct_kernel<BM, BN, BKS, WM, WN, STAGES, EPI, PREF>), grid,
                        dim3(WM * WN * 64), 0, stream, q);
@@ -1250,6 +1269,49 @@ hipError_t launch_dense(const DenseProblem& p, Epilogue epi, hipStream_t stream)
             break;
     }
     return hipErrorInvalidValue;
+}
+
+// Two products of one A: the second problem's column tiles follow the first's
+// in one grid, so the two share the rounds of one launch instead of each
+// leaving its own last round partly empty (5120 x 11008 x 2048 twice: 1720
+// tiles of 256 x 256, 6.7 rounds, against 2 x 3.4). The tile is the one the
+// cost model picks for the combined problem (M, 2N, K); no column split.
+// Operands outside the direct kernels' reach (K % 8 != 0, or a forced
+// register-staged tile) run as two ordinary launches.
+hipError_t launch_dense_dual(const DenseProblem& p, const uint16_t* B1, uint16_t* C1, hipStream_t stream) {
+    const bool vec = (p.K % 8) == 0 && (int64_t)p.K * 640 < (int64_t(1) << 31);
+    const int forced = env_int("BLOCKGEMM_TILE");
+    if (!vec || forced == 0) {
+        hipError_t e = launch_dense(p, EPI_STORE_BF16, stream);
+        if (e != hipSuccess) return e;
+        DenseProblem p1 = p;
+        p1.B = B1;
+        p1.C = C1;
+        return launch_dense(p1, EPI_STORE_BF16, stream);
+    }
+    KParams kp{};
+    kp.A = p.A;
+    kp.B = p.B;
+    kp.C = p.C;
+    kp.B1 = B1;
+    kp.C1 = C1;
+    kp.M = (int)p.M;
+    kp.N = (int)p.N;
+    kp.K = (int)p.K;
+    kp.lda = kp.ldb = (int)p.K;
+    kp.ldc = (int)p.N;
+    kp.k_chunk = (int)p.K;
+    kp.cus = p.cus > 0 ? (int)p.cus : 256;
+    int cfg = forced;
+    if (cfg < 0) {
+        if (p.K <= 128) {
+            cfg = 9;
+        } else {
+            double t;
+            cfg = best_single(kp.M, 2 * kp.N, kp.K, 1, kp.cus, &t)->cfg;
+        }
+    }
+    return launch_tile_cfg<EPI_STORE_BF16>(kp, 1, cfg, stream);
 }
 
 // W4A16 tile choices (register-staged kernel; BLOCKGEMM_W4A16_TILE, a tuning

@@ -68,6 +68,25 @@ bg_status gemm_bf16(const uint16_t* A, const uint16_t* B, uint16_t* C,
                     uint32_t M, uint32_t N, uint32_t K, void* stream);
 
 /*
+ * gemm_bf16_dual: two products of the same activations in one launch,
+ *   C0 = bf16(A * B0^T) and C1 = bf16(A * B1^T),
+ * each exactly what gemm_bf16 returns for it (bit-identical: every output is
+ * one tile's FP32 sum over K in the same order).
+ *
+ * sm121a_matmul.py page, module docstring: the MLP gate and up projections
+ * are two GEMMs of one activation matrix with N = 11008 weights each (M =
+ * 5120, K = 2048). Launched separately, each pays its own partly filled
+ * last round of tiles on the 256 compute units; scheduled together their
+ * tiles fill the rounds of one launch.
+ *
+ *  A: [M, K] BF16.  B0, B1: [N, K] BF16.  C0, C1: [M, N] BF16, written.
+ *  Same shape rules, alignment and errors as gemm_bf16 for each pair; C0 and
+ *  C1 must not overlap each other, A, B0 or B1 (BG_ERR_ALIAS).
+ */
+bg_status gemm_bf16_dual(const uint16_t* A, const uint16_t* B0, const uint16_t* B1, uint16_t* C0,
+                         uint16_t* C1, uint32_t M, uint32_t N, uint32_t K, void* stream);
+
+/*
  * gemm_bf16_strided: gemm_bf16 on operands and an output that are row ranges
  * of larger row-major buffers. Row i of A starts lda elements after row i-1,
  * row j of B ldb elements after row j-1, row i of C ldc elements after row

@@ -64,6 +64,7 @@ def test_empty_problems_are_ok_without_pointers():
     assert L.fp4_scales_from_blocked(None, None, 128, 4, 0, None) == bg.BG_OK
     assert L.bf16_scaled_add(None, None, 0, 1.0, None) == bg.BG_OK
     assert L.gemm_bf16_splitk(None, None, None, None, 0, 0, 4, 64, 4, None) == bg.BG_OK
+    assert L.gemm_bf16_dual(None, None, None, None, None, 0, 4, 64, None) == bg.BG_OK
 
 
 def test_null_pointers():
@@ -79,6 +80,8 @@ def test_null_pointers():
     assert L.gemm_fp4_blockscaled_batched(A, S1, B, None, C, 4, 4, 32, 2, None) == bg.BG_ERR_NULL
     assert L.fp4_scales_from_blocked(S1, None, 128, 4, 1, None) == bg.BG_ERR_NULL
     assert L.bf16_scaled_add(None, B, 8, 1.0, None) == bg.BG_ERR_NULL
+    assert L.gemm_bf16_dual(A, B, None, C, W, 4, 4, 8, None) == bg.BG_ERR_NULL
+    assert L.gemm_bf16_dual(A, B, S1, C, None, 4, 4, 8, None) == bg.BG_ERR_NULL
 
 
 def test_misaligned_pointers():
@@ -93,6 +96,8 @@ def test_misaligned_pointers():
     assert L.fp4_scales_from_blocked(S1 + 4, S2, 128, 4, 1, None) == bg.BG_ERR_ALIGN
     assert L.gemm_fp4_blockscaled_splitk(A, S1, B, S2, C, W + 4, 1 << 20, 4, 4, 128, 2, None) == bg.BG_ERR_ALIGN
     assert L.gemm_bf16_splitk(A, B, C, W + 4, 1 << 20, 4, 4, 128, 2, None) == bg.BG_ERR_ALIGN
+    assert L.gemm_bf16_dual(A, B, S1 + 2, C, W, 4, 4, 8, None) == bg.BG_ERR_ALIGN
+    assert L.gemm_bf16_dual(A, B, S1, C, W + 8, 4, 4, 8, None) == bg.BG_ERR_ALIGN
 
 
 def test_aliasing_outputs():
@@ -115,6 +120,10 @@ def test_aliasing_outputs():
     assert L.gemm_fp4_blockscaled_splitk(A, S1, B, S2, C, C, 1 << 20, 4, 4, 128, 2, None) == bg.BG_ERR_ALIAS
     assert L.fp4_scales_from_blocked(S1, S1 + 256, 128, 4, 1, None) == bg.BG_ERR_ALIAS
     assert L.bf16_scaled_add(A, A + 16, 64, 1.0, None) == bg.BG_ERR_ALIAS
+    # dual: the two outputs overlap each other, or one output overlaps the other product's weights
+    assert L.gemm_bf16_dual(A, B, S1, C, C + 16, 4, 4, 64, None) == bg.BG_ERR_ALIAS
+    assert L.gemm_bf16_dual(A, B, S1, S1 + 16, W, 4, 4, 64, None) == bg.BG_ERR_ALIAS
+    assert L.gemm_bf16_dual(A, B, S1, C, B, 4, 4, 64, None) == bg.BG_ERR_ALIAS
     # adjacent but disjoint ranges are fine up to the device check
     if torch.cuda.device_count() == 0:
         assert L.gemm_bf16(A, A + 4 * 64 * 2, A + 2 * 4 * 64 * 2, 4, 4, 64, None) == bg.BG_ERR_DEVICE
@@ -134,6 +143,7 @@ def test_shape_rules():
     assert L.gemm_bf16_splitk(A, B, C, W, 1 << 30, 4, 4, 128, 0, None) == bg.BG_ERR_SHAPE
     assert L.gemm_bf16_splitk(A, B, C, W, 1 << 30, 4, 4, 128, 65, None) == bg.BG_ERR_SHAPE
     assert L.gemm_bf16(A, B, C, 1 << 31, 4, 4, None) == bg.BG_ERR_SHAPE
+    assert L.gemm_bf16_dual(A, B, S1, C, W, 4, 1 << 31, 4, None) == bg.BG_ERR_SHAPE
     assert L.gemm_bf16_strided(A, 7, B, 8, C, 4, 4, 4, 8, None) == bg.BG_ERR_SHAPE    # lda < K
     assert L.gemm_bf16_strided(A, 8, B, 7, C, 4, 4, 4, 8, None) == bg.BG_ERR_SHAPE    # ldb < K
     assert L.gemm_bf16_strided(A, 8, B, 8, C, 3, 4, 4, 8, None) == bg.BG_ERR_SHAPE    # ldc < N
@@ -156,6 +166,7 @@ def test_valid_arguments_reach_the_device_check():
     assert L.gemm_bf16_splitk(A, B, C, None, 0, 4, 4, 8, 1, None) == bg.BG_ERR_DEVICE
     assert L.gemm_w4a16(A, B, S2, 0.5, C, 4, 4, 32, None) == bg.BG_ERR_DEVICE
     assert L.gemm_bf16_strided(A, 13, B, 8, C, 5, 4, 4, 8, None) == bg.BG_ERR_DEVICE
+    assert L.gemm_bf16_dual(A, B, S1, C, W, 4, 4, 8, None) == bg.BG_ERR_DEVICE
 
 
 def test_python_binding_raises_on_status():
