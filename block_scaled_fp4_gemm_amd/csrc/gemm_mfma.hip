@@ -345,6 +345,16 @@ struct Stager<ROWS, NT, SRC_FP4_BF16, BK> : Fp4Stager<ROWS, NT, false> {};
 // row's whole 2*BKS-byte segment. Only whole BKS steps use this path; rows
 // beyond the matrix are clamped to its last row.
 // ---------------------------------------------------------------------------
+// A pointer every lane holds the same value of, stated as such so that a
+// buffer resource built from it stays in scalar registers (the inline-asm
+// loads need it there) whatever the compiler's divergence analysis concludes.
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+}
+
 template <int ROWS, int NT, int BKS>
 struct DirectStager {
     static constexpr int CPR = BKS / 8;          // 16-byte chunks per row
@@ -366,8 +376,8 @@ struct DirectStager {
     __amdgpu_buffer_rsrc_t rsrc;
 
     __device__ __forceinline__ void init(const uint16_t* base, int row0, int nrows, int ld, int wave, int lane) {
-        rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + (int64_t)row0 * ld), (short)0,
-                                                 0x7FFFFFFF, 0x00020000);
+        rsrc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(base + (int64_t)row0 * ld), (short)0, 0x7FFFFFFF,
+                                                 0x00020000);
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             const int seg = min(wave + j * NW, SEGS - 1);
@@ -509,7 +519,7 @@ template <int EPI, int BM, int BN, int WM, int WN, int FM, int FN, int NT, int C
 __device__ __forceinline__ void staged_epilogue(const KParams& p, const f32x16 (&acc)[FM][FN],
                                                 uint8_t* lds, int m0, int n0, int wm, int wn,
                                                 int lane, int tid, int split,
-                                                const u32x4* pre = nullptr) {
+                                                const u32x4* pre = nullptr, void* c_base = nullptr) {
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int ELEM = (EPI == EPI_STORE_F32) ? 4 : 2;
     constexpr int ROWB = BN * ELEM;            // bytes per staged row
@@ -520,6 +530,7 @@ __device__ __forceinline__ void staged_epilogue(const KParams& p, const f32x16 (
     constexpr int NPASS = (BM + RP - 1) / RP;
     constexpr int EPC = 16 / ELEM;             // elements per chunk
     const int M = p.M, N = p.N, ldc = p.ldc;
+    void* const Cb = c_base != nullptr ? c_base : p.C;   // the output (a dual launch's second one)
     const bool vec_ok = (N % EPC) == 0 && (ldc % EPC) == 0;
 
     // chunks rotate by the row index, so the 32 rows one store instruction
@@ -569,7 +580,7 @@ __device__ __forceinline__ void staged_epilogue(const KParams& p, const f32x16 (
             const int64_t off = (int64_t)m * ldc + n;
             const bool full = vec_ok && n + EPC <= N;
             if constexpr (EPI == EPI_STORE_F32) {
-                float* plane = reinterpret_cast<float*>(p.C) + (int64_t)split * M * ldc;
+                float* plane = reinterpret_cast<float*>(Cb) + (int64_t)split * M * ldc;
                 if (full) {
                     *reinterpret_cast<u32x4*>(plane + off) = w;
                 } else {
@@ -577,7 +588,7 @@ __device__ __forceinline__ void staged_epilogue(const KParams& p, const f32x16 (
                     for (int e = 0; e < 4 && n + e < N; ++e) plane[off + e] = __builtin_bit_cast(float, e4[e]);
                 }
             } else if constexpr (EPI == EPI_STORE_BF16 || EPI == EPI_SCALE_BF16) {
-                uint16_t* C = reinterpret_cast<uint16_t*>(p.C);
+                uint16_t* C = reinterpret_cast<uint16_t*>(Cb);
                 if (full) {
                     *reinterpret_cast<u32x4*>(C + off) = w;
                 } else {
@@ -585,7 +596,7 @@ __device__ __forceinline__ void staged_epilogue(const KParams& p, const f32x16 (
                     for (int e = 0; e < 8 && n + e < N; ++e) C[off + e] = (uint16_t)(e4[e >> 1] >> ((e & 1) * 16));
                 }
             } else {  // EPI_SCALED_ACC: out = bf16(out + scale * delta), delta already BF16
-                uint16_t* O = reinterpret_cast<uint16_t*>(p.C);
+                uint16_t* O = reinterpret_cast<uint16_t*>(Cb);
                 const float sc = p.scale;
                 const uint32_t d4[4] = {w.x, w.y, w.z, w.w};
                 if (full) {
@@ -828,8 +839,8 @@ gemm_mfma_kernel(KParams p) {
 // first wait leave them in flight. Otherwise the first wait counts none of
 // them and so also waits for whichever were issued.
 template <int BM, int BN, int BKS, int WM, int WN, int STAGES, int NEXTRA, class Extra>
-__device__ __forceinline__ void direct_mainloop(const KParams& p, uint16_t* smem, int m0, int n0, int kb,
-                                                int ke, int wave, int lane, int tid,
+__device__ __forceinline__ void direct_mainloop(const KParams& p, const uint16_t* Bop, uint16_t* smem, int m0,
+                                                int n0, int kb, int ke, int wave, int lane, int tid,
                                                 f32x16 (&acc)[BM / WM / 32][BN / WN / 32], Extra&& extra) {
     constexpr int NT = WM * WN * 64;
     constexpr int TM = BM / WM, TN = BN / WN;
@@ -850,7 +861,7 @@ __device__ __forceinline__ void direct_mainloop(const KParams& p, uint16_t* smem
     DirectStager<BM, NT, BKS> dsa;
     DirectStager<BN, NT, BKS> dsb;
     dsa.init(p.A, m0, p.M, p.lda, wave, lane);
-    dsb.init(p.B, n0, p.N, p.ldb, wave, lane);
+    dsb.init(Bop, n0, p.N, p.ldb, wave, lane);
     auto issue = [&](int k0, uint16_t* buf) {
         dsa.issue_buf(k0, buf, wave);
         dsb.issue_buf(k0, buf + BM * BKS, wave);
@@ -878,7 +889,7 @@ __device__ __forceinline__ void direct_mainloop(const KParams& p, uint16_t* smem
         Stager<BM, NT, SRC_BF16_VEC, BKS> sa;
         Stager<BN, NT, SRC_BF16_VEC, BKS> sb;
         sa.load(p.A, m0, p.M, p.lda, kb, kb + ragged, tid);
-        sb.load(p.B, n0, p.N, p.ldb, kb, kb + ragged, tid);
+        sb.load(Bop, n0, p.N, p.ldb, kb, kb + ragged, tid);
         sa.store(smem, tid);
         sb.store(smem + BM * BKS, tid);
         k_next = kb + ragged;
@@ -975,17 +986,18 @@ gemm_mfma_direct_kernel(KParams p) {
     tile_of_block(p.tiles_m, p.tiles_n, tm, tn);
     // the second problem of a dual launch: same A and shape, its own B and C
     // (uniform per workgroup)
-    KParams q = p;
+    const uint16_t* Bop = p.B;
+    void* Cop = p.C;
     if (p.dual_tiles_n > 0 && tn >= p.dual_tiles_n) {
         tn -= p.dual_tiles_n;
-        q.B = p.B1;
-        q.C = p.C1;
+        Bop = p.B1;
+        Cop = p.C1;
     }
     const int m0 = tm * BM, n0 = tn * BN;
 
     const int split = blockIdx.y;
-    const int kb = (int)min((int64_t)q.K, (int64_t)split * q.k_chunk);
-    const int ke = (int)min((int64_t)q.K, (int64_t)kb + q.k_chunk);
+    const int kb = (int)min((int64_t)p.K, (int64_t)split * p.k_chunk);
+    const int ke = (int)min((int64_t)p.K, (int64_t)kb + p.k_chunk);
 
     f32x16 acc[FM][FN];
     zero_acc(acc);
@@ -1002,26 +1014,26 @@ gemm_mfma_direct_kernel(KParams p) {
     static_assert(!PREF || NPRE * NT == BM * PCPR, "prefetch rounds cover the tile exactly");
     u32x4 pre[NPRE > 0 ? NPRE : 1];
     direct_mainloop<BM, BN, BKS, WM, WN, STAGES, NPRE>(
-        q, smem, m0, n0, kb, ke, wave, lane, tid, acc, [&]() {
+        p, Bop, smem, m0, n0, kb, ke, wave, lane, tid, acc, [&]() {
             if constexpr (PREF) {
-                const uint16_t* O = reinterpret_cast<const uint16_t*>(q.C);
-                const bool vec_ok = (q.N & 7) == 0 && (q.ldc & 7) == 0;
+                const uint16_t* O = reinterpret_cast<const uint16_t*>(Cop);
+                const bool vec_ok = (p.N & 7) == 0 && (p.ldc & 7) == 0;
 #pragma unroll
                 for (int it = 0; it < NPRE; ++it) {
                     const int piece = tid + it * NT;
                     const int row = piece / PCPR, chunk = piece % PCPR;
                     const int m = m0 + row, n = n0 + chunk * 8;
-                    if (m < q.M && vec_ok && n + 8 <= q.N)
-                        pre[it] = *reinterpret_cast<const u32x4*>(O + (int64_t)m * q.ldc + n);
+                    if (m < p.M && vec_ok && n + 8 <= p.N)
+                        pre[it] = *reinterpret_cast<const u32x4*>(O + (int64_t)m * p.ldc + n);
                 }
                 // edge tiles skip some prefetch loads: uniform per workgroup
-                return vec_ok && m0 + BM <= q.M && n0 + BN <= q.N;
+                return vec_ok && m0 + BM <= p.M && n0 + BN <= p.N;
             }
             return true;
         });
 
     staged_epilogue<EPI, BM, BN, WM, WN, FM, FN, NT, SMEM_ELEMS * 2, NPRE>(
-        q, acc, reinterpret_cast<uint8_t*>(smem), m0, n0, wm, wn, lane, tid, split, pre);
+        p, acc, reinterpret_cast<uint8_t*>(smem), m0, n0, wm, wn, lane, tid, split, pre, Cop);
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, int SRC, int RSETS = 2>
