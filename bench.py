@@ -256,12 +256,13 @@ def main():
 
 def sample_sclk(run_once, seconds, sync):
     """Runs run_once() back to back for about `seconds` while a thread reads
-    the active engine-clock level (the line marked '*' in the driver's
-    pp_dpm_sclk file) every 2 ms. Returns the mean MHz and the sample count,
-    or None when no such file is readable."""
+    the active engine-clock and memory-clock levels (the lines marked '*' in
+    the driver's pp_dpm_sclk and pp_dpm_mclk files) every 2 ms. Returns the
+    engine clock's mean, min and max MHz, the memory clock's mean MHz and the
+    sample count, or None when no engine-clock file is readable."""
     import glob
     import threading
-    paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    cards = sorted(glob.glob("/sys/class/drm/card*/device"))
 
     def read(path):
         try:
@@ -273,18 +274,22 @@ def sample_sclk(run_once, seconds, sync):
             return None
         return None
 
-    paths = [p for p in paths if read(p) is not None]
-    if not paths:
+    cards = [c for c in cards if read(c + "/pp_dpm_sclk") is not None]
+    if not cards:
         return None
-    samples = {p: [] for p in paths}
+    samples = {c: [] for c in cards}
+    msamples = {c: [] for c in cards}
     stop = threading.Event()
 
     def poll():
         while not stop.is_set():
-            for p in paths:
-                v = read(p)
+            for c in cards:
+                v = read(c + "/pp_dpm_sclk")
                 if v is not None:
-                    samples[p].append(v)
+                    samples[c].append(v)
+                m = read(c + "/pp_dpm_mclk")
+                if m is not None:
+                    msamples[c].append(m)
             time.sleep(0.002)
 
     th = threading.Thread(target=poll, daemon=True)
@@ -296,13 +301,16 @@ def sample_sclk(run_once, seconds, sync):
         sync()
     stop.set()
     th.join()
-    # the GPU under load is the card whose clock ran highest
-    best = max(paths, key=lambda p: sum(samples[p]) / max(1, len(samples[p])))
-    v = samples[best]
+    # the GPU under load is the card whose engine clock ran highest
+    best = max(cards, key=lambda c: sum(samples[c]) / max(1, len(samples[c])))
+    v, mv = samples[best], msamples[best]
     if not v:
         return None
-    return {"sclk_mhz_mean": round(sum(v) / len(v), 1), "sclk_mhz_min": min(v), "sclk_mhz_max": max(v),
-            "samples": len(v), "source": best}
+    res = {"sclk_mhz_mean": round(sum(v) / len(v), 1), "sclk_mhz_min": min(v), "sclk_mhz_max": max(v),
+           "samples": len(v), "source": best + "/pp_dpm_sclk"}
+    if mv:
+        res["mclk_mhz_mean"] = round(sum(mv) / len(mv), 1)
+    return res
 
 
 def traffic_for_current_kernel():
@@ -598,10 +606,15 @@ def cpu_baseline(gemms, seconds):
         f, t, n = rate(lambda a_, w_, r: cpp.gemm_bf16_ref_rows(a_, w_, np.arange(r), threads), a, w, per)
         tot_f, tot_t = tot_f + f, tot_t + t
         parts.append(f"{name}: {n} rows")
+    # the same definition on one host thread (gate rows only)
+    f1, t1, n1 = rate(lambda a_, w_, r: cpp.gemm_bf16_ref_rows(a_, w_, np.arange(r), 1), gemms[0][1], gemms[0][2],
+                      min(per, 3.0))
     res = {"value": round(tot_f / tot_t / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
            "sample": f"C++ oracle orc_gemm_bf16_f64_rows (FP64, ascending k, {threads} threads) on leading rows "
                      f"of the MLP step's GEMMs ({', '.join(parts)}; {tot_f / 1e9:.1f} GFLOP in {tot_t:.1f} s wall)"}
 
+    res["one_thread"] = {"value": round(f1 / t1 / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+                         "sample": f"{gemms[0][0]}: {n1} rows, {f1 / 1e9:.1f} GFLOP in {t1:.1f} s wall"}
     blas = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
     nf, nt, nparts = 0.0, 0.0, []
     for name, a, w in gemms:
