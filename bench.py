@@ -529,7 +529,7 @@ def measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream, oracle_seconds
     del A4, SA, B4, SB, C
 
     # the kernelbot page's decode shapes (M = 128) through FP4 split-K, best
-    # k_splits of 4/8/16. Bounds: the 16-bit MFMA rate (exact dequantization)
+    # k_splits of 4/8/12/16. Bounds: the 16-bit MFMA rate (exact dequantization)
     # and HBM for the algorithmic bytes (A, B, scales read once, C written once).
     for m, n, k in ((128, 7168, 16384), (128, 4096, 7168)):
         ad, sad, bd, sbd = synthetic.fp4_decode(m=m, n=n, k=k)
@@ -537,7 +537,7 @@ def measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream, oracle_seconds
         C = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         WS = torch.empty((16, m, n), dtype=torch.float32, device=dev)
         best = None
-        for ks in (4, 8, 16):
+        for ks in (4, 8, 12, 16):
             w, c = timed(lambda: bg.gemm_fp4_blockscaled_splitk(AD, SAD, BD, SBD, ks, workspace=WS[:ks], out=C))
             if best is None or w < best[1]:
                 best = (ks, w, c, dict(spread))
