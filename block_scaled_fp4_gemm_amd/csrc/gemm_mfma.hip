@@ -459,6 +459,45 @@ __device__ __forceinline__ void load_frags(const uint16_t* sA, const uint16_t* s
     }
 }
 
+// Fragment addresses for 64-wide K steps, precomputed. With rows of eight
+// 16-byte chunks swizzled by chunk_slot<8>, the chunk a lane reads for
+// fragment i at sub-step kk is (2kk + h) ^ s(row), and since every fragment
+// starts on a 32-row boundary, s(row of fragment i) = s0 ^ 4(i & 1) with s0
+// the swizzle of the lane's row in fragment 0. Hence the byte offset is
+// v[kk ^ 2(i & 1)] + 4096 i with four per-lane values v[j] (one table for the
+// A fragments, one for B): the per-read work is an immediate offset instead
+// of a shift-xor-add chain. (Checked exhaustively against chunk_slot<8> for
+// every lane, fragment, sub-step and 32-row-aligned origin.)
+struct FragAddr64 {
+    uint32_t va[4], vb[4];   // byte offsets from the stage's first A row
+
+    __device__ __forceinline__ static void table(uint32_t (&v)[4], int row0, int lane, uint32_t base) {
+        const int row = row0 + (lane & 31), h = lane >> 5;
+        const int s0 = (row ^ (row >> 3)) & 7;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            v[j] = base + (uint32_t)(row * 128 + 16 * (h ^ (s0 & 1)) + 32 * (j ^ (s0 >> 1)));
+    }
+
+    template <int BM, int TM, int TN>
+    __device__ __forceinline__ void init(int wm, int wn, int lane) {
+        table(va, wm * TM, lane, 0u);
+        table(vb, wn * TN, lane, (uint32_t)BM * 128u);
+    }
+};
+
+template <int FM, int FN>
+__device__ __forceinline__ void load_frags64(const uint16_t* sA, const FragAddr64& fa_addr, int kk,
+                                             bf16x8 (&fa)[FM], bf16x8 (&fb)[FN]) {
+    const char* base = reinterpret_cast<const char*>(sA);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+        fa[i] = *reinterpret_cast<const bf16x8*>(base + fa_addr.va[kk ^ (2 * (i & 1))] + 4096 * i);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+        fb[j] = *reinterpret_cast<const bf16x8*>(base + fa_addr.vb[kk ^ (2 * (j & 1))] + 4096 * j);
+}
+
 // F16: the fragments hold FP16 bit patterns (dequantized FP4), multiplied with
 // the FP16 MFMA of the same shape and rate.
 template <int FM, int FN, bool F16 = false>
@@ -729,7 +768,9 @@ gemm_mfma_kernel(KParams p) {
     lds_barrier();
 
     bf16x8 fa[2][FM], fb[2][FN];
-    if (nsteps > 0) load_frags<FM, FN, TM, TN, BK>(smem, smem + BM * BK, wm, wn, lane, 0, fa[0], fb[0]);
+    FragAddr64 fadr;
+    fadr.init<BM, TM, TN>(wm, wn, lane);
+    if (nsteps > 0) load_frags64<FM, FN>(smem, fadr, 0, fa[0], fb[0]);
 
     // Conversion of the held set is spread over the KK-1 leading sub-steps:
     // part kk covers units [U*kk/(KK-1), U*(kk+1)/(KK-1)) of the U = PA + PB
@@ -759,7 +800,7 @@ gemm_mfma_kernel(KParams p) {
 #pragma unroll
         for (int kk = 0; kk + 1 < KK; ++kk) {
             const int cur = kk & 1;
-            load_frags<FM, FN, TM, TN, BK>(sA, sA + BM * BK, wm, wn, lane, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
+            load_frags64<FM, FN>(sA, fadr, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
             store_part(held_a, held_b, dst, kk);
             mfma_block<FM, FN, SRC == SRC_FP4>(fa[cur], fb[cur], acc);
             interleave_mfma_cvt<FM * FN, FM + FN, CVT_VALU, CVT_DSW>();
@@ -768,7 +809,7 @@ gemm_mfma_kernel(KParams p) {
         // last step this reads a buffer of zeros (harmless).
         lds_barrier();
         const uint16_t* nA = smem + ((t + 1) & 1) * STAGE;
-        load_frags<FM, FN, TM, TN, BK>(nA, nA + BM * BK, wm, wn, lane, 0, fa[LAST ^ 1], fb[LAST ^ 1]);
+        load_frags64<FM, FN>(nA, fadr, 0, fa[LAST ^ 1], fb[LAST ^ 1]);
         mfma_block<FM, FN, SRC == SRC_FP4>(fa[LAST], fb[LAST], acc);
         interleave_mfma<FM * FN, FM + FN, 0>();
     };
@@ -786,7 +827,7 @@ gemm_mfma_kernel(KParams p) {
 #pragma unroll
         for (int kk = 0; kk + 1 < KK; ++kk) {
             const int cur = kk & 1;
-            load_frags<FM, FN, TM, TN, BK>(sA, sA + BM * BK, wm, wn, lane, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
+            load_frags64<FM, FN>(sA, fadr, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
             if (kk == KK - 2) {
                 // not earlier: hoisted conversions would wait for the loads
                 // just issued
@@ -802,7 +843,7 @@ gemm_mfma_kernel(KParams p) {
         if (t + 1 < nsteps) {
             lds_barrier();
             const uint16_t* nA = smem + ((t + 1) & 1) * STAGE;
-            load_frags<FM, FN, TM, TN, BK>(nA, nA + BM * BK, wm, wn, lane, 0, fa[LAST ^ 1], fb[LAST ^ 1]);
+            load_frags64<FM, FN>(nA, fadr, 0, fa[LAST ^ 1], fb[LAST ^ 1]);
         }
         mfma_block<FM, FN, SRC == SRC_FP4>(fa[LAST], fb[LAST], acc);
         interleave_mfma<FM * FN, FM + FN, 0>();
@@ -920,7 +961,16 @@ __device__ __forceinline__ void direct_mainloop(const KParams& p, const uint16_t
     static_assert(KK % 2 == 0, "fragment double buffer assumes an even sub-step count");
     constexpr int LAST = (KK - 1) & 1;
     bf16x8 fa[2][FM], fb[2][FN];
-    if (nsteps > 0) load_frags<FM, FN, TM, TN, BKS>(smem, smem + BM * BKS, wm, wn, lane, 0, fa[0], fb[0]);
+    FragAddr64 fadr;
+    if constexpr (BKS == 64) fadr.init<BM, TM, TN>(wm, wn, lane);
+    // fragments of sub-step kk of the stage at sA
+    auto frags = [&](const uint16_t* sA, int kk, bf16x8 (&a)[FM], bf16x8 (&b)[FN]) {
+        if constexpr (BKS == 64)
+            load_frags64<FM, FN>(sA, fadr, kk, a, b);
+        else
+            load_frags<FM, FN, TM, TN, BKS>(sA, sA + BM * BKS, wm, wn, lane, kk, a, b);
+    };
+    if (nsteps > 0) frags(smem, 0, fa[0], fb[0]);
 
     // The stage refilled after a step's barrier: part 0 right after the
     // barrier, parts 1..KK-1 at the starts of the next step's leading
@@ -934,7 +984,7 @@ __device__ __forceinline__ void direct_mainloop(const KParams& p, const uint16_t
         for (int kk = 0; kk + 1 < KK; ++kk) {
             const int cur = kk & 1;
             if (parts) issue_part(pk, pbuf, kk + 1);
-            load_frags<FM, FN, TM, TN, BKS>(sA, sA + BM * BKS, wm, wn, lane, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
+            frags(sA, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
             mfma_block<FM, FN>(fa[cur], fb[cur], acc);
             interleave_mfma<FM * FN, FM + FN, 0>();
         }
@@ -950,7 +1000,7 @@ __device__ __forceinline__ void direct_mainloop(const KParams& p, const uint16_t
         k_next += BKS;
         issue_part(pk, pbuf, 0);
         const uint16_t* nA = smem + ((t + 1) % STAGES) * STAGE;
-        load_frags<FM, FN, TM, TN, BKS>(nA, nA + BM * BKS, wm, wn, lane, 0, fa[LAST ^ 1], fb[LAST ^ 1]);
+        frags(nA, 0, fa[LAST ^ 1], fb[LAST ^ 1]);
         mfma_block<FM, FN>(fa[LAST], fb[LAST], acc);
         interleave_mfma<FM * FN, FM + FN, 0>();
     }
