@@ -78,10 +78,12 @@ struct KParams {
     // Bq, SFB (bytes) and C (elements); zero for one problem
     int64_t bs_a, bs_sa, bs_b, bs_sb, bs_c;
     // two products of the same A in one launch (direct kernels, BF16 store):
-    // column tiles [dual_tiles_n, 2*dual_tiles_n) of the grid compute
-    // C1 = A * B1^T; 0 for a single problem
+    // `dual` requests it (B1 may be NULL when K = 0); the launcher then sets
+    // dual_tiles_n, and column tiles [dual_tiles_n, 2*dual_tiles_n) of the
+    // grid compute C1 = A * B1^T; 0 for a single problem
     const uint16_t* B1;
     void* C1;
+    int dual;
     int dual_tiles_n;
 };
 
@@ -1107,7 +1109,7 @@ hipError_t launch_direct(const KParams& kp, int splits, hipStream_t stream) {
     q.tiles_m = (kp.M + BM - 1) / BM;
     q.tiles_n = (kp.N + BN - 1) / BN;
     q.dual_tiles_n = 0;
-    if (kp.B1 != nullptr) {   // dual launch: the second product's tiles follow the first's
+    if (kp.dual) {   // dual launch: the second product's tiles follow the first's
         q.dual_tiles_n = q.tiles_n;
         q.tiles_n *= 2;
     }
@@ -1357,6 +1359,7 @@ hipError_t launch_dense_dual(const DenseProblem& p, const uint16_t* B1, uint16_t
     kp.C = p.C;
     kp.B1 = B1;
     kp.C1 = C1;
+    kp.dual = 1;
     kp.M = (int)p.M;
     kp.N = (int)p.N;
     kp.K = (int)p.K;

@@ -97,3 +97,15 @@ def test_dual_repeat_runs_are_identical():
     for c0, c1 in outs[1:]:
         assert_bits_equal(bits_of(c0), bits_of(outs[0][0]), "repeat C0")
         assert_bits_equal(bits_of(c1), bits_of(outs[0][1]), "repeat C1")
+
+
+def test_dual_k_zero_gives_positive_zero():
+    """K = 0: both outputs are the empty sum, +0, over their whole extent."""
+    dev = "cuda"
+    a = torch.empty((70, 0), dtype=torch.bfloat16, device=dev)
+    b = torch.empty((40, 0), dtype=torch.bfloat16, device=dev)
+    c0 = torch.full((70, 40), 1.0, dtype=torch.bfloat16, device=dev)
+    c1 = torch.full((70, 40), -1.0, dtype=torch.bfloat16, device=dev)
+    bg.gemm_bf16_dual(a, b, b.clone(), out0=c0, out1=c1)
+    torch.cuda.synchronize()
+    assert not bits_of(c0).any() and not bits_of(c1).any()
