@@ -57,7 +57,24 @@ enum Source : int {
     SRC_FP4 = 2,        // both operands FP4, dequantized to FP16
     SRC_W4A16 = 3,
     SRC_FP4_BF16 = 4,   // staging only: FP4 dequantized to BF16
+    // the same with 32-element staging units (K % 32 == 0)
+    SRC_FP4W = 5,
+    SRC_W4A16W = 6,
+    SRC_FP4W_BF16 = 7,
 };
+
+constexpr bool src_fp4(int src) { return src == SRC_FP4 || src == SRC_FP4W; }
+constexpr bool src_w4a16(int src) { return src == SRC_W4A16 || src == SRC_W4A16W; }
+// K elements per staging unit of an FP4 operand of `rows` tile rows staged by
+// nt threads (0: not FP4). The 32-element units are taken only where they
+// divide evenly among the threads: otherwise some waves would convert twice
+// as many elements as others, and every step waits for the slowest.
+constexpr int fp4_unit(int src, int rows, int nt) {
+    return src == SRC_FP4 || src == SRC_FP4_BF16                      ? 16
+           : (src == SRC_FP4W || src == SRC_FP4W_BF16) && rows * 2 % nt == 0 ? 32
+           : src == SRC_FP4W || src == SRC_FP4W_BF16                  ? 16
+                                                                      : 0;
+}
 
 struct KParams {
     const uint16_t* A;     // bf16 [M,K]            (SRC_BF16_*)
@@ -241,64 +258,77 @@ struct Stager<ROWS, NT, SRC_BF16_SCALAR, BKS> {
     __device__ __forceinline__ void store(uint16_t* lds, int tid) const { store_units(lds, tid, 0, PER); }
 };
 
-// Block-scaled FP4: a unit is one 16-element scale group of one row (8 packed
-// bytes + 1 scale byte); it is dequantized exactly while being written to LDS
-// as two 16-byte chunks. Every e2m1 value, every e4m3 scale and their product
-// (at most 6 significant bits, magnitude between 2^-10 and 2688, or zero, or
-// NaN from a NaN scale) is exact in FP16 and in BF16.
+// Block-scaled FP4: a unit is UE consecutive K elements of one row (UE / 2
+// packed bytes and UE / 16 scale bytes); it is dequantized exactly while being
+// written to LDS as UE / 8 16-byte chunks. Every e2m1 value, every e4m3 scale
+// and their product (at most 6 significant bits, magnitude between 2^-10 and
+// 2688, or zero, or NaN from a NaN scale) is exact in FP16 and in BF16.
 //  - F16OUT (both operands FP4, FP16 MFMA): FP16 convert, then half a packed
 //    FP16 multiply per element; the multiply rounds nothing.
 //  - BF16 (W4A16 weights next to BF16 activations, BF16 MFMA): FP32 convert,
 //    FP32 multiply (exact), BF16 pack (exact).
-template <int ROWS, int NT, bool F16OUT>
+// UE = 32 (K % 32 == 0): one 16-byte load and one 2-byte scale load per unit,
+// two lanes per 32-byte row step: a quarter of the load instructions of
+// UE = 16 (an 8-byte and a 1-byte load per 16 elements) and fewer registers
+// per held step, so the 256 x 256 FP16 tile holds two steps without spilling.
+// UE = 16 serves K % 32 == 16, where a 32-element unit would straddle the end
+// of K, and operands whose 32-element units do not divide evenly among the
+// threads.
+template <int ROWS, int NT, bool F16OUT, int UE = 16>
 struct Fp4Stager {
-    static constexpr int PER = ROWS * (BK / 16) / NT;
-    static_assert(PER * NT == ROWS * (BK / 16), "tile not divisible among threads");
-    u32x2 w[PER];
+    static_assert(UE == 16 || UE == 32, "unit of one or two scale groups");
+    static constexpr int UPR = BK / UE;                  // units per row step
+    static constexpr int UNITS = ROWS * UPR;
+    static constexpr int PER = (UNITS + NT - 1) / NT;    // surplus slots (u >= UNITS) do nothing
+    static constexpr int WORDS = UE / 8;                 // 32-bit words of packed data per unit
+    typedef uint32_t Words __attribute__((ext_vector_type(WORDS)));
+    Words w[PER];
     uint32_t s[PER];
     uint32_t valid;   // bit i: unit i lies inside the K range (applied when converting)
 
     __device__ __forceinline__ void load(const uint8_t* q, const uint8_t* sf, int row0,
                                          int nrows, int K, int k0, int k_end, int tid) {
+        valid = 0u;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int u = tid + i * NT;
-            const int row = u >> 2, g = u & 3;
+            if (PER * NT != UNITS && u >= UNITS) break;
+            const int row = u / UPR, g = u % UPR;
             const int grow = min(row0 + row, nrows - 1);
-            const int gk = k0 + g * 16;
-            // always load from a valid group (K >= 16 whenever a step exists),
-            // then zero what lies past the end of this K range
-            const int gkc = min(gk, K - 16);
-            w[i] = *reinterpret_cast<const u32x2*>(q + (int64_t)grow * (K >> 1) + (gkc >> 1));
-            s[i] = sf[(int64_t)grow * (K >> 4) + (gkc >> 4)];
-            if (i == 0) valid = 0u;
+            const int gk = k0 + g * UE;
+            // always load from a valid unit (K >= UE whenever a step exists:
+            // K is a multiple of UE), then zero what lies past the end of this
+            // K range (k_end is a multiple of UE too)
+            const int gkc = min(gk, K - UE);
+            w[i] = *reinterpret_cast<const Words*>(q + (int64_t)grow * (K >> 1) + (gkc >> 1));
+            if constexpr (UE == 16)
+                s[i] = sf[(int64_t)grow * (K >> 4) + (gkc >> 4)];
+            else
+                s[i] = *reinterpret_cast<const uint16_t*>(sf + (int64_t)grow * (K >> 4) + (gkc >> 4));
             valid |= (gk < k_end ? 1u : 0u) << i;
         }
     }
 
-    // Two e2m1 values (byte `byte` of word: low nibble first) times the
-    // scale, as two packed 16-bit values.
-    __device__ __forceinline__ static uint32_t deq2(uint32_t word, f16x2 sc16, float sc32, int byte) {
+    // Eight e2m1 values (word: low nibble first) times the scale, as four
+    // packed 16-bit pairs. sc16 holds the scale in both halves.
+    __device__ __forceinline__ static u32x4 deq8(uint32_t word, f16x2 sc16, float sc32) {
+        u32x4 r;
         if constexpr (F16OUT) {
-            f16x2 v;
-            switch (byte) {   // byte select must be an immediate
-                case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0); break;
-                case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1); break;
-                case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2); break;
-                default: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3); break;
-            }
-            const f16x2 sc = {sc16.x, sc16.x};
-            return __builtin_bit_cast(uint32_t, v * sc);   // v_pk_mul_f16, exact
+            r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * sc16);
+            r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * sc16);
+            r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * sc16);
+            r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * sc16);
         } else {
-            f32x2 v;
-            switch (byte) {
-                case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0); break;
-                case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1); break;
-                case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2); break;
-                default: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3); break;
-            }
-            return pack_bf16x2(v.x * sc32, v.y * sc32);
+            f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0);
+            r.x = pack_bf16x2(v.x * sc32, v.y * sc32);
+            v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1);
+            r.y = pack_bf16x2(v.x * sc32, v.y * sc32);
+            v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2);
+            r.z = pack_bf16x2(v.x * sc32, v.y * sc32);
+            v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3);
+            r.w = pack_bf16x2(v.x * sc32, v.y * sc32);
         }
+        return r;
     }
 
     __device__ __forceinline__ void store(uint16_t* lds, int tid) const { store_units(lds, tid, 0, PER); }
@@ -309,24 +339,27 @@ struct Fp4Stager {
         for (int i = 0; i < PER; ++i) {
             if (i < lo || i >= hi) continue;
             const int u = tid + i * NT;
-            const int row = u >> 2, g = u & 3;
+            if (PER * NT != UNITS && u >= UNITS) break;
+            const int row = u / UPR, g = u % UPR;
             const bool in = (valid >> i) & 1u;
-            const uint32_t wx = in ? w[i].x : 0u, wy = in ? w[i].y : 0u;
-            // e4m3fn byte -> FP16 or FP32 (exact, NaN stays NaN); a unit past
+            // e4m3fn bytes -> FP16 or FP32 (exact, NaN stays NaN); a unit past
             // the K range gets scale 0 and zero data
             const uint32_t sb = in ? s[i] : 0u;
             f16x2 sc16 = {};
-            float sc32 = 0.0f;
+            f32x2 sc32 = {};
             if constexpr (F16OUT)
                 sc16 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
             else
-                sc32 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sb, 1.0f, false)[0];
-            const u32x4 lo = {deq2(wx, sc16, sc32, 0), deq2(wx, sc16, sc32, 1), deq2(wx, sc16, sc32, 2),
-                              deq2(wx, sc16, sc32, 3)};
-            const u32x4 hi = {deq2(wy, sc16, sc32, 0), deq2(wy, sc16, sc32, 1), deq2(wy, sc16, sc32, 2),
-                              deq2(wy, sc16, sc32, 3)};
-            *reinterpret_cast<u32x4*>(lds + row * BK + chunk_slot<8>(row, 2 * g) * 8) = lo;
-            *reinterpret_cast<u32x4*>(lds + row * BK + chunk_slot<8>(row, 2 * g + 1) * 8) = hi;
+                sc32 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sb, 1.0f, false);
+            uint16_t* dst = lds + row * BK;
+#pragma unroll
+            for (int c = 0; c < WORDS; ++c) {
+                // word c holds elements 8c .. 8c+7 of the unit: scale group c / 2
+                const uint32_t wc = in ? w[i][c] : 0u;
+                const f16x2 s16 = c < 2 ? f16x2{sc16.x, sc16.x} : f16x2{sc16.y, sc16.y};
+                const float s32 = c < 2 ? sc32.x : sc32.y;
+                *reinterpret_cast<u32x4*>(dst + chunk_slot<8>(row, WORDS * g + c) * 8) = deq8(wc, s16, s32);
+            }
         }
     }
 };
@@ -336,6 +369,12 @@ struct Stager<ROWS, NT, SRC_FP4, BK> : Fp4Stager<ROWS, NT, true> {};
 
 template <int ROWS, int NT>
 struct Stager<ROWS, NT, SRC_FP4_BF16, BK> : Fp4Stager<ROWS, NT, false> {};
+
+template <int ROWS, int NT>
+struct Stager<ROWS, NT, SRC_FP4W, BK> : Fp4Stager<ROWS, NT, true, fp4_unit(SRC_FP4W, ROWS, NT)> {};
+
+template <int ROWS, int NT>
+struct Stager<ROWS, NT, SRC_FP4W_BF16, BK> : Fp4Stager<ROWS, NT, false, fp4_unit(SRC_FP4W_BF16, ROWS, NT)> {};
 
 // ---------------------------------------------------------------------------
 // Direct global -> LDS staging (buffer_load_dwordx4 ... lds) for BF16 rows
@@ -700,7 +739,7 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[FM][FN]) {
 template <int BM, int BN, int WM, int WN, int EPI, int SRC, int RSETS = 2>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_mfma_kernel(KParams p) {
-    if constexpr (SRC == SRC_FP4) {
+    if constexpr (src_fp4(SRC)) {
         const int64_t l = blockIdx.z;   // batch index (0 for one problem)
         p.Aq += l * p.bs_a;
         p.SFA += l * p.bs_sa;
@@ -734,8 +773,8 @@ gemm_mfma_kernel(KParams p) {
     f32x16 acc[FM][FN];
     zero_acc(acc);
 
-    constexpr int SRC_A = SRC == SRC_W4A16 ? SRC_BF16_VEC : SRC;
-    constexpr int SRC_B = SRC == SRC_W4A16 ? SRC_FP4_BF16 : SRC;
+    constexpr int SRC_A = src_w4a16(SRC) ? SRC_BF16_VEC : SRC;
+    constexpr int SRC_B = SRC == SRC_W4A16 ? SRC_FP4_BF16 : SRC == SRC_W4A16W ? SRC_FP4W_BF16 : SRC;
     // RSETS register sets form a ring: set r holds the steps t with t % RSETS == r
     constexpr int NSETS = RSETS > 1 ? RSETS : 1;
     Stager<BM, NT, SRC_A> sa[NSETS];
@@ -743,10 +782,10 @@ gemm_mfma_kernel(KParams p) {
     Stager<BM, NT, SRC_A>& sa0 = sa[0];
     Stager<BN, NT, SRC_B>& sb0 = sb[0];
     auto load = [&](auto& sa, auto& sb, int k0) {
-        if constexpr (SRC == SRC_FP4) {
+        if constexpr (src_fp4(SRC)) {
             sa.load(p.Aq, p.SFA, m0, p.M, p.K, k0, ke, tid);
             sb.load(p.Bq, p.SFB, n0, p.N, p.K, k0, ke, tid);
-        } else if constexpr (SRC == SRC_W4A16) {
+        } else if constexpr (src_w4a16(SRC)) {
             sa.load(p.A, m0, p.M, p.lda, k0, ke, tid);
             sb.load(p.Bq, p.SFB, n0, p.N, p.K, k0, ke, tid);
         } else {
@@ -779,9 +818,12 @@ gemm_mfma_kernel(KParams p) {
     // units (A's first), interleaved with that sub-step's MFMAs.
     constexpr int PA = Stager<BM, NT, SRC_A>::PER, PB = Stager<BN, NT, SRC_B>::PER, U = PA + PB;
     // approximate VALU instructions and LDS writes per unit, for the schedule
-    constexpr int VU_A = SRC_A == SRC_FP4 ? 24 : 0;
-    constexpr int VU_B = SRC_B == SRC_FP4 ? 24 : SRC_B == SRC_FP4_BF16 ? 32 : 0;
-    constexpr int WU_A = SRC_A == SRC_FP4 ? 2 : 1, WU_B = SRC_B == SRC_BF16_VEC || SRC_B == SRC_BF16_SCALAR ? 1 : 2;
+    // (per 16 FP4 elements: 24 to FP16, 32 to BF16, and two 16-byte writes)
+    constexpr int UEA = fp4_unit(SRC_A, BM, NT), UEB = fp4_unit(SRC_B, BN, NT);
+    constexpr int VU_A = src_fp4(SRC_A) ? 24 * UEA / 16 : 0;
+    constexpr int VU_B = src_fp4(SRC_B) ? 24 * UEB / 16 : UEB * 2;
+    constexpr int WU_A = UEA ? UEA / 8 : 1;
+    constexpr int WU_B = UEB ? UEB / 8 : 1;
     constexpr int CVT_VALU = (PA * VU_A + PB * VU_B + KK - 2) / (KK - 1);
     constexpr int CVT_DSW = (PA * WU_A + PB * WU_B + KK - 2) / (KK - 1);
     auto store_part = [&](auto& sa, auto& sb, uint16_t* buf, int part) {
@@ -804,7 +846,7 @@ gemm_mfma_kernel(KParams p) {
             const int cur = kk & 1;
             load_frags64<FM, FN>(sA, fadr, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
             store_part(held_a, held_b, dst, kk);
-            mfma_block<FM, FN, SRC == SRC_FP4>(fa[cur], fb[cur], acc);
+            mfma_block<FM, FN, src_fp4(SRC)>(fa[cur], fb[cur], acc);
             interleave_mfma_cvt<FM * FN, FM + FN, CVT_VALU, CVT_DSW>();
         }
         // step t+1 is in LDS for every wave; step t's buffer is free. Past the
@@ -812,7 +854,7 @@ gemm_mfma_kernel(KParams p) {
         lds_barrier();
         const uint16_t* nA = smem + ((t + 1) & 1) * STAGE;
         load_frags64<FM, FN>(nA, fadr, 0, fa[LAST ^ 1], fb[LAST ^ 1]);
-        mfma_block<FM, FN, SRC == SRC_FP4>(fa[LAST], fb[LAST], acc);
+        mfma_block<FM, FN, src_fp4(SRC)>(fa[LAST], fb[LAST], acc);
         interleave_mfma<FM * FN, FM + FN, 0>();
     };
 
@@ -835,10 +877,10 @@ gemm_mfma_kernel(KParams p) {
                 // just issued
                 __builtin_amdgcn_sched_barrier(0);
                 store(sa0, sb0, smem + ((t + 1) & 1) * STAGE);
-                mfma_block<FM, FN, SRC == SRC_FP4>(fa[cur], fb[cur], acc);
+                mfma_block<FM, FN, src_fp4(SRC)>(fa[cur], fb[cur], acc);
                 interleave_mfma_cvt<FM * FN, FM + FN, CVT_VALU * (KK - 1), CVT_DSW * (KK - 1)>();
             } else {
-                mfma_block<FM, FN, SRC == SRC_FP4>(fa[cur], fb[cur], acc);
+                mfma_block<FM, FN, src_fp4(SRC)>(fa[cur], fb[cur], acc);
                 interleave_mfma<FM * FN, FM + FN, 0>();
             }
         }
@@ -847,7 +889,7 @@ gemm_mfma_kernel(KParams p) {
             const uint16_t* nA = smem + ((t + 1) & 1) * STAGE;
             load_frags64<FM, FN>(nA, fadr, 0, fa[LAST ^ 1], fb[LAST ^ 1]);
         }
-        mfma_block<FM, FN, SRC == SRC_FP4>(fa[LAST], fb[LAST], acc);
+        mfma_block<FM, FN, src_fp4(SRC)>(fa[LAST], fb[LAST], acc);
         interleave_mfma<FM * FN, FM + FN, 0>();
     };
 
@@ -1410,6 +1452,47 @@ int choose_w4a16(int M, int N, int cus) {
     return best;
 }
 
+// FP4 tile choices (BLOCKGEMM_FP4_TILE and BLOCKGEMM_FP4_SK_TILE, tuning
+// hooks, force one when `tuned`).
+template <int SRC>
+hipError_t launch_fp4_src(const KParams& kp, int M, int splits, int batch, bool tuned, hipStream_t stream) {
+    // FP32 planes (split-K) for the small-M decode shapes
+    if (splits > 1) {
+        int sk = tuned ? env_int("BLOCKGEMM_FP4_SK_TILE") : -1;
+        if (sk < 0) sk = M <= 192 ? 3 : 2;
+        if constexpr (SRC == SRC_FP4W) {
+            switch (sk) {
+                case 0: return launch_cfg<128, 128, 2, 2, EPI_STORE_F32, SRC, 2>(kp, splits, stream);
+                case 1: return launch_cfg<128, 256, 2, 4, EPI_STORE_F32, SRC, 1>(kp, splits, stream);
+                case 4: return launch_cfg<128, 256, 2, 4, EPI_STORE_F32, SRC, 3>(kp, splits, stream);
+                case 5: return launch_cfg<128, 256, 2, 4, EPI_STORE_F32, SRC, 4>(kp, splits, stream);
+                case 6: return launch_cfg<128, 128, 2, 2, EPI_STORE_F32, SRC, 4>(kp, splits, stream);
+                default: break;
+            }
+        }
+        if (sk == 3) return launch_cfg<128, 256, 2, 4, EPI_STORE_F32, SRC, 2>(kp, splits, stream);
+        return launch_cfg<256, 256, 2, 4, EPI_STORE_F32, SRC, 1>(kp, splits, stream);
+    }
+    int cfg = tuned ? env_int("BLOCKGEMM_FP4_TILE") : -1;
+    // 256 x 256 tiles with two register sets where the 32-element units
+    // leave room for them (3% ahead of one set on 4096 x 4096 x 8192)
+    if (cfg < 0) cfg = M <= 192 ? 2 : SRC == SRC_FP4W ? 1 : 0;
+    if constexpr (SRC == SRC_FP4W) {
+        switch (cfg) {
+            case 1: return launch_cfg<256, 256, 2, 4, EPI_STORE_BF16, SRC, 2>(kp, 1, stream, batch);
+            case 3: return launch_cfg<256, 256, 2, 2, EPI_STORE_BF16, SRC, 1>(kp, 1, stream, batch);
+            case 5: return launch_cfg<128, 256, 2, 4, EPI_STORE_BF16, SRC, 2>(kp, 1, stream, batch);
+            case 6: return launch_cfg<256, 128, 4, 2, EPI_STORE_BF16, SRC, 2>(kp, 1, stream, batch);
+            case 7: return launch_cfg<128, 256, 2, 4, EPI_STORE_BF16, SRC, 3>(kp, 1, stream, batch);
+            case 8: return launch_cfg<256, 128, 4, 2, EPI_STORE_BF16, SRC, 3>(kp, 1, stream, batch);
+            case 9: return launch_cfg<128, 256, 2, 4, EPI_STORE_BF16, SRC, 4>(kp, 1, stream, batch);
+            default: break;
+        }
+    }
+    if (cfg == 2) return launch_cfg<128, 128, 2, 2, EPI_STORE_BF16, SRC, 2>(kp, 1, stream, batch);
+    return launch_cfg<256, 256, 2, 4, EPI_STORE_BF16, SRC, 1>(kp, 1, stream, batch);
+}
+
 hipError_t launch_fp4(const Fp4Problem& p, hipStream_t stream) {
     KParams kp{};
     kp.Aq = p.A;
@@ -1431,33 +1514,10 @@ hipError_t launch_fp4(const Fp4Problem& p, hipStream_t stream) {
         kp.bs_sb = (int64_t)p.N * (p.K / 16);
         kp.bs_c = (int64_t)p.M * p.N;
     }
-    // FP32 planes (split-K) for the small-M decode shapes
-    if (splits > 1) {
-        int sk = env_int("BLOCKGEMM_FP4_SK_TILE");   // tuning only
-        if (sk < 0) sk = p.M <= 192 ? 3 : 2;
-        switch (sk) {
-            case 0: return launch_cfg<128, 128, 2, 2, EPI_STORE_F32, SRC_FP4, 2>(kp, splits, stream);
-            case 1: return launch_cfg<128, 256, 2, 4, EPI_STORE_F32, SRC_FP4, 1>(kp, splits, stream);
-            case 3: return launch_cfg<128, 256, 2, 4, EPI_STORE_F32, SRC_FP4, 2>(kp, splits, stream);
-            case 4: return launch_cfg<128, 256, 2, 4, EPI_STORE_F32, SRC_FP4, 3>(kp, splits, stream);
-            case 5: return launch_cfg<128, 256, 2, 4, EPI_STORE_F32, SRC_FP4, 4>(kp, splits, stream);
-            case 6: return launch_cfg<128, 128, 2, 2, EPI_STORE_F32, SRC_FP4, 4>(kp, splits, stream);
-            default: return launch_cfg<256, 256, 2, 4, EPI_STORE_F32, SRC_FP4, 1>(kp, splits, stream);
-        }
-    }
-    int cfg = env_int("BLOCKGEMM_FP4_TILE");   // tuning only
-    if (cfg < 0) cfg = p.M <= 192 ? 2 : 0;
-    switch (cfg) {
-        case 1: return launch_cfg<256, 256, 2, 4, EPI_STORE_BF16, SRC_FP4, 2>(kp, 1, stream, batch);
-        case 2: return launch_cfg<128, 128, 2, 2, EPI_STORE_BF16, SRC_FP4, 2>(kp, 1, stream, batch);
-        case 3: return launch_cfg<256, 256, 2, 2, EPI_STORE_BF16, SRC_FP4, 1>(kp, 1, stream, batch);
-        case 5: return launch_cfg<128, 256, 2, 4, EPI_STORE_BF16, SRC_FP4, 2>(kp, 1, stream, batch);
-        case 6: return launch_cfg<256, 128, 4, 2, EPI_STORE_BF16, SRC_FP4, 2>(kp, 1, stream, batch);
-        case 7: return launch_cfg<128, 256, 2, 4, EPI_STORE_BF16, SRC_FP4, 3>(kp, 1, stream, batch);
-        case 8: return launch_cfg<256, 128, 4, 2, EPI_STORE_BF16, SRC_FP4, 3>(kp, 1, stream, batch);
-        case 9: return launch_cfg<128, 256, 2, 4, EPI_STORE_BF16, SRC_FP4, 4>(kp, 1, stream, batch);
-        default: return launch_cfg<256, 256, 2, 4, EPI_STORE_BF16, SRC_FP4, 1>(kp, 1, stream, batch);
-    }
+    // 32-element staging units when no unit can straddle the end of K; the
+    // 16-element units (K % 32 == 16) take the default tiles only
+    if (p.K % 32 == 0) return launch_fp4_src<SRC_FP4W>(kp, (int)p.M, splits, batch, true, stream);
+    return launch_fp4_src<SRC_FP4>(kp, (int)p.M, splits, batch, false, stream);
 }
 
 // Blocked (NVIDIA hardware) scale layout -> plain [L, rows, k_groups]: the
@@ -1506,16 +1566,20 @@ hipError_t launch_w4a16(const W4a16Problem& p, hipStream_t stream) {
     kp.scale = p.scale_2;
     int cfg = env_int("BLOCKGEMM_W4A16_TILE");
     if (cfg < 0) cfg = choose_w4a16(kp.M, kp.N, p.cus > 0 ? (int)p.cus : 256);
+    // 32-element weight units when no unit can straddle the end of K; the
+    // 16-element units (K % 32 == 16) take the 256 x 256 tile
+    if (p.K % 32 != 0) return launch_cfg<256, 256, 2, 4, EPI_SCALE_BF16, SRC_W4A16, 1>(kp, 1, stream);
+    constexpr int S = SRC_W4A16W;
     switch (cfg) {
-        case 1: return launch_cfg<128, 256, 2, 4, EPI_SCALE_BF16, SRC_W4A16, 1>(kp, 1, stream);
-        case 2: return launch_cfg<128, 128, 2, 2, EPI_SCALE_BF16, SRC_W4A16, 2>(kp, 1, stream);
-        case 3: return launch_cfg<256, 256, 2, 2, EPI_SCALE_BF16, SRC_W4A16, 1>(kp, 1, stream);
-        case 4: return launch_cfg<128, 384, 2, 4, EPI_SCALE_BF16, SRC_W4A16, 1>(kp, 1, stream);
-        case 5: return launch_cfg<256, 192, 2, 3, EPI_SCALE_BF16, SRC_W4A16, 1>(kp, 1, stream);
-        case 6: return launch_cfg<128, 384, 2, 4, EPI_SCALE_BF16, SRC_W4A16, 2>(kp, 1, stream);
-        case 7: return launch_cfg<128, 256, 2, 4, EPI_SCALE_BF16, SRC_W4A16, 2>(kp, 1, stream);
-        case 9: return launch_cfg<128, 256, 2, 4, EPI_SCALE_BF16, SRC_W4A16, 3>(kp, 1, stream);
-        default: return launch_cfg<256, 256, 2, 4, EPI_SCALE_BF16, SRC_W4A16, 1>(kp, 1, stream);
+        case 1: return launch_cfg<128, 256, 2, 4, EPI_SCALE_BF16, S, 1>(kp, 1, stream);
+        case 2: return launch_cfg<128, 128, 2, 2, EPI_SCALE_BF16, S, 2>(kp, 1, stream);
+        case 3: return launch_cfg<256, 256, 2, 2, EPI_SCALE_BF16, S, 1>(kp, 1, stream);
+        case 4: return launch_cfg<128, 384, 2, 4, EPI_SCALE_BF16, S, 1>(kp, 1, stream);
+        case 5: return launch_cfg<256, 192, 2, 3, EPI_SCALE_BF16, S, 1>(kp, 1, stream);
+        case 6: return launch_cfg<128, 384, 2, 4, EPI_SCALE_BF16, S, 2>(kp, 1, stream);
+        case 7: return launch_cfg<128, 256, 2, 4, EPI_SCALE_BF16, S, 2>(kp, 1, stream);
+        case 9: return launch_cfg<128, 256, 2, 4, EPI_SCALE_BF16, S, 3>(kp, 1, stream);
+        default: return launch_cfg<256, 256, 2, 4, EPI_SCALE_BF16, S, 1>(kp, 1, stream);
     }
 }
 
