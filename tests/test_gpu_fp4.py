@@ -18,7 +18,8 @@ def _run(a, sfa, b, sfb):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 1, 16), (65, 129, 48), (7, 300, 64), (130, 66, 272),
-                                   (257, 255, 1040), (128, 128, 128), (33, 17, 16 * 33)])
+                                   (257, 255, 1040), (128, 128, 128), (33, 17, 16 * 33),
+                                   (1, 1, 32), (65, 129, 96), (300, 200, 1056)])
 def test_fp4_edge_shapes(m, n, k):
     print(f"fp4 edge m={m} n={n} k={k}", flush=True)
     a, b = synthetic.fp4_packed(m, k, 60, 0), synthetic.fp4_packed(n, k, 60, 1)
@@ -67,11 +68,18 @@ def test_fp4_config_sampled_rows():
                 oracle.rms(oracle.dequant_fp4(b, sfb)), "fp4 config")
 
 
+# K % 32 == 16 takes 16-element FP4 staging units and the default tiles;
+# K % 32 == 0 takes 32-element units and every forced tile (the K = 96,
+# 224 and 1056 cases end in half a 64-wide step)
+FP4_TILE_SHAPES = [(1, 1, 16), (65, 129, 48), (257, 255, 1040), (300, 520, 208),
+                   (1, 1, 32), (65, 129, 96), (257, 255, 1056), (300, 520, 224)]
+
+
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 5, 6, 7, 8, 9])
 def test_every_fp4_tile_config(cfg, monkeypatch):
     """Each FP4 tile variant (BLOCKGEMM_FP4_TILE, a tuning hook) on ragged shapes."""
     monkeypatch.setenv("BLOCKGEMM_FP4_TILE", str(cfg))
-    for m, n, k in [(1, 1, 16), (65, 129, 48), (257, 255, 1040), (300, 520, 208)]:
+    for m, n, k in FP4_TILE_SHAPES:
         a, b = synthetic.fp4_packed(m, k, 70 + cfg, 0), synthetic.fp4_packed(n, k, 70 + cfg, 1)
         sfa = synthetic.e4m3_uniform(m, k // 16, 2 ** -4, 2 ** 4, 70, 4)
         sfb = synthetic.e4m3_uniform(n, k // 16, 2 ** -4, 2 ** 4, 70, 5)
@@ -89,8 +97,9 @@ def test_every_fp4_tile_config(cfg, monkeypatch):
 # batched FP4, FP4 split-K (decode shapes) and the blocked-scale importer
 # ---------------------------------------------------------------------------
 
-def test_fp4_batched_equals_per_problem_calls():
-    L, m, n, k = 3, 130, 66, 272
+@pytest.mark.parametrize("L,m,n,k", [(3, 130, 66, 272), (3, 130, 66, 288), (2, 260, 70, 288)])
+def test_fp4_batched_equals_per_problem_calls(L, m, n, k):
+    print(f"fp4 batched L={L} m={m} n={n} k={k}", flush=True)
     a = np.stack([synthetic.fp4_packed(m, k, 130 + l, 0) for l in range(L)])
     b = np.stack([synthetic.fp4_packed(n, k, 130 + l, 1) for l in range(L)])
     sfa = np.stack([synthetic.e4m3_uniform(m, k // 16, 2 ** -4, 2 ** 4, 130 + l, 4) for l in range(L)])
@@ -202,7 +211,7 @@ def test_every_fp4_splitk_tile(tile, monkeypatch):
     """Each FP4 split-K tile (BLOCKGEMM_FP4_SK_TILE, a tuning hook): planes
     summed in order equal the exact result on power-of-two scales."""
     monkeypatch.setenv("BLOCKGEMM_FP4_SK_TILE", str(tile))
-    for m, n, k, ks in [(128, 384, 4096, 8), (65, 129, 1040, 3), (300, 520, 2048, 5)]:
+    for m, n, k, ks in [(128, 384, 4096, 8), (65, 129, 1040, 3), (300, 520, 2048, 5), (65, 129, 1056, 3)]:
         a, b = synthetic.fp4_packed(m, k, 150 + tile, 0), synthetic.fp4_packed(n, k, 150 + tile, 1)
         sfa = synthetic.e4m3_choice(m, k // 16, [0x38, 0x40], 150, 4)
         sfb = synthetic.e4m3_choice(n, k // 16, [0x38, 0x40], 150, 5)

@@ -29,7 +29,8 @@ def _check(a, b, sfb, s2, rows=None, what=""):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 1, 16), (65, 129, 48), (7, 300, 64), (130, 66, 272),
-                                   (257, 255, 1040), (33, 17, 528), (300, 520, 2048)])
+                                   (257, 255, 1040), (33, 17, 528), (300, 520, 2048),
+                                   (65, 129, 96), (300, 200, 1056)])
 def test_w4a16_edge_shapes(m, n, k):
     print(f"w4a16 edge m={m} n={n} k={k}", flush=True)
     a = synthetic.normal_bf16((m, k), 1.0, 100 + m, 0)
@@ -55,11 +56,18 @@ def test_w4a16_qkvz_workload_all_rows():
     _check(a, b, sfb, s2, what="w4a16 qkvz")
 
 
+# K % 32 == 16 takes 16-element FP4 staging units and the default tiles;
+# K % 32 == 0 takes 32-element units and every forced tile (the K = 96,
+# 224 and 1056 cases end in half a 64-wide step)
+FP4_TILE_SHAPES = [(1, 1, 16), (65, 129, 48), (257, 255, 1040), (300, 520, 208),
+                   (1, 1, 32), (65, 129, 96), (257, 255, 1056), (300, 520, 224)]
+
+
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 6, 7, 9])
 def test_every_w4a16_tile_config(cfg, monkeypatch):
     """Each W4A16 tile variant (BLOCKGEMM_W4A16_TILE, a tuning hook) on ragged shapes."""
     monkeypatch.setenv("BLOCKGEMM_W4A16_TILE", str(cfg))
-    for m, n, k in [(1, 1, 16), (65, 129, 48), (257, 255, 1040), (300, 520, 208)]:
+    for m, n, k in FP4_TILE_SHAPES:
         a = synthetic.normal_bf16((m, k), 1.0, 110 + cfg, 0)
         b = synthetic.fp4_packed(n, k, 110 + cfg, 1)
         sfb = synthetic.e4m3_uniform(n, k // 16, 2 ** -4, 2 ** 4, 110, 5)
