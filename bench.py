@@ -588,7 +588,10 @@ def cpu_baseline(gemms, seconds):
     threads = min(16, cpp.hardware_threads())   # the host share of one GPU
 
     def rate(fn, a, w, budget):
-        rows, t, flops, done = 8, 0.0, 0.0, 0
+        """Calls fn on the leading r rows (r grows toward the budget, capped at
+        all rows, so a fast oracle repeats whole passes) until `budget` seconds
+        of wall time; returns flops, seconds and a description of the sample."""
+        rows, t, flops, done, calls, top = 8, 0.0, 0.0, 0, 0, 0
         while t < budget:
             r = min(rows, a.shape[0])
             t0 = time.time()
@@ -596,31 +599,31 @@ def cpu_baseline(gemms, seconds):
             dt = time.time() - t0
             t += dt
             flops += 2.0 * r * w.shape[0] * a.shape[1]
-            done += r
+            done, calls, top = done + r, calls + 1, max(top, r)
             rows = max(8, int(r * max(1.0, (budget - t) / max(dt, 1e-3)) * 0.9))
-        return flops, t, done
+        return flops, t, f"{done} output rows in {calls} calls on its first {top} of {a.shape[0]} rows"
 
     per = seconds / len(gemms)
     tot_f, tot_t, parts = 0.0, 0.0, []
     for name, a, w in gemms:
         f, t, n = rate(lambda a_, w_, r: cpp.gemm_bf16_ref_rows(a_, w_, np.arange(r), threads), a, w, per)
         tot_f, tot_t = tot_f + f, tot_t + t
-        parts.append(f"{name}: {n} rows")
+        parts.append(f"{name}: {n}")
     # the same definition on one host thread (gate rows only)
     f1, t1, n1 = rate(lambda a_, w_, r: cpp.gemm_bf16_ref_rows(a_, w_, np.arange(r), 1), gemms[0][1], gemms[0][2],
                       min(per, 3.0))
     res = {"value": round(tot_f / tot_t / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-           "sample": f"C++ oracle orc_gemm_bf16_f64_rows (FP64, ascending k, {threads} threads) on leading rows "
-                     f"of the MLP step's GEMMs ({', '.join(parts)}; {tot_f / 1e9:.1f} GFLOP in {tot_t:.1f} s wall)"}
+           "sample": f"C++ oracle orc_gemm_bf16_f64_rows (FP64, ascending k, {threads} threads) on the "
+                     f"leading rows of the MLP step's GEMMs ({', '.join(parts)}; {tot_f / 1e9:.1f} GFLOP in {tot_t:.1f} s wall)"}
 
     res["one_thread"] = {"value": round(f1 / t1 / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
-                         "sample": f"{gemms[0][0]}: {n1} rows, {f1 / 1e9:.1f} GFLOP in {t1:.1f} s wall"}
+                         "sample": f"{gemms[0][0]}: {n1}, {f1 / 1e9:.1f} GFLOP in {t1:.1f} s wall"}
     blas = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
     nf, nt, nparts = 0.0, 0.0, []
     for name, a, w in gemms:
         f, t, n = rate(lambda a_, w_, r: oracle.gemm_bf16_ref(a_[:r], w_), a, w, min(per, 3.0))
         nf, nt = nf + f, nt + t
-        nparts.append(f"{name}: {n} rows")
+        nparts.append(f"{name}: {n}")
     res["numpy_oracle"] = {"value": round(nf / nt / 1e12, 4), "unit": "TFLOP/s", "cores": int(blas),
                            "sample": f"gemm_bf16_ref (decode + FP64 BLAS matmul) ({', '.join(nparts)}; "
                                      f"{nf / 1e9:.0f} GFLOP in {nt:.1f} s wall)"}
