@@ -1081,7 +1081,14 @@ gemm_mfma_direct_kernel(KParams p) {
     const int wm = wave / WN, wn = wave % WN;
 
     int tm, tn;
-    tile_of_block(p.tiles_m, p.tiles_n, tm, tn);
+    if constexpr (PREF) {
+        // The fold streams `out` once: in dispatch order, adjacent tiles run
+        // on different XCDs at the same time (7% faster on 2048 x 17408 than
+        // the XCD-contiguous order, which serves L2 reuse of the operands).
+        grouped_tile((int)blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+    } else {
+        tile_of_block(p.tiles_m, p.tiles_n, tm, tn);
+    }
     // the second problem of a dual launch: same A and shape, its own B and C
     // (uniform per workgroup)
     const uint16_t* Bop = p.B;
