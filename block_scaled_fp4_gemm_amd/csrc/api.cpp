@@ -7,6 +7,7 @@
 #include <cstring>
 
 #include "bg_internal.hpp"
+#include "tile_order.hpp"
 
 namespace {
 
@@ -68,6 +69,8 @@ bg_status check_device() {
 
 bg_status launched(hipError_t e) { return e == hipSuccess ? BG_OK : BG_ERR_LAUNCH; }
 
+std::atomic<int> g_tune[BG_TUNE_COUNT] = {{-1}, {-1}, {-1}, {-1}, {-1}, {-1}};
+
 // Common checks of a dense BF16 problem A[M,K], B[N,K] -> out[M,N] of
 // `out_elem` bytes per element.
 bg_status check_dense(const void* A, const void* B, const void* out, uint32_t M, uint32_t N,
@@ -108,7 +111,40 @@ bg_status check_fp4(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, cons
 
 }  // namespace
 
+namespace bg {
+int tune(int key) {
+    return key >= 0 && key < BG_TUNE_COUNT ? g_tune[key].load(std::memory_order_relaxed) : -1;
+}
+}  // namespace bg
+
 extern "C" {
+
+bg_status bg_tune_set(int key, int value) {
+    if (key < 0 || key >= BG_TUNE_COUNT || value < -1) return BG_ERR_SHAPE;
+    g_tune[key].store(value, std::memory_order_relaxed);
+    return BG_OK;
+}
+
+int bg_tune_get(int key) { return bg::tune(key); }
+
+bg_status bg_tile_map(int order, uint32_t tiles_m, uint32_t tiles_n, int32_t* tm, int32_t* tn) {
+    const uint64_t n = (uint64_t)tiles_m * tiles_n;
+    if (order < 0 || order > 2 || n >= (uint64_t(1) << 31)) return BG_ERR_SHAPE;
+    if (n == 0) return BG_OK;
+    if (tm == nullptr || tn == nullptr) return BG_ERR_NULL;
+    for (uint64_t b = 0; b < n; ++b) {
+        int r = 0, c = 0;
+        if (order == bg::ORDER_GEMM)
+            bg::tile_of<bg::ORDER_GEMM>((int)b, (int)tiles_m, (int)tiles_n, r, c);
+        else if (order == bg::ORDER_FOLD)
+            bg::tile_of<bg::ORDER_FOLD>((int)b, (int)tiles_m, (int)tiles_n, r, c);
+        else
+            bg::tile_of<bg::ORDER_ROWS>((int)b, (int)tiles_m, (int)tiles_n, r, c);
+        tm[b] = r;
+        tn[b] = c;
+    }
+    return BG_OK;
+}
 
 const char* bg_status_string(bg_status s) {
     switch (s) {
@@ -221,16 +257,18 @@ bg_status gemm_bf16_ordered(const uint16_t* A, const uint16_t* B, uint16_t* C, u
                             uint32_t N, uint32_t K, void* stream) {
     bg_status s = check_dense(A, B, C, M, N, K, 2);
     if (s != BG_OK || M == 0 || N == 0) return s;
-    if ((s = check_device()) != BG_OK) return s;
-    return launched(bg::launch_ordered(A, B, C, false, M, N, K, (hipStream_t)stream));
+    uint32_t cus = 0;
+    if ((s = check_device(&cus)) != BG_OK) return s;
+    return launched(bg::launch_ordered(A, B, C, false, M, N, K, cus, (hipStream_t)stream));
 }
 
 bg_status gemm_bf16_ordered_f32(const uint16_t* A, const uint16_t* B, float* C32, uint32_t M,
                                 uint32_t N, uint32_t K, void* stream) {
     bg_status s = check_dense(A, B, C32, M, N, K, 4);
     if (s != BG_OK || M == 0 || N == 0) return s;
-    if ((s = check_device()) != BG_OK) return s;
-    return launched(bg::launch_ordered(A, B, C32, true, M, N, K, (hipStream_t)stream));
+    uint32_t cus = 0;
+    if ((s = check_device(&cus)) != BG_OK) return s;
+    return launched(bg::launch_ordered(A, B, C32, true, M, N, K, cus, (hipStream_t)stream));
 }
 
 bg_status gemm_fp4_blockscaled(const uint8_t* A, const uint8_t* SFA, const uint8_t* B,

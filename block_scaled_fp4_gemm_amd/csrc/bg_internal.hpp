@@ -53,6 +53,9 @@ struct W4a16Problem {
     uint32_t cus;        // compute units of the current device (tile choice)
 };
 
+// Current tuning override of a bg_tune_key (-1: automatic choice).
+int tune(int key);
+
 // Kernel launchers (defined in the .hip files). They enqueue on `stream` and
 // return hipGetLastError() of the launch. Shapes are already validated and
 // non-empty (M > 0, N > 0).
@@ -65,7 +68,7 @@ hipError_t launch_scales_from_blocked(const uint8_t* src, uint8_t* dst, uint32_t
                                       uint32_t batch, hipStream_t stream);
 hipError_t launch_w4a16(const W4a16Problem& p, hipStream_t stream);
 hipError_t launch_ordered(const uint16_t* A, const uint16_t* B, void* C, bool f32_out,
-                          uint32_t M, uint32_t N, uint32_t K, hipStream_t stream);
+                          uint32_t M, uint32_t N, uint32_t K, uint32_t cus, hipStream_t stream);
 hipError_t launch_splitk_reduce(const float* ws, uint16_t* C, uint32_t M, uint32_t N,
                                 uint32_t splits, hipStream_t stream);
 hipError_t launch_scaled_add(uint16_t* out, const uint16_t* delta, size_t count, float scale,

@@ -26,10 +26,10 @@
 // dense_gemm_splitk's FP32 partial planes); kernelbot NVFP4 GEMM page
 // ("SCALE FACTORS": one E4M3 scale per 16 K elements multiplied into each
 // E2M1 element, then an FP32-accumulated dot product).
-#include <cstdlib>
 #include <type_traits>
 
 #include "bg_internal.hpp"
+#include "tile_order.hpp"
 
 #pragma clang fp contract(off)
 
@@ -47,11 +47,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BK = 64;       // K elements per pipeline step
-// tile-rows per group in the grouped order. With 32 CUs per XCD, 4 gives the
-// concurrent tiles of an XCD a 4 x 8 block (4 A panels, 8 B panels): measured
-// against 2, 3, 5, 6, 8 and 16 on the MLP and attention shapes, 4 ran the
-// gate+up dual call 1.6% and Q/O 5.4% faster than 8, other rows within 2%.
-constexpr int GROUP_M = 4;
 
 // Operand sources. A kernel's SRC names both operands: SRC_W4A16 is BF16 A
 // (SRC_BF16_VEC staging) with FP4 B dequantized to BF16 (SRC_FP4_BF16).
@@ -144,29 +139,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
-// Dispatch places workgroup b of an n-workgroup grid on XCD b % 8. The
-// returned logical id gives each XCD one contiguous range of ids.
-__device__ __forceinline__ int xcd_order(int b, int n) {
-    const int per = n >> 3, rem = n & 7;
-    const int x = b & 7, j = b >> 3;
-    return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + j;
-}
-
-// Logical tile id -> (tile_m, tile_n) in grouped order: GROUP_M tile-rows at
-// a time, m fastest, so tiles that run together share B columns in L2.
-__device__ __forceinline__ void grouped_tile(int logical, int tiles_m, int tiles_n, int& tm, int& tn) {
-    const int width = GROUP_M * tiles_n;
-    const int g = logical / width;
-    const int first_m = g * GROUP_M;
-    const int gsize = min(tiles_m - first_m, GROUP_M);
-    const int r = logical - g * width;
-    tm = first_m + r % gsize;
-    tn = r / gsize;
-}
-
 // One workgroup per tile: workgroup -> (tile_m, tile_n).
 __device__ __forceinline__ void tile_of_block(int tiles_m, int tiles_n, int& tm, int& tn) {
-    grouped_tile(xcd_order(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
+    tile_of<ORDER_GEMM>((int)blockIdx.x, tiles_m, tiles_n, tm, tn);
 }
 
 // ---------------------------------------------------------------------------
@@ -1085,7 +1060,7 @@ gemm_mfma_direct_kernel(KParams p) {
         // The fold streams `out` once: in dispatch order, adjacent tiles run
         // on different XCDs at the same time (7% faster on 2048 x 17408 than
         // the XCD-contiguous order, which serves L2 reuse of the operands).
-        grouped_tile((int)blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+        tile_of<ORDER_FOLD>((int)blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
     } else {
         tile_of_block(p.tiles_m, p.tiles_n, tm, tn);
     }
@@ -1170,14 +1145,6 @@ hipError_t launch_direct(const KParams& kp, int splits, hipStream_t stream) {
     hipLaunchKernelGGL((gemm_mfma_direct_kernel<BM, BN, BKS, WM, WN, STAGES, EPI, PREF>), grid,
                        dim3(WM * WN * 64), 0, stream, q);
     return hipGetLastError();
-}
-
-// Tuning hooks (environment): `BLOCKGEMM_TILE` forces one of the table
-// entries below for the whole problem; `BLOCKGEMM_SPLIT=0` turns the column
-// split off.
-int env_int(const char* name) {
-    const char* e = getenv(name);
-    return e ? atoi(e) : -1;
 }
 
 template <int EPI>
@@ -1324,10 +1291,10 @@ Schedule choose_schedule(int M, int N, int K, int splits, int cus, int epi) {
 
 template <int EPI>
 hipError_t launch_dense_vec(const KParams& kp, int splits, hipStream_t stream) {
-    const int forced = env_int("BLOCKGEMM_TILE");
+    const int forced = tune(BG_TUNE_TILE);
     if (forced >= 0) return launch_tile_cfg<EPI>(kp, splits, forced, stream);
     Schedule sch = choose_schedule(kp.M, kp.N, kp.K, splits, kp.cus, EPI);
-    if (env_int("BLOCKGEMM_SPLIT") == 0 && sch.n1 < kp.N) {
+    if (tune(BG_TUNE_COLSPLIT) == 0 && sch.n1 < kp.N) {
         double t;
         sch = {best_single(kp.M, kp.N, kp.K, splits, kp.cus, &t)->cfg, kp.N, 0};
     }
@@ -1397,7 +1364,7 @@ hipError_t launch_dense(const DenseProblem& p, Epilogue epi, hipStream_t stream)
 // register-staged tile) run as two ordinary launches.
 hipError_t launch_dense_dual(const DenseProblem& p, const uint16_t* B1, uint16_t* C1, hipStream_t stream) {
     const bool vec = (p.K % 8) == 0 && (int64_t)p.K * 640 < (int64_t(1) << 31);
-    const int forced = env_int("BLOCKGEMM_TILE");
+    const int forced = tune(BG_TUNE_TILE);
     if (!vec || forced == 0) {
         hipError_t e = launch_dense(p, EPI_STORE_BF16, stream);
         if (e != hipSuccess) return e;
@@ -1432,8 +1399,8 @@ hipError_t launch_dense_dual(const DenseProblem& p, const uint16_t* B1, uint16_t
     return launch_tile_cfg<EPI_STORE_BF16>(kp, 1, cfg, stream);
 }
 
-// W4A16 tile choices (register-staged kernel; BLOCKGEMM_W4A16_TILE, a tuning
-// hook, forces one). The estimate is rounds x blocks per CU x tile area /
+// W4A16 tile choices (register-staged kernel; the BG_TUNE_W4A16_TILE override
+// forces one). The estimate is rounds x blocks per CU x tile area /
 // measured rate, as for the BF16 tiles.
 struct W4a16Choice {
     int cfg, bm, bn, occ;
@@ -1463,13 +1430,13 @@ int choose_w4a16(int M, int N, int cus) {
     return best;
 }
 
-// FP4 tile choices (BLOCKGEMM_FP4_TILE and BLOCKGEMM_FP4_SK_TILE, tuning
-// hooks, force one when `tuned`).
+// FP4 tile choices (the BG_TUNE_FP4_TILE and BG_TUNE_FP4_SPLITK_TILE
+// overrides force one when `tuned`).
 template <int SRC>
 hipError_t launch_fp4_src(const KParams& kp, int M, int splits, int batch, bool tuned, hipStream_t stream) {
     // FP32 planes (split-K) for the small-M decode shapes
     if (splits > 1) {
-        int sk = tuned ? env_int("BLOCKGEMM_FP4_SK_TILE") : -1;
+        int sk = tuned ? tune(BG_TUNE_FP4_SPLITK_TILE) : -1;
         if (sk < 0) sk = M <= 192 ? 3 : 2;
         if constexpr (SRC == SRC_FP4W) {
             switch (sk) {
@@ -1484,7 +1451,7 @@ hipError_t launch_fp4_src(const KParams& kp, int M, int splits, int batch, bool 
         if (sk == 3) return launch_cfg<128, 256, 2, 4, EPI_STORE_F32, SRC, 2>(kp, splits, stream);
         return launch_cfg<256, 256, 2, 4, EPI_STORE_F32, SRC, 1>(kp, splits, stream);
     }
-    int cfg = tuned ? env_int("BLOCKGEMM_FP4_TILE") : -1;
+    int cfg = tuned ? tune(BG_TUNE_FP4_TILE) : -1;
     // 256 x 256 tiles with two register sets where the 32-element units
     // leave room for them (3% ahead of one set on 4096 x 4096 x 8192)
     if (cfg < 0) cfg = M <= 192 ? 2 : SRC == SRC_FP4W ? 1 : 0;
@@ -1575,7 +1542,7 @@ hipError_t launch_w4a16(const W4a16Problem& p, hipStream_t stream) {
     kp.ldc = (int)p.N;
     kp.k_chunk = (int)p.K;
     kp.scale = p.scale_2;
-    int cfg = env_int("BLOCKGEMM_W4A16_TILE");
+    int cfg = tune(BG_TUNE_W4A16_TILE);
     if (cfg < 0) cfg = choose_w4a16(kp.M, kp.N, p.cus > 0 ? (int)p.cus : 256);
     // 32-element weight units when no unit can straddle the end of K; the
     // 16-element units (K % 32 == 16) take the 256 x 256 tile

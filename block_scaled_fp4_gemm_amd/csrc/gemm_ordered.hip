@@ -16,9 +16,9 @@
 // row-major with a padded pitch. The per-output k order is untouched by the
 // tiling: tiles are visited in ascending k and, inside a tile, k ascends.
 #include <cmath>
-#include <cstdlib>
 
 #include "bg_internal.hpp"
+#include "tile_order.hpp"
 
 #pragma clang fp contract(off)
 
@@ -95,9 +95,8 @@ gemm_ordered_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__
     // Dispatch places workgroup b on XCD b % 8; renumbered so each XCD holds
     // one contiguous range of tiles, the column tiles of a row block (which
     // share its A rows) run on the same XCD and hit in its L2.
-    const int nb = gridDim.x, per = nb >> 3, rem = nb & 7, x = blockIdx.x & 7, j = blockIdx.x >> 3;
-    const int logical = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + j;
-    const int tm = logical / tiles_n, tn = logical % tiles_n;
+    int tm, tn;
+    tile_of<ORDER_ROWS>((int)blockIdx.x, (int)gridDim.x / tiles_n, tiles_n, tm, tn);
     const int m0 = tm * TM, n0 = tn * TN;
     const bool vec = (K & 7) == 0;
 
@@ -249,16 +248,9 @@ hipError_t run_ordered(const uint16_t* A, const uint16_t* B, void* C, bool f32_o
 }  // namespace
 
 hipError_t launch_ordered(const uint16_t* A, const uint16_t* B, void* C, bool f32_out, uint32_t M,
-                          uint32_t N, uint32_t K, hipStream_t stream) {
-    int simds = 1024;
-    int dev = 0;
-    if (hipGetDevice(&dev) == hipSuccess) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
-            simds = 4 * cus;
-    }
-    const char* e = getenv("BLOCKGEMM_ORD_TILE");   // tuning only: index into kOrdChoices
-    int pick = e ? atoi(e) : -1;
+                          uint32_t N, uint32_t K, uint32_t cus, hipStream_t stream) {
+    const int simds = 4 * (cus > 0 ? (int)cus : 256);
+    int pick = tune(BG_TUNE_ORDERED);   // forced register-block variant, or -1
     if (pick < 0 || pick >= (int)(sizeof(kOrdChoices) / sizeof(kOrdChoices[0]))) {
         double best = -1.0;
         for (int c = 0; c < (int)(sizeof(kOrdChoices) / sizeof(kOrdChoices[0])); ++c) {

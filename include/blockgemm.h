@@ -290,6 +290,59 @@ bg_status bf16_scaled_add(uint16_t* out, const uint16_t* delta, size_t count,
 /* Static, NUL-terminated description of a status code. */
 const char* bg_status_string(bg_status status);
 
+/*
+ * Tuning overrides: each key names one automatic choice the library makes
+ * per call. bg_tune_set(key, v) with v >= 0 forces that choice for every
+ * later call in the process (any device, any thread); v = -1, the initial
+ * state, restores the automatic choice. Nothing is read from the
+ * environment. Meant for tests that must cover every tile configuration and
+ * for tile sweeps; a forced choice changes speed only, never the promised
+ * result (bit-identical where an entry point promises it, within the FP32
+ * summation-order tolerance otherwise).
+ *
+ *  BG_TUNE_TILE:       dense tile configuration (gemm_bf16 and the entry
+ *                      points built on it: dual, strided, scaled_acc,
+ *                      split-K planes), an index into the library's tile table
+ *  BG_TUNE_COLSPLIT:   0 turns the column split of gemm_bf16 off
+ *  BG_TUNE_ORDERED:    register-block variant of gemm_bf16_ordered
+ *  BG_TUNE_FP4_TILE:   tile of gemm_fp4_blockscaled(_batched)
+ *  BG_TUNE_FP4_SPLITK_TILE: tile of gemm_fp4_blockscaled_splitk's planes
+ *  BG_TUNE_W4A16_TILE: tile of gemm_w4a16
+ * Returns BG_ERR_SHAPE for an unknown key or v < -1; an index past a table
+ * selects that table's default entry.
+ */
+typedef enum bg_tune_key {
+    BG_TUNE_TILE = 0,
+    BG_TUNE_COLSPLIT = 1,
+    BG_TUNE_ORDERED = 2,
+    BG_TUNE_FP4_TILE = 3,
+    BG_TUNE_FP4_SPLITK_TILE = 4,
+    BG_TUNE_W4A16_TILE = 5,
+    BG_TUNE_COUNT = 6
+} bg_tune_key;
+
+bg_status bg_tune_set(int key, int value);
+
+/* The current override of `key` (-1: automatic; also -1 for an unknown key). */
+int bg_tune_get(int key);
+
+/*
+ * bg_tile_map: the workgroup -> output tile mapping of the GEMM kernels,
+ * evaluated on the host by the same code the kernels run (no device needed).
+ * For every workgroup b of a tiles_m x tiles_n grid it writes the tile row
+ * tm[b] and tile column tn[b]; each mapping is a bijection onto the grid.
+ *
+ *  order 0: the GEMM kernels (the sm121a_matmul.py page's grouped program
+ *           order, 4 tile-rows per group, applied to ids renumbered so each
+ *           of the 8 XCDs holds one contiguous range);
+ *  order 1: the LoRA fold (grouped order on the raw dispatch index);
+ *  order 2: the order-preserving kernel (XCD-contiguous ids, row-major).
+ *  tm, tn: host arrays of tiles_m * tiles_n int32 each.
+ * BG_ERR_SHAPE for another order or tiles_m * tiles_n >= 2^31; BG_ERR_NULL
+ * for a NULL array of a non-empty grid.
+ */
+bg_status bg_tile_map(int order, uint32_t tiles_m, uint32_t tiles_n, int32_t* tm, int32_t* tn);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,6 @@ from .codecs import (  # noqa: F401
     unpack_e2m1,
 )
 from .gemm import (  # noqa: F401
-    bf16_in_closed_range,
     gemm_bf16_ref,
     gemm_fp4_ref,
     gemm_fp4_splitk_planes_ref,
@@ -37,7 +36,8 @@ from .gemm import (  # noqa: F401
     gemm_w4a16_exact,
     gemm_w4a16_ref,
     rms,
-    scaled_acc_candidates,
+    scaled_acc_admissible,
+    scaled_acc_candidate_deltas,
     scaled_acc_epilogue,
     splitk_chunk,
     splitk_reduce,

@@ -40,7 +40,9 @@ def gemm_bf16_ref(a_bits, b_bits) -> np.ndarray:
 
 
 def rms(values_f64) -> float:
-    """Root mean square of a decoded input tensor (0 for an empty one)."""
+    """Root mean square sqrt(mean(v^2)) of a decoded input tensor, in FP64
+    (0 for an empty one): the sigma_A, sigma_B of the tolerance below, taken
+    from the stored values rather than the nominal standard deviation."""
     v = np.asarray(values_f64, dtype=np.float64)
     return float(np.sqrt(np.mean(v * v))) if v.size else 0.0
 
@@ -108,27 +110,18 @@ def gemm_scaled_acc_exact(out_bits, x_bits, b_bits, scale) -> np.ndarray:
     return scaled_acc_epilogue(out_bits, f32_to_bf16(delta), scale)
 
 
-def scaled_acc_candidates(out_bits, x_bits, b_bits, scale, depth_factor: float = 2.0):
-    """All BF16 outputs a correct fused fold may produce, given unknown FP32 order.
+def _f32_ceil(x) -> np.ndarray:
+    """Smallest FP32 value >= x (elementwise, x finite FP64)."""
+    x = np.asarray(x, dtype=np.float64)
+    f = x.astype(np.float32)
+    return np.where(f.astype(np.float64) < x, np.nextafter(f, np.float32(np.inf)), f).astype(np.float32)
 
-    The FP32 accumulator of a K-term dot product lies within
-    Bd = depth_factor * K * 2^-24 * sum|x*b| of the exact sum. Every BF16 value
-    bf16(d32) reachable from that interval is a candidate delta; the epilogue is
-    applied to each. Returns (lo_out, hi_out, n_candidates) where lo/hi are the
-    outputs at the smallest and largest candidate delta and n_candidates counts
-    the distinct BF16 deltas (1 where the rounding is unambiguous).
-    """
-    x = bf16_to_f64(x_bits)
-    b = bf16_to_f64(b_bits)
-    k = x.shape[1]
-    exact = x @ b.T
-    bound = depth_factor * k * 2.0 ** -24 * (np.abs(x) @ np.abs(b).T)
-    lo_d = f32_to_bf16((exact - bound).astype(np.float32))
-    hi_d = f32_to_bf16((exact + bound).astype(np.float32))
-    lo_o = scaled_acc_epilogue(out_bits, lo_d, scale)
-    hi_o = scaled_acc_epilogue(out_bits, hi_d, scale)
-    n_cand = _bf16_steps_between(lo_d, hi_d) + 1
-    return lo_o, hi_o, n_cand
+
+def _f32_floor(x) -> np.ndarray:
+    """Largest FP32 value <= x (elementwise, x finite FP64)."""
+    x = np.asarray(x, dtype=np.float64)
+    f = x.astype(np.float32)
+    return np.where(f.astype(np.float64) > x, np.nextafter(f, np.float32(-np.inf)), f).astype(np.float32)
 
 
 def _bf16_order_key(bits) -> np.ndarray:
@@ -137,14 +130,71 @@ def _bf16_order_key(bits) -> np.ndarray:
     return np.where(u & 0x8000, -(u & 0x7FFF), u)
 
 
-def _bf16_steps_between(lo_bits, hi_bits) -> np.ndarray:
-    return np.abs(_bf16_order_key(hi_bits) - _bf16_order_key(lo_bits))
+def _bf16_from_key(key) -> np.ndarray:
+    """Inverse of _bf16_order_key (key 0 gives +0)."""
+    k = np.asarray(key, dtype=np.int64)
+    return np.where(k < 0, 0x8000 | (-k), k).astype(np.uint16)
 
 
-def bf16_in_closed_range(v_bits, lo_bits, hi_bits) -> np.ndarray:
-    """v lies between lo and hi (inclusive) in BF16 value order."""
-    kv, kl, kh = _bf16_order_key(v_bits), _bf16_order_key(lo_bits), _bf16_order_key(hi_bits)
-    return (kv >= np.minimum(kl, kh)) & (kv <= np.maximum(kl, kh))
+def scaled_acc_candidate_deltas(x_bits, b_bits, depth_factor: float = 2.0):
+    """The BF16 deltas a correct FP32 accumulation of X * B^T may round to.
+
+    The MFMA summation order is not specified, so the FP32 accumulator of a
+    K-term dot product is only known to lie within
+        Bd = depth_factor * K * 2^-24 * sum_k |x_k * b_k|
+    of the exact sum (the classical bound for recursive summation with unit
+    roundoff 2^-24 is (K-1) * 2^-24 * sum|x*b| to first order; depth_factor = 2
+    doubles it to cover accumulators that truncate). The reachable FP32 values
+    are those in [exact - Bd, exact + Bd]; BF16 rounding is monotone and moves
+    at most one BF16 step between adjacent FP32 values, so the candidate
+    deltas are every BF16 value from bf16(lowest reachable) to
+    bf16(highest reachable).
+
+    Returns (lo_bits, hi_bits, n_candidates): the extreme candidate deltas as
+    BF16 bits and the number of distinct candidate values (1 where the
+    rounding is unambiguous).
+    """
+    x = bf16_to_f64(x_bits)
+    b = bf16_to_f64(b_bits)
+    k = x.shape[1]
+    exact = x @ b.T
+    bound = depth_factor * k * 2.0 ** -24 * (np.abs(x) @ np.abs(b).T)
+    lo_d = f32_to_bf16(_f32_ceil(exact - bound))
+    hi_d = f32_to_bf16(_f32_floor(exact + bound))
+    n_cand = _bf16_order_key(hi_d) - _bf16_order_key(lo_d) + 1
+    return lo_d, hi_d, n_cand
+
+
+def scaled_acc_admissible(got_bits, out_bits, x_bits, b_bits, scale, depth_factor: float = 2.0):
+    """Which fused-fold outputs equal the epilogue at one candidate delta.
+
+    For each element, got is admissible when
+        got == scaled_acc_epilogue(out, d, scale)
+    for some d among scaled_acc_candidate_deltas (both zeros are tried where
+    the candidates include zero). Every candidate is enumerated: the output
+    must be exactly one candidate's result, not merely lie between the
+    extreme candidates' results. Returns (ok_mask, n_candidates).
+    """
+    got = np.asarray(got_bits, dtype=np.uint16)
+    out = np.asarray(out_bits, dtype=np.uint16)
+    lo_d, hi_d, n_cand = scaled_acc_candidate_deltas(x_bits, b_bits, depth_factor)
+    lo_key = _bf16_order_key(lo_d)
+    ok = np.zeros(got.shape, dtype=bool)
+    idx = np.arange(got.size)
+    flat_n = n_cand.reshape(-1)
+    c = 0
+    while idx.size:
+        d = _bf16_from_key(lo_key.reshape(-1)[idx] + c)
+        o = out.reshape(-1)[idx]
+        hit = scaled_acc_epilogue(o, d, scale) == got.reshape(-1)[idx]
+        zero = d == 0
+        if zero.any():   # -0 as well as +0
+            neg = scaled_acc_epilogue(o[zero], np.full(int(zero.sum()), 0x8000, np.uint16), scale)
+            hit[zero] |= neg == got.reshape(-1)[idx][zero]
+        ok.reshape(-1)[idx[hit]] = True
+        c += 1
+        idx = idx[~hit & (flat_n[idx] > c)]
+    return ok, n_cand
 
 
 # ---------------------------------------------------------------------------

@@ -83,19 +83,13 @@ def e4m3_choice(rows: int, groups: int, choices, seed: int, tensor_id: int) -> n
 
 
 def sample_rows(m: int, count: int, seed: int) -> np.ndarray:
-    """Sorted distinct row indices: always 0 and m-1, the rest seeded uniform."""
+    """Sorted distinct row indices: always 0 and m-1, and count-2 more drawn
+    uniformly without replacement from 1..m-2 (all rows when m <= count)."""
     if m <= count:
         return np.arange(m, dtype=np.int64)
     g = _rng(seed, 99)
-    picked = set([0, m - 1])
-    while len(picked) < count:
-        picked.update(int(v) for v in g.integers(0, m, size=count))
-    out = np.array(sorted(picked), dtype=np.int64)
-    # keep 0 and m-1, trim the middle deterministically
-    if len(out) > count:
-        mid = out[1:-1][: count - 2]
-        out = np.concatenate([[0], mid, [m - 1]])
-    return out
+    mid = g.choice(np.arange(1, m - 1, dtype=np.int64), size=count - 2, replace=False)
+    return np.concatenate([[0], np.sort(mid), [m - 1]]).astype(np.int64)
 
 
 # ---------------------------------------------------------------------------

@@ -4,7 +4,7 @@ When the last round of 256x256 tiles would be poorly filled, gemm_bf16 runs
 the first n1 columns as whole rounds of 256x256 tiles and the remaining
 columns as a second launch with a smaller tile, writing into the same C
 (row stride N). Each output is still one tile's FP32 sum over K in the same
-order, so the split result must equal the unsplit one (BLOCKGEMM_SPLIT=0, a
+order, so the split result must equal the unsplit one (the BG_TUNE_COLSPLIT override set to 0, a
 tuning hook) bit for bit, and the oracle within the GEMM tolerance.
 
 With 256 CUs the shapes below split as noted (first part, second tile).
@@ -30,22 +30,22 @@ SPLIT_SHAPES = [
 ]
 
 
-def _both(a_bits, b_bits, monkeypatch):
+def _both(a_bits, b_bits, force):
     da, db = to_dev_bf16(a_bits), to_dev_bf16(b_bits)
     split = bits_of(bg.gemm_bf16(da, db))
-    monkeypatch.setenv("BLOCKGEMM_SPLIT", "0")
+    force(bg.TUNE_COLSPLIT, 0)
     whole = bits_of(bg.gemm_bf16(da, db))
-    monkeypatch.delenv("BLOCKGEMM_SPLIT")
+    force(bg.TUNE_COLSPLIT, -1)
     torch.cuda.synchronize()
     return split, whole
 
 
 @pytest.mark.parametrize("m,n,k", SPLIT_SHAPES)
-def test_column_split_equals_unsplit_bitwise(m, n, k, monkeypatch):
+def test_column_split_equals_unsplit_bitwise(m, n, k, force):
     print(f"column split m={m} n={n} k={k}", flush=True)
     a = synthetic.normal_bf16((m, k), 1.0, 70, 0)
     b = synthetic.normal_bf16((n, k), 0.05, 70, 1)
-    split, whole = _both(a, b, monkeypatch)
+    split, whole = _both(a, b, force)
     assert_bits_equal(split, whole, f"split vs unsplit {m}x{n}x{k}")
     rows = synthetic.sample_rows(m, min(m, 256), 1020)
     check_close(split[rows], oracle.gemm_bf16_ref(a[rows], b), k, oracle.rms(oracle.bf16_to_f64(a)),

@@ -98,14 +98,14 @@ def test_mlp_gate_up_sampled_rows_and_determinism():
     _sampled_check(a, b, g1, 2, "gate/up")
 
 
-# every entry of the tile table (BLOCKGEMM_TILE forces one; a tuning hook)
+# every entry of the tile table (the BG_TUNE_TILE override forces one)
 TILE_CFGS = list(range(0, 24))
 CFG_SHAPES = [(1, 1, 8), (65, 129, 72), (161, 257, 136), (257, 225, 1000), (320, 448, 520), (33, 70, 64)]
 
 
 @pytest.mark.parametrize("cfg", TILE_CFGS)
-def test_every_tile_config_edge_shapes(cfg, monkeypatch):
-    monkeypatch.setenv("BLOCKGEMM_TILE", str(cfg))
+def test_every_tile_config_edge_shapes(cfg, force):
+    force(bg.TUNE_TILE, cfg)
     for m, n, k in CFG_SHAPES:
         a = synthetic.normal_bf16((m, k), 1.0, 3000 + m, 0)
         b = synthetic.normal_bf16((n, k), 0.5, 3000 + n, 1)

@@ -51,8 +51,8 @@ def test_dual_matches_oracle_and_single_calls(m, n, k):
 # tuning hook (0 is the register-staged tile: the dual call then runs two
 # ordinary launches)
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 6, 8, 9, 10, 12, 14, 23])
-def test_dual_every_tile_config(cfg, monkeypatch):
-    monkeypatch.setenv("BLOCKGEMM_TILE", str(cfg))
+def test_dual_every_tile_config(cfg, force):
+    force(bg.TUNE_TILE, cfg)
     for m, n, k in [(65, 257, 136), (257, 300, 520), (33, 70, 64)]:
         _check(*_inputs(m, n, k, 5000 + cfg), f"cfg {cfg} dual {m}x{n}x{k}")
 

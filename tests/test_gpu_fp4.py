@@ -76,9 +76,9 @@ FP4_TILE_SHAPES = [(1, 1, 16), (65, 129, 48), (257, 255, 1040), (300, 520, 208),
 
 
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 5, 6, 7, 8, 9])
-def test_every_fp4_tile_config(cfg, monkeypatch):
-    """Each FP4 tile variant (BLOCKGEMM_FP4_TILE, a tuning hook) on ragged shapes."""
-    monkeypatch.setenv("BLOCKGEMM_FP4_TILE", str(cfg))
+def test_every_fp4_tile_config(cfg, force):
+    """Each FP4 tile variant (the BG_TUNE_FP4_TILE override) on ragged shapes."""
+    force(bg.TUNE_FP4_TILE, cfg)
     for m, n, k in FP4_TILE_SHAPES:
         a, b = synthetic.fp4_packed(m, k, 70 + cfg, 0), synthetic.fp4_packed(n, k, 70 + cfg, 1)
         sfa = synthetic.e4m3_uniform(m, k // 16, 2 ** -4, 2 ** 4, 70, 4)
@@ -207,10 +207,10 @@ def test_gemm_on_imported_scales_equals_plain_scales():
 
 
 @pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6])
-def test_every_fp4_splitk_tile(tile, monkeypatch):
-    """Each FP4 split-K tile (BLOCKGEMM_FP4_SK_TILE, a tuning hook): planes
+def test_every_fp4_splitk_tile(tile, force):
+    """Each FP4 split-K tile (the BG_TUNE_FP4_SPLITK_TILE override): planes
     summed in order equal the exact result on power-of-two scales."""
-    monkeypatch.setenv("BLOCKGEMM_FP4_SK_TILE", str(tile))
+    force(bg.TUNE_FP4_SPLITK_TILE, tile)
     for m, n, k, ks in [(128, 384, 4096, 8), (65, 129, 1040, 3), (300, 520, 2048, 5), (65, 129, 1056, 3)]:
         a, b = synthetic.fp4_packed(m, k, 150 + tile, 0), synthetic.fp4_packed(n, k, 150 + tile, 1)
         sfa = synthetic.e4m3_choice(m, k // 16, [0x38, 0x40], 150, 4)

@@ -64,9 +64,9 @@ FP4_TILE_SHAPES = [(1, 1, 16), (65, 129, 48), (257, 255, 1040), (300, 520, 208),
 
 
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 6, 7, 9])
-def test_every_w4a16_tile_config(cfg, monkeypatch):
-    """Each W4A16 tile variant (BLOCKGEMM_W4A16_TILE, a tuning hook) on ragged shapes."""
-    monkeypatch.setenv("BLOCKGEMM_W4A16_TILE", str(cfg))
+def test_every_w4a16_tile_config(cfg, force):
+    """Each W4A16 tile variant (the BG_TUNE_W4A16_TILE override) on ragged shapes."""
+    force(bg.TUNE_W4A16_TILE, cfg)
     for m, n, k in FP4_TILE_SHAPES:
         a = synthetic.normal_bf16((m, k), 1.0, 110 + cfg, 0)
         b = synthetic.fp4_packed(n, k, 110 + cfg, 1)

@@ -224,15 +224,105 @@ def test_scaled_acc_scale_zero_keeps_values_and_unit_rows_add():
             assert got[i, j] == want
 
 
-def test_scaled_acc_candidates_bracket_exact_result():
+def _bits_of_values(vals):
+    return torch_bf16_bits(np.asarray(vals, np.float32)[None, :])
+
+
+def test_candidate_deltas_one_when_far_from_a_rounding_midpoint():
+    # exact delta 1.5 (a BF16 value), bound 4 * 2^-24 * 1.5: one candidate
+    lo, hi, n = oracle.scaled_acc_candidate_deltas(_bits_of_values([1.0, 0.0]), _bits_of_values([1.5, 0.0]))
+    assert int(n[0, 0]) == 1 and int(lo[0, 0]) == int(hi[0, 0]) == 0x3FC0
+
+
+def test_candidate_deltas_exactly_two_at_a_midpoint():
+    # exact delta 1 + 2^-8 lies halfway between the BF16 values 1.0 (0x3F80)
+    # and 1 + 2^-7 (0x3F81): any nonzero error bound admits both, and a bound
+    # of a few FP32 ulps admits nothing else
+    lo, hi, n = oracle.scaled_acc_candidate_deltas(_bits_of_values([1.0, 2.0 ** -8]), _bits_of_values([1.0, 1.0]))
+    assert (int(lo[0, 0]), int(hi[0, 0]), int(n[0, 0])) == (0x3F80, 0x3F81, 2)
+
+
+def test_candidate_bound_size_pinned_from_both_sides():
+    """K = 3, sum|x*b| = 1 + 2^-8 + e, so Bd = 2 * 3 * 2^-24 * (1 + 2^-8 + e)
+    = 3.58e-7 (to 3 digits). The exact delta is the midpoint 1 + 2^-8 plus e:
+    e = 2^-23 (1.19e-7, inside Bd) keeps the midpoint reachable (two
+    candidates); e = 2^-21 (4.77e-7, outside Bd) does not (one candidate,
+    0x3F81). A bound too small by 3x or too large by 1.4x fails one case."""
+    b = _bits_of_values([1.0, 1.0, 1.0])
+    _, _, n_in = oracle.scaled_acc_candidate_deltas(_bits_of_values([1.0, 2.0 ** -8, 2.0 ** -23]), b)
+    lo, hi, n_out = oracle.scaled_acc_candidate_deltas(_bits_of_values([1.0, 2.0 ** -8, 2.0 ** -21]), b)
+    assert int(n_in[0, 0]) == 2
+    assert int(n_out[0, 0]) == 1 and int(lo[0, 0]) == 0x3F81
+    # the same exact delta with a bound of 1/3 or 1.4x the default
+    _, _, n_small = oracle.scaled_acc_candidate_deltas(_bits_of_values([1.0, 2.0 ** -8, 2.0 ** -23]), b,
+                                                       depth_factor=2.0 / 3.5)
+    _, _, n_big = oracle.scaled_acc_candidate_deltas(_bits_of_values([1.0, 2.0 ** -8, 2.0 ** -21]), b,
+                                                     depth_factor=2.0 * 1.4)
+    assert int(n_small[0, 0]) == 1 and int(n_big[0, 0]) == 2
+
+
+def test_admissible_requires_a_candidate_output_not_the_range():
+    """Candidates delta in {1.0, 1 + 2^-7}, out = 0, scale 3: the outputs are
+    bf16(3.0) = 0x4040 and bf16(3.0234375) = 0x4042 (a tie rounded to even).
+    0x4041 lies between them but no candidate produces it."""
+    x, b = _bits_of_values([1.0, 2.0 ** -8]), _bits_of_values([1.0, 1.0])
+    out = np.zeros((1, 1), np.uint16)
+    for got, want in ((0x4040, True), (0x4041, False), (0x4042, True), (0x403F, False), (0x4043, False)):
+        ok, n = oracle.scaled_acc_admissible(np.array([[got]], np.uint16), out, x, b, 3.0)
+        assert bool(ok[0, 0]) == want, hex(got)
+        assert int(n[0, 0]) == 2
+
+
+def test_admissible_accepts_the_exact_result_and_rejects_neighbours():
     out = rand_bf16((8, 32), 60)
     x = synthetic.normal_bf16((8, 64), 0.1, 61, 0)
     b = synthetic.normal_bf16((32, 64), 0.1, 61, 1)
-    lo, hi, n = oracle.scaled_acc_candidates(out, x, b, 2.0)
     exact = oracle.scaled_acc_epilogue(out, oracle.f32_to_bf16(oracle.gemm_bf16_ref(x, b).astype(np.float32)), 2.0)
-    assert oracle.bf16_in_closed_range(exact, lo, hi).all()
+    ok, n = oracle.scaled_acc_admissible(exact, out, x, b, 2.0)
+    assert ok.all()
     # near-zero deltas may admit several BF16 values; most admit exactly one
     assert (n >= 1).all() and (n == 1).mean() > 0.8
+    # one BF16 step away from the exact output is rejected wherever only one
+    # candidate exists and the output is not zero
+    one = (n == 1) & ((exact & 0x7FFF) != 0)
+    ok_up, _ = oracle.scaled_acc_admissible((exact + 1).astype(np.uint16), out, x, b, 2.0)
+    assert not ok_up[one].any()
+
+
+def test_admissible_zero_delta_tries_both_signs():
+    # out = -0, delta = exactly zero: -0 + 2*(+0) = +0 and -0 + 2*(-0) = -0 are both admissible
+    x, b = _bits_of_values([0.0]), _bits_of_values([1.0])
+    out = np.array([[0x8000]], np.uint16)
+    for got in (0x0000, 0x8000):
+        ok, _ = oracle.scaled_acc_admissible(np.array([[got]], np.uint16), out, x, b, 2.0)
+        assert ok[0, 0]
+
+
+# ---------------------------------------------------------------------------
+# RMS (the sigma of the tolerance)
+# ---------------------------------------------------------------------------
+
+def test_rms_closed_forms():
+    assert oracle.rms(np.array([3.0, 4.0])) == np.sqrt(12.5)
+    assert oracle.rms(np.array([[1.0, -1.0], [-1.0, 1.0]])) == 1.0
+    assert oracle.rms(np.full((7, 3), -0.25)) == 0.25
+    assert oracle.rms(np.zeros((0, 5))) == 0.0
+    # sqrt(mean): one large value among n zeros gives |v| / sqrt(n)
+    v = np.zeros(16)
+    v[5] = 8.0
+    assert oracle.rms(v) == 2.0
+
+
+def test_rms_of_the_config_weights_matches_their_standard_deviation():
+    """N(0, 0.02) weights of the Q/O projection, 2048 x 2048 draws: the RMS of
+    the stored BF16 values is 0.02 up to sampling error (relative standard
+    error 1/sqrt(2n) = 3.5e-4) and BF16 rounding (relative 2^-9 per value,
+    zero-mean)."""
+    _, w = synthetic.attn_proj(n=2048)
+    r = oracle.rms(oracle.bf16_to_f64(w))
+    assert abs(r / 0.02 - 1.0) < 2e-3
+    a, _ = synthetic.mlp_gate_up(m=256)
+    assert abs(oracle.rms(oracle.bf16_to_f64(a)) - 1.0) < 5e-3
 
 
 # ---------------------------------------------------------------------------
