@@ -29,16 +29,33 @@ def empty_bf16(m, n, fill_bits=None):
 
 
 def check_close(got_bits: np.ndarray, ref: np.ndarray, k: int, sig_a: float, sig_b: float, what=""):
-    """|c - ref| <= 8e-3*|ref| + 4e-3*sqrt(K)*sA*sB element by element."""
+    """|c - ref| <= 8e-3*|ref| + 4e-3*sqrt(K)*sA*sB element by element where
+    ref is finite; where ref is NaN the output must be NaN, and where ref is
+    +-Inf the output must be the same infinity."""
     got = oracle.bf16_to_f64(got_bits)
-    tol = oracle.tolerance(ref, k, sig_a, sig_b)
+    ref = np.asarray(ref, dtype=np.float64)
+    fin = np.isfinite(ref)
+    tol = oracle.tolerance(np.where(fin, ref, 0.0), k, sig_a, sig_b)
     err = np.abs(got - ref)
-    bad = ~(err <= tol)
+    bad = np.where(fin, ~(err <= tol), ~((np.isnan(ref) & np.isnan(got)) | (got == ref)))
     if bad.any():
         idx = np.argwhere(bad)[:5]
         detail = ", ".join(f"{tuple(i)}: got {got[tuple(i)]!r} ref {ref[tuple(i)]!r}" for i in idx)
         raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; {detail}")
-    return float((err / np.maximum(tol, 1e-300)).max()) if err.size else 0.0
+    e = np.where(fin, err / np.maximum(tol, 1e-300), 0.0)
+    return float(e.max()) if e.size else 0.0
+
+
+def assert_values_equal(got_bits: np.ndarray, want_bits: np.ndarray, what=""):
+    """BF16 outputs equal as values: NaN matches any NaN, -0 matches +0;
+    everything else bit for bit."""
+    g = oracle.bf16_to_f64(got_bits)
+    w = oracle.bf16_to_f64(want_bits)
+    same = (np.isnan(g) & np.isnan(w)) | (g == w)
+    if not same.all():
+        i = tuple(np.argwhere(~same)[0])
+        raise AssertionError(f"{what}: {int((~same).sum())} of {same.size} differ; first at {i}: "
+                             f"got {int(got_bits[i]):#x} want {int(want_bits[i]):#x}")
 
 
 def assert_bits_equal(got: np.ndarray, want: np.ndarray, what=""):
