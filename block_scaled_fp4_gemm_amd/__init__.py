@@ -33,6 +33,7 @@ _SIGS = {
     "gemm_bf16_dual": [_p, _p, _p, _p, _p, _u32, _u32, _u32, _p],
     "gemm_bf16_scaled_acc": [_p, _p, _p, _u32, _u32, _u32, _f32, _p],
     "gemm_bf16_splitk": [_p, _p, _p, _p, _sz, _u32, _u32, _u32, _u32, _p],
+    "gemm_bf16_splitk_noalloc": [_p, _p, _p, _u32, _u32, _u32, _u32, _p],
     "gemm_bf16_ordered": [_p, _p, _p, _u32, _u32, _u32, _p],
     "gemm_bf16_ordered_f32": [_p, _p, _p, _u32, _u32, _u32, _p],
     "gemm_fp4_blockscaled": [_p, _p, _p, _p, _p, _u32, _u32, _u32, _p],
@@ -272,6 +273,26 @@ def gemm_bf16_splitk(a: torch.Tensor, b: torch.Tensor, k_splits: int,
     ws_bytes = 0 if workspace is None else workspace.numel() * 4
     _check(lib.gemm_bf16_splitk(_ptr(a), _ptr(b), _ptr(out), _ptr(workspace), ws_bytes, m, n, k,
                                 k_splits, _stream(stream)), "gemm_bf16_splitk")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # BG_NOALLOC_SCRATCH_BYTES
+
+
+def gemm_bf16_splitk_noalloc(a: torch.Tensor, b: torch.Tensor, k_splits: int, out: torch.Tensor,
+                             stream=None):
+    """Split-K GEMM whose FP32 planes live in the library's static per-device
+    scratch (k_splits*M*N*4 <= NOALLOC_SCRATCH_BYTES); allocates nothing, so
+    `out` must be supplied. Calls that may overlap on one device race."""
+    m, k = _dims(_bits16(a, "A"), 2, "A")
+    n, _ = _dims(_bits16(b, "B"), 2, "B")
+    _shape(b, (n, k), "B")
+    if out is None:
+        raise ValueError("gemm_bf16_splitk_noalloc allocates nothing: pass `out`")
+    _shape(_bits16(out, "out"), (m, n), "out")
+    _on_device(a, b, out)
+    _check(lib.gemm_bf16_splitk_noalloc(_ptr(a), _ptr(b), _ptr(out), m, n, k, k_splits, _stream(stream)),
+           "gemm_bf16_splitk_noalloc")
     return out
 
 

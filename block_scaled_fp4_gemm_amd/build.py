@@ -18,7 +18,7 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libblockgemm.so")
 OBJDIR = os.path.join(ROOT, "_build", "obj")
 
-SOURCES = ["api.cpp", "gemm_mfma.hip", "gemm_ordered.hip"]
+SOURCES = ["api.cpp", "gemm_mfma.hip", "gemm_ordered.hip", "noalloc.hip"]
 
 ARCH = "gfx950"
 COMMON = [

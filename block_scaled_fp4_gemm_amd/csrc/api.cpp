@@ -253,6 +253,30 @@ bg_status gemm_bf16_splitk(const uint16_t* A, const uint16_t* B, uint16_t* C, fl
     return launched(bg::launch_splitk_reduce(workspace, C, M, N, k_splits, st));
 }
 
+bg_status gemm_bf16_splitk_noalloc(const uint16_t* A, const uint16_t* B, uint16_t* C, uint32_t M,
+                                   uint32_t N, uint32_t K, uint32_t k_splits, void* stream) {
+    if (k_splits == 0 || k_splits > kMaxSplits) return BG_ERR_SHAPE;
+    bg_status s = check_dense(A, B, C, M, N, K, 2);
+    if (s != BG_OK || M == 0 || N == 0) return s;
+    const uint64_t need = (uint64_t)k_splits * M * N * 4;
+    if (k_splits > 1 && need > bg::kNoallocScratchBytes) return BG_ERR_WORKSPACE;
+    uint32_t cus = 0;
+    if ((s = check_device(&cus)) != BG_OK) return s;
+    const hipStream_t st = (hipStream_t)stream;
+    if (k_splits == 1) {
+        bg::DenseProblem p{A, B, C, M, N, K, K, K, N, K, 1, 0.0f, cus};
+        return launched(bg::launch_dense(p, bg::EPI_STORE_BF16, st));
+    }
+    void* ws = nullptr;
+    if (bg::noalloc_scratch(&ws) != hipSuccess) return BG_ERR_DEVICE;
+    const uint64_t per = ((uint64_t)K + k_splits - 1) / k_splits;
+    const uint32_t chunk = (uint32_t)((per + 63) / 64 * 64);
+    bg::DenseProblem p{A, B, ws, M, N, K, K, K, N, chunk, k_splits, 0.0f, cus};
+    hipError_t e = bg::launch_dense(p, bg::EPI_STORE_F32, st);
+    if (e != hipSuccess) return BG_ERR_LAUNCH;
+    return launched(bg::launch_splitk_reduce(static_cast<const float*>(ws), C, M, N, k_splits, st));
+}
+
 bg_status gemm_bf16_ordered(const uint16_t* A, const uint16_t* B, uint16_t* C, uint32_t M,
                             uint32_t N, uint32_t K, void* stream) {
     bg_status s = check_dense(A, B, C, M, N, K, 2);

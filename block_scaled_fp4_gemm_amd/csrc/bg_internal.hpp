@@ -53,6 +53,12 @@ struct W4a16Problem {
     uint32_t cus;        // compute units of the current device (tile choice)
 };
 
+// Size of the library-owned split-K scratch of gemm_bf16_splitk_noalloc, per
+// device (noalloc.hip).
+constexpr size_t kNoallocScratchBytes = BG_NOALLOC_SCRATCH_BYTES;
+// Device address of the current device's scratch (taken once per device).
+hipError_t noalloc_scratch(void** ptr);
+
 // Current tuning override of a bg_tune_key (-1: automatic choice).
 int tune(int key);
 

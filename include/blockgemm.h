@@ -154,6 +154,30 @@ bg_status gemm_bf16_splitk(const uint16_t* A, const uint16_t* B, uint16_t* C,
 size_t gemm_bf16_splitk_workspace_bytes(uint32_t M, uint32_t N, uint32_t k_splits);
 
 /*
+ * gemm_bf16_splitk_noalloc: gemm_bf16_splitk without a caller workspace and
+ * without any allocation, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. The FP32 planes go to a library-owned static device buffer of
+ * BG_NOALLOC_SCRATCH_BYTES (32 MiB) that each device holds from the first
+ * call on it until the process ends.
+ *
+ * Same result, chunking and reduction order as gemm_bf16_splitk (bit-identical
+ * for the same arguments). Limit: k_splits * M * N * 4 <=
+ * BG_NOALLOC_SCRATCH_BYTES, else BG_ERR_WORKSPACE (nothing is enqueued).
+ * k_splits == 1 writes C directly and uses no scratch.
+ *
+ * Every call on one device shares that device's buffer, which keeps the last
+ * call's planes: calls that may overlap on one device (other streams, other
+ * threads) race on it and must be ordered by the caller. Nothing in the buffer
+ * needs clearing: every plane element is written before the reduce reads it.
+ * Other rules as gemm_bf16_splitk.
+ */
+#define BG_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+bg_status gemm_bf16_splitk_noalloc(const uint16_t* A, const uint16_t* B, uint16_t* C,
+                                   uint32_t M, uint32_t N, uint32_t K, uint32_t k_splits,
+                                   void* stream);
+
+/*
  * gemm_bf16_ordered: order-preserving GEMM for router logits.
  *   acc = +0.0f; for k = 0, 1, ..., K-1: acc = fl32(acc + fl32(A[i,k] * B[j,k]));
  *   C[i,j] = bf16(acc).

@@ -87,6 +87,11 @@ hipError_t launch_scaled_add(uint16_t* out, const uint16_t* delta, size_t count,
     ++g_launches;
     return hipSuccess;
 }
+static float g_fake_scratch[4];
+hipError_t noalloc_scratch(void** ptr) {
+    *ptr = g_fake_scratch;
+    return hipSuccess;
+}
 }  // namespace bg
 
 template <class T>
@@ -107,6 +112,8 @@ int main() {
     CHECK(gemm_bf16_splitk(u16(A), u16(B), u16(C), f32(W), (size_t)8 * 5120 * 2048 * 4, 5120, 2048, 11008, 8,
                            nullptr) == BG_OK);
     CHECK(g_last.splits == 8 && g_last.k_chunk == 1408);
+    CHECK(gemm_bf16_splitk_noalloc(u16(A), u16(B), u16(C), 128, 2048, 11008, 8, nullptr) == BG_OK);
+    CHECK(gemm_bf16_splitk_noalloc(u16(A), u16(B), u16(C), 1024, 2048, 11008, 8, nullptr) == BG_ERR_WORKSPACE);
     CHECK(gemm_bf16_dual(u16(A), u16(B), u16(S1), u16(C), u16(W), 5120, 11008, 2048, nullptr) == BG_OK);
     CHECK(gemm_bf16_strided(u16(A), 4099, u16(B), 2048, u16(C), 11008, 17, 11008, 2048, nullptr) == BG_OK);
     CHECK(gemm_bf16_scaled_acc(u16(A), u16(B), u16(C), 2048, 17408, 64, 2.0f, nullptr) == BG_OK);
@@ -130,6 +137,7 @@ int main() {
     CHECK(gemm_bf16(u16(A), u16(B), u16(A + 16), 4, 4, 64, nullptr) == BG_ERR_ALIAS);
     CHECK(gemm_bf16_splitk(u16(A), u16(B), u16(C), f32(W), 10, 4, 4, 128, 2, nullptr) == BG_ERR_WORKSPACE);
     CHECK(gemm_bf16_splitk(u16(A), u16(B), u16(C), f32(W), 1 << 20, 4, 4, 128, 65, nullptr) == BG_ERR_SHAPE);
+    CHECK(gemm_bf16_splitk_noalloc(u16(A), u16(B), u16(C), big, 4, 4, 2, nullptr) == BG_ERR_SHAPE);
     CHECK(gemm_bf16_strided(u16(A), big, u16(B), 8, u16(C), 4, 4, 4, 8, nullptr) == BG_ERR_SHAPE);
     CHECK(gemm_bf16_strided(u16(A), 0x7FFFFFFFu, u16(B), 0x7FFFFFFFu, u16(C), 0x7FFFFFFFu, 0x7FFFFFFFu,
                             0x7FFFFFFFu, 8, nullptr) == BG_ERR_ALIAS);

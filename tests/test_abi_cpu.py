@@ -152,6 +152,13 @@ def test_shape_rules():
 
 def test_workspace_rules():
     L = bg.lib
+    # the allocation-free split-K: k_splits * M * N * 4 must fit the 32 MiB scratch
+    assert L.gemm_bf16_splitk_noalloc(A, B, C, 1024, 2048, 256, 5, None) == bg.BG_ERR_WORKSPACE
+    assert L.gemm_bf16_splitk_noalloc(A, B, C, 1024, 2048, 256, 0, None) == bg.BG_ERR_SHAPE
+    assert L.gemm_bf16_splitk_noalloc(A, B, C, 1024, 2048, 256, 65, None) == bg.BG_ERR_SHAPE
+    assert L.gemm_bf16_splitk_noalloc(A, B, None, 4, 4, 8, 2, None) == bg.BG_ERR_NULL
+    assert L.gemm_bf16_splitk_noalloc(A, B, A + 16, 4, 4, 64, 2, None) == bg.BG_ERR_ALIAS
+    assert L.gemm_bf16_splitk_noalloc(None, None, None, 0, 4, 64, 2, None) == bg.BG_OK
     need = 2 * 4 * 4 * 4
     assert L.gemm_bf16_splitk(A, B, C, None, need, 4, 4, 128, 2, None) == bg.BG_ERR_WORKSPACE
     assert L.gemm_bf16_splitk(A, B, C, W, need - 1, 4, 4, 128, 2, None) == bg.BG_ERR_WORKSPACE
@@ -167,6 +174,7 @@ def test_valid_arguments_reach_the_device_check():
     assert L.gemm_w4a16(A, B, S2, 0.5, C, 4, 4, 32, None) == bg.BG_ERR_DEVICE
     assert L.gemm_bf16_strided(A, 13, B, 8, C, 5, 4, 4, 8, None) == bg.BG_ERR_DEVICE
     assert L.gemm_bf16_dual(A, B, S1, C, W, 4, 4, 8, None) == bg.BG_ERR_DEVICE
+    assert L.gemm_bf16_splitk_noalloc(A, B, C, 1024, 2048, 256, 4, None) == bg.BG_ERR_DEVICE
 
 
 def test_python_binding_raises_on_status():
