@@ -38,6 +38,7 @@ _SIGS = {
     "gemm_bf16_ordered_f32": [_p, _p, _p, _u32, _u32, _u32, _p],
     "gemm_fp4_blockscaled": [_p, _p, _p, _p, _p, _u32, _u32, _u32, _p],
     "gemm_w4a16": [_p, _p, _p, _f32, _p, _u32, _u32, _u32, _p],
+    "gemm_w4a16_t": [_p, _p, _p, _u32, _f32, _p, _u32, _u32, _u32, _p],
     "gemm_fp4_blockscaled_batched": [_p, _p, _p, _p, _p, _u32, _u32, _u32, _u32, _p],
     "gemm_fp4_blockscaled_splitk": [_p, _p, _p, _p, _p, _p, _sz, _u32, _u32, _u32, _u32, _p],
     "fp4_scales_from_blocked": [_p, _p, _u32, _u32, _u32, _p],
@@ -391,6 +392,24 @@ def gemm_w4a16(a: torch.Tensor, b: torch.Tensor, sfb: torch.Tensor, scale_2: flo
     _on_device(a, b, sfb, out)
     _check(lib.gemm_w4a16(_ptr(a), _ptr(b), _ptr(sfb), float(scale_2), _ptr(out), m, n, k, _stream(stream)),
            "gemm_w4a16")
+    return out
+
+
+def gemm_w4a16_t(a: torch.Tensor, bt: torch.Tensor, sfbt: torch.Tensor, n: int, scale_2: float,
+                 out: torch.Tensor | None = None, stream=None):
+    """gemm_w4a16 with transposed weights: Bt [K/2, ldb] bytes (k pairs as rows), SFBt [K/16, ldb],
+    ldb >= n taken from Bt's row length (pad columns n..ldb-1 unused)."""
+    m, k = _dims(_bits16(a, "A"), 2, "A")
+    if k % 16 != 0:
+        raise ValueError(f"K = {k} must be a multiple of 16 (one scale per 16 elements)")
+    rows, ldb = _dims(_bytes(bt, "Bt"), 2, "Bt")
+    if rows != k // 2 or ldb < n or n < 0:
+        raise ValueError(f"Bt must be [K/2, ldb] = [{k // 2}, >= {n}], got {tuple(bt.shape)}")
+    _shape(_bytes(sfbt, "SFBt"), (k // 16, ldb), "SFBt")
+    out = _out16(out, (m, n), a)
+    _on_device(a, bt, sfbt, out)
+    _check(lib.gemm_w4a16_t(_ptr(a), _ptr(bt), _ptr(sfbt), ldb, float(scale_2), _ptr(out), m, n, k,
+                            _stream(stream)), "gemm_w4a16_t")
     return out
 
 

@@ -378,7 +378,29 @@ bg_status gemm_w4a16(const uint16_t* A, const uint8_t* B, const uint8_t* SFB, fl
     uint32_t cus = 0;
     bg_status s = check_device(&cus);
     if (s != BG_OK) return s;
-    bg::W4a16Problem p{A, B, SFB, C, M, N, K, scale_2, cus};
+    bg::W4a16Problem p{A, B, SFB, C, M, N, K, scale_2, cus, 0};
+    return launched(bg::launch_w4a16(p, (hipStream_t)stream));
+}
+
+bg_status gemm_w4a16_t(const uint16_t* A, const uint8_t* Bt, const uint8_t* SFBt, uint32_t ldb, float scale_2,
+                       uint16_t* C, uint32_t M, uint32_t N, uint32_t K, void* stream) {
+    if (!dims_ok(M, N, K) || (K % 16) != 0 || ldb > kMaxDim || ldb < N || ldb == 0) return BG_ERR_SHAPE;
+    if (M == 0 || N == 0) return BG_OK;
+    const uint64_t a_bytes = (uint64_t)M * K * 2;
+    const uint64_t b_bytes = (uint64_t)(K / 2) * ldb, sb_bytes = (uint64_t)(K / 16) * ldb;
+    const uint64_t c_bytes = (uint64_t)M * N * 2;
+    if (missing(A, a_bytes) || missing(Bt, b_bytes) || missing(SFBt, sb_bytes) || missing(C, c_bytes))
+        return BG_ERR_NULL;
+    if (misaligned(A, a_bytes) || misaligned(Bt, b_bytes) || misaligned(SFBt, sb_bytes) || misaligned(C, c_bytes))
+        return BG_ERR_ALIGN;
+    const Range rc = range_of(C, c_bytes);
+    if (overlap(rc, range_of(A, a_bytes)) || overlap(rc, range_of(Bt, b_bytes)) ||
+        overlap(rc, range_of(SFBt, sb_bytes)))
+        return BG_ERR_ALIAS;
+    uint32_t cus = 0;
+    bg_status s = check_device(&cus);
+    if (s != BG_OK) return s;
+    bg::W4a16Problem p{A, Bt, SFBt, C, M, N, K, scale_2, cus, ldb};
     return launched(bg::launch_w4a16(p, (hipStream_t)stream));
 }
 

@@ -51,6 +51,7 @@ struct W4a16Problem {
     uint32_t M, N, K;
     float scale_2;       // per-tensor weight scale
     uint32_t cus;        // compute units of the current device (tile choice)
+    uint32_t ldbt;       // 0: B [N, K/2], SFB [N, K/16]; else B [K/2, ldbt], SFB [K/16, ldbt] (transposed)
 };
 
 // Size of the library-owned split-K scratch of gemm_bf16_splitk_noalloc, per

@@ -60,10 +60,19 @@ enum Source : int {
     SRC_FP4W = 5,
     SRC_W4A16W = 6,
     SRC_FP4W_BF16 = 7,
+    // W4A16 with the weights in the transposed layout [K/2, ldb] bytes (byte
+    // (r, n) holds k = 2r and 2r+1 of weight row n) and scales [K/16, ldb]:
+    // 4-byte loads where ldb % 4 == 0, byte loads otherwise
+    SRC_W4A16T4 = 8,
+    SRC_W4A16T1 = 9,
+    SRC_FP4T4_BF16 = 10,   // staging only
+    SRC_FP4T1_BF16 = 11,
 };
 
 constexpr bool src_fp4(int src) { return src == SRC_FP4 || src == SRC_FP4W; }
-constexpr bool src_w4a16(int src) { return src == SRC_W4A16 || src == SRC_W4A16W; }
+constexpr bool src_w4a16t(int src) { return src == SRC_W4A16T4 || src == SRC_W4A16T1; }
+constexpr bool src_w4a16(int src) { return src == SRC_W4A16 || src == SRC_W4A16W || src_w4a16t(src); }
+constexpr bool src_fp4t(int src) { return src == SRC_FP4T4_BF16 || src == SRC_FP4T1_BF16; }
 // K elements per staging unit of an FP4 operand of `rows` tile rows staged by
 // nt threads (0: not FP4). The 32-element units are taken only where they
 // divide evenly among the threads: otherwise some waves would convert twice
@@ -86,6 +95,7 @@ struct KParams {
     int M, N, K;
     int lda, ldb;          // elements between consecutive rows of A and B (BF16 operands; >= K)
     int ldc;               // elements between consecutive rows of C (N, or more for a column range)
+    int ldbt;              // bytes between rows of transposed FP4 weights and of their scales
     int k_chunk;           // K elements per split (blockIdx.y)
     int tiles_m, tiles_n;
     float scale;
@@ -354,6 +364,104 @@ struct Stager<ROWS, NT, SRC_FP4W, BK> : Fp4Stager<ROWS, NT, true, fp4_unit(SRC_F
 
 template <int ROWS, int NT>
 struct Stager<ROWS, NT, SRC_FP4W_BF16, BK> : Fp4Stager<ROWS, NT, false, fp4_unit(SRC_FP4W_BF16, ROWS, NT)> {};
+
+// NVFP4 weights in the transposed layout of the gemm_dense.rs page's `_ldb`
+// W4A16 launchers: byte (r, n) at Bt + r*ldb + n holds the E2M1 codes of
+// weight row n at k = 2r (low nibble) and k = 2r + 1 (high nibble), and the
+// E4M3 scale of group g of row n is at SFBt + g*ldb + n; ldb >= N may be any
+// value (odd for a vocabulary-sized N). A unit is TW consecutive weight rows
+// (n) times one 16-element scale group: 8 loads of TW bytes (one per k-pair
+// row) and one TW-byte scale load, transposed in registers into each weight
+// row's 8 packed bytes (the K-contiguous form), then dequantized exactly to
+// BF16 as in Fp4Stager and written as two 16-byte chunks per weight row.
+// Columns past the last valid one are clamped to it (their outputs are never
+// stored); with TW = 4 a unit starts at a multiple of 4 below ldb, so every
+// 4-byte load stays inside its row of ldb bytes.
+template <int ROWS, int NT, int TW>
+struct Fp4TStager {
+    static_assert(TW == 1 || TW == 4, "1- or 4-byte column loads");
+    static constexpr int CPU_ = 4;                        // weight rows per unit (TW = 1: 4 byte loads)
+    static constexpr int UNITS = (ROWS / CPU_) * (BK / 16);
+    static constexpr int PER = (UNITS + NT - 1) / NT;
+    uint32_t d[PER][8];   // d[i][r]: bytes of k-pair row r, weight rows c = 0..3 in bytes c
+    uint32_t s[PER];      // scale bytes of the unit's 4 weight rows
+    uint32_t valid;
+
+    __device__ __forceinline__ void load(const uint8_t* bt, const uint8_t* sft, int n0, int N, int ldb,
+                                         int K, int k0, int k_end, int tid) {
+        valid = 0u;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int u = tid + i * NT;
+            if (PER * NT != UNITS && u >= UNITS) break;
+            const int quad = u / (BK / 16), g = u % (BK / 16);
+            const int gk = k0 + g * 16;
+            const int gkc = min(gk, K - 16);             // K >= 16 whenever a step exists
+            const uint8_t* rowp = bt + (int64_t)(gkc >> 1) * ldb;
+            const uint8_t* srow = sft + (int64_t)(gkc >> 4) * ldb;
+            if constexpr (TW == 4) {
+                const int n = min(n0 + quad * 4, ldb - 4);   // ldb % 4 == 0, so n % 4 == 0
+#pragma unroll
+                for (int r = 0; r < 8; ++r) d[i][r] = *reinterpret_cast<const uint32_t*>(rowp + (int64_t)r * ldb + n);
+                s[i] = *reinterpret_cast<const uint32_t*>(srow + n);
+            } else {
+                int n[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) n[c] = min(n0 + quad * 4 + c, N - 1);
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const uint8_t* q = rowp + (int64_t)r * ldb;
+                    d[i][r] = (uint32_t)q[n[0]] | ((uint32_t)q[n[1]] << 8) | ((uint32_t)q[n[2]] << 16) |
+                              ((uint32_t)q[n[3]] << 24);
+                }
+                s[i] = (uint32_t)srow[n[0]] | ((uint32_t)srow[n[1]] << 8) | ((uint32_t)srow[n[2]] << 16) |
+                       ((uint32_t)srow[n[3]] << 24);
+            }
+            valid |= (gk < k_end ? 1u : 0u) << i;
+        }
+    }
+
+    // byte c of each of four words, gathered into one word (word r -> byte r)
+    __device__ __forceinline__ static uint32_t column(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, int c) {
+        const int sh = 8 * c;
+        return ((w0 >> sh) & 0xFFu) | (((w1 >> sh) & 0xFFu) << 8) | (((w2 >> sh) & 0xFFu) << 16) |
+               (((w3 >> sh) & 0xFFu) << 24);
+    }
+
+    __device__ __forceinline__ void store(uint16_t* lds, int tid) const { store_units(lds, tid, 0, PER); }
+
+    __device__ __forceinline__ void store_units(uint16_t* lds, int tid, int lo, int hi) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            if (i < lo || i >= hi) continue;
+            const int u = tid + i * NT;
+            if (PER * NT != UNITS && u >= UNITS) break;
+            const int quad = u / (BK / 16), g = u % (BK / 16);
+            const bool in = (valid >> i) & 1u;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int row = quad * 4 + c;
+                // the 16 elements of weight row n0+row in this group, K-contiguous:
+                // k-pair rows 0..3 in the low word, 4..7 in the high word
+                const uint32_t lo_w = in ? column(d[i][0], d[i][1], d[i][2], d[i][3], c) : 0u;
+                const uint32_t hi_w = in ? column(d[i][4], d[i][5], d[i][6], d[i][7], c) : 0u;
+                const uint32_t sb = in ? (s[i] >> (8 * c)) & 0xFFu : 0u;
+                const f32x2 sc32 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sb, 1.0f, false);
+                uint16_t* dst = lds + row * BK;
+                *reinterpret_cast<u32x4*>(dst + chunk_slot<8>(row, 2 * g) * 8) =
+                    Fp4Stager<ROWS, NT, false>::deq8(lo_w, f16x2{}, sc32.x);
+                *reinterpret_cast<u32x4*>(dst + chunk_slot<8>(row, 2 * g + 1) * 8) =
+                    Fp4Stager<ROWS, NT, false>::deq8(hi_w, f16x2{}, sc32.x);
+            }
+        }
+    }
+};
+
+template <int ROWS, int NT>
+struct Stager<ROWS, NT, SRC_FP4T4_BF16, BK> : Fp4TStager<ROWS, NT, 4> {};
+
+template <int ROWS, int NT>
+struct Stager<ROWS, NT, SRC_FP4T1_BF16, BK> : Fp4TStager<ROWS, NT, 1> {};
 
 // ---------------------------------------------------------------------------
 // Direct global -> LDS staging (buffer_load_dwordx4 ... lds) for BF16 rows
@@ -753,7 +861,11 @@ gemm_mfma_kernel(KParams p) {
     zero_acc(acc);
 
     constexpr int SRC_A = src_w4a16(SRC) ? SRC_BF16_VEC : SRC;
-    constexpr int SRC_B = SRC == SRC_W4A16 ? SRC_FP4_BF16 : SRC == SRC_W4A16W ? SRC_FP4W_BF16 : SRC;
+    constexpr int SRC_B = SRC == SRC_W4A16    ? SRC_FP4_BF16
+                          : SRC == SRC_W4A16W   ? SRC_FP4W_BF16
+                          : SRC == SRC_W4A16T4  ? SRC_FP4T4_BF16
+                          : SRC == SRC_W4A16T1  ? SRC_FP4T1_BF16
+                                                : SRC;
     // RSETS register sets form a ring: set r holds the steps t with t % RSETS == r
     constexpr int NSETS = RSETS > 1 ? RSETS : 1;
     Stager<BM, NT, SRC_A> sa[NSETS];
@@ -764,6 +876,9 @@ gemm_mfma_kernel(KParams p) {
         if constexpr (src_fp4(SRC)) {
             sa.load(p.Aq, p.SFA, m0, p.M, p.K, k0, ke, tid);
             sb.load(p.Bq, p.SFB, n0, p.N, p.K, k0, ke, tid);
+        } else if constexpr (src_w4a16t(SRC)) {
+            sa.load(p.A, m0, p.M, p.lda, k0, ke, tid);
+            sb.load(p.Bq, p.SFB, n0, p.N, p.ldbt, p.K, k0, ke, tid);
         } else if constexpr (src_w4a16(SRC)) {
             sa.load(p.A, m0, p.M, p.lda, k0, ke, tid);
             sb.load(p.Bq, p.SFB, n0, p.N, p.K, k0, ke, tid);
@@ -800,9 +915,10 @@ gemm_mfma_kernel(KParams p) {
     // (per 16 FP4 elements: 24 to FP16, 32 to BF16, and two 16-byte writes)
     constexpr int UEA = fp4_unit(SRC_A, BM, NT), UEB = fp4_unit(SRC_B, BN, NT);
     constexpr int VU_A = src_fp4(SRC_A) ? 24 * UEA / 16 : 0;
-    constexpr int VU_B = src_fp4(SRC_B) ? 24 * UEB / 16 : UEB * 2;
+    // (a transposed-weight unit: 64 elements, about 150 VALU, eight writes)
+    constexpr int VU_B = src_fp4t(SRC_B) ? 150 : src_fp4(SRC_B) ? 24 * UEB / 16 : UEB * 2;
     constexpr int WU_A = UEA ? UEA / 8 : 1;
-    constexpr int WU_B = UEB ? UEB / 8 : 1;
+    constexpr int WU_B = src_fp4t(SRC_B) ? 8 : UEB ? UEB / 8 : 1;
     constexpr int CVT_VALU = (PA * VU_A + PB * VU_B + KK - 2) / (KK - 1);
     constexpr int CVT_DSW = (PA * WU_A + PB * WU_B + KK - 2) / (KK - 1);
     auto store_part = [&](auto& sa, auto& sb, uint16_t* buf, int part) {
@@ -1529,6 +1645,33 @@ hipError_t launch_scales_from_blocked(const uint8_t* src, uint8_t* dst, uint32_t
     return hipGetLastError();
 }
 
+// Transposed-weight W4A16 (weights [K/2, ldb] bytes, scales [K/16, ldb]):
+// three tiles, chosen by the W4A16 cost model; 4-byte column loads when ldb
+// is a multiple of 4, byte loads otherwise.
+template <int S>
+hipError_t launch_w4a16_t(const KParams& kp, int cus, hipStream_t stream) {
+    int cfg = tune(BG_TUNE_W4A16_TILE);
+    if (cfg < 0) {
+        double best_t = 1e300;
+        for (const W4a16Choice& c : kW4a16Choices) {
+            if (c.cfg > 2) continue;
+            const double tiles = (double)((kp.M + c.bm - 1) / c.bm) * ((kp.N + c.bn - 1) / c.bn);
+            const double slots = (double)cus * c.occ;
+            const double rounds = tiles <= cus ? 1.0 : (double)(int64_t)((tiles + slots - 1) / slots);
+            const double t = rounds * (tiles <= cus ? 1.0 : c.occ) * c.bm * c.bn / c.rate;
+            if (t < best_t) {
+                best_t = t;
+                cfg = c.cfg;
+            }
+        }
+    }
+    switch (cfg) {
+        case 1: return launch_cfg<128, 256, 2, 4, EPI_SCALE_BF16, S, 2>(kp, 1, stream);
+        case 2: return launch_cfg<128, 128, 2, 2, EPI_SCALE_BF16, S, 2>(kp, 1, stream);
+        default: return launch_cfg<256, 256, 2, 4, EPI_SCALE_BF16, S, 1>(kp, 1, stream);
+    }
+}
+
 hipError_t launch_w4a16(const W4a16Problem& p, hipStream_t stream) {
     KParams kp{};
     kp.A = p.A;
@@ -1542,6 +1685,12 @@ hipError_t launch_w4a16(const W4a16Problem& p, hipStream_t stream) {
     kp.ldc = (int)p.N;
     kp.k_chunk = (int)p.K;
     kp.scale = p.scale_2;
+    if (p.ldbt > 0) {
+        kp.ldbt = (int)p.ldbt;
+        const int cus = p.cus > 0 ? (int)p.cus : 256;
+        return p.ldbt % 4 == 0 ? launch_w4a16_t<SRC_W4A16T4>(kp, cus, stream)
+                               : launch_w4a16_t<SRC_W4A16T1>(kp, cus, stream);
+    }
     int cfg = tune(BG_TUNE_W4A16_TILE);
     if (cfg < 0) cfg = choose_w4a16(kp.M, kp.N, p.cus > 0 ? (int)p.cus : 256);
     // 32-element weight units when no unit can straddle the end of K; the

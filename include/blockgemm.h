@@ -303,6 +303,33 @@ bg_status gemm_w4a16(const uint16_t* A, const uint8_t* B, const uint8_t* SFB, fl
                      uint16_t* C, uint32_t M, uint32_t N, uint32_t K, void* stream);
 
 /*
+ * gemm_w4a16_t: gemm_w4a16 with the weights in the transposed layout and an
+ * explicit row stride, for weight matrices whose N is not a multiple of 16
+ * (the vocabulary-sized lm_head).
+ *
+ * gemm_dense.rs page, doc comments of w4a16_gemm_n128_ldb and
+ * w4a16_gemm_n128_m128_bf16_ldb: the transposed weight's row r sits at
+ * r * ldb; with N odd (248077) an unpadded stride misaligns 15 of every 16
+ * rows for 16-byte loads, so the caller passes ldb = align_up(N, 128) with
+ * the pad columns zero-filled. Here any ldb >= N is accepted: ldb % 4 == 0
+ * takes 4-byte column loads, any other stride byte loads; neither faults.
+ *
+ *  A:    [M, K] BF16 activations.
+ *  Bt:   [K/2, ldb] bytes: byte (r, n) holds weight row n's E2M1 codes for
+ *        k = 2r (LOW nibble) and k = 2r + 1 (high nibble); columns N..ldb-1
+ *        are padding (read, never used). The whole (K/2) * ldb bytes must be
+ *        readable.
+ *  SFBt: [K/16, ldb] E4M3FN bytes: byte (g, n) scales k in [16g, 16g + 16) of
+ *        weight row n (the scale tensor transposed with the same stride).
+ *  C:    [M, N] BF16, C[i,j] = bf16(fl32(s2 * sum_k A[i,k] * w[j,k])) exactly
+ *        as gemm_w4a16 with the same weights in its [N, K/2] layout.
+ *  K % 16 == 0 and N <= ldb <= 2^31 - 1 (BG_ERR_SHAPE otherwise); C must not
+ *  overlap A, Bt or SFBt (BG_ERR_ALIAS).
+ */
+bg_status gemm_w4a16_t(const uint16_t* A, const uint8_t* Bt, const uint8_t* SFBt, uint32_t ldb, float scale_2,
+                       uint16_t* C, uint32_t M, uint32_t N, uint32_t K, void* stream);
+
+/*
  * bf16_scaled_add: out[i] = bf16( f32(out[i]) + fl32(scale * f32(delta[i])) )
  * over `count` BF16 elements. The second half of the unfused LoRA fold that
  * gemm_bf16_scaled_acc must equal bit for bit (gemm_dense.rs page, doc comment

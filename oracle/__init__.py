@@ -19,6 +19,7 @@ from .codecs import (  # noqa: F401
     bf16_to_f32,
     bf16_to_f64,
     dequant_fp4,
+    dequant_fp4_t,
     e2m1_to_f64,
     e4m3fn_to_f64,
     f32_to_bf16,
@@ -35,6 +36,7 @@ from .gemm import (  # noqa: F401
     gemm_splitk_planes_ref,
     gemm_w4a16_exact,
     gemm_w4a16_ref,
+    gemm_w4a16_t_ref,
     rms,
     scaled_acc_admissible,
     scaled_acc_candidate_deltas,

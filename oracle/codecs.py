@@ -123,3 +123,23 @@ def scales_from_blocked(blocked, rows: int, k_groups: int, batch: int = 1) -> np
                             out[l, tile_m * 128 + i_m * 32 + g_m, tile_k * 4 + i_k] = src[pos]
                             pos += 1
     return out
+
+
+def dequant_fp4_t(bt, sfbt, n: int) -> np.ndarray:
+    """Weights stored transposed, as exact FP64 values in [n, K] (row j = weight row j).
+
+    gemm_dense.rs page, doc comments of the `_ldb` W4A16 launchers: the
+    transposed weight has one row per k pair at a row stride ldb >= N (pad
+    columns unused). Byte (r, j) = bt[r, j] holds weight row j's codes for
+    k = 2r (low nibble) and k = 2r + 1 (high nibble); the E4M3 scale of k in
+    [16g, 16g + 16) of row j is sfbt[g, j].
+    """
+    b = np.asarray(bt, dtype=np.uint8)[:, :n]
+    sf = np.asarray(sfbt, dtype=np.uint8)[:, :n]
+    k = 2 * b.shape[0]
+    assert sf.shape[0] * 16 == k, "one scale row per 16 K elements"
+    codes = np.empty((k, n), dtype=np.uint8)
+    codes[0::2] = b & 0x0F
+    codes[1::2] = b >> 4
+    vals = e2m1_to_f64(codes) * np.repeat(e4m3fn_to_f64(sf), 16, axis=0)
+    return vals.T

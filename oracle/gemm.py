@@ -18,7 +18,7 @@ import math
 
 import numpy as np
 
-from .codecs import bf16_to_f32, bf16_to_f64, dequant_fp4, f32_to_bf16
+from .codecs import bf16_to_f32, bf16_to_f64, dequant_fp4, dequant_fp4_t, f32_to_bf16
 
 
 # ---------------------------------------------------------------------------
@@ -287,6 +287,13 @@ def gemm_w4a16_exact(a_bits, b_packed, sfb, scale_2) -> np.ndarray:
         raise ValueError("dot products are not exact in FP32")
     prod = np.float32(scale_2) * acc32        # one IEEE single multiply, RNE
     return f32_to_bf16(prod.astype(np.float32))
+
+
+def gemm_w4a16_t_ref(a_bits, bt, sfbt, n: int, scale_2) -> np.ndarray:
+    """gemm_w4a16_ref for weights in the transposed layout (dequant_fp4_t):
+    ref[i, j] = s2 * sum_k A[i, k] * w[j, k] in FP64, s2 = fl32(scale_2)."""
+    s2 = float(np.float32(scale_2))
+    return s2 * (bf16_to_f64(a_bits) @ dequant_fp4_t(bt, sfbt, n).T)
 
 
 def gemm_fp4_splitk_planes_ref(a_packed, sfa, b_packed, sfb, k_splits: int) -> np.ndarray:

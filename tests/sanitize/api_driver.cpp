@@ -126,6 +126,7 @@ int main() {
     CHECK(fp4_scales_from_blocked(u8(S1), u8(S2), 256, 64, 2, nullptr) == BG_OK);
     CHECK(gemm_w4a16(u16(A), u8(B), u8(S2), 0.5f, u16(C), 1016, 12288, 2048, nullptr) == BG_OK);
     CHECK(bf16_scaled_add(u16(A), u16(B), 1000, 0.5f, nullptr) == BG_OK);
+    CHECK(gemm_w4a16_t(u16(A), u8(B), u8(S2), 248192, 0.5f, u16(C), 37, 248077, 2048, nullptr) == BG_OK);
     const int valid = g_launches;
 
     // invalid calls return their status and launch nothing
@@ -146,6 +147,8 @@ int main() {
                                        65535, nullptr) != BG_OK);
     CHECK(fp4_scales_from_blocked(u8(S1), u8(S2), 100, 4, 1, nullptr) == BG_ERR_SHAPE);
     CHECK(gemm_w4a16(u16(A), u8(B), u8(S2), 1.0f, u16(C), 4, big, 32, nullptr) == BG_ERR_SHAPE);
+    CHECK(gemm_w4a16_t(u16(A), u8(B), u8(S2), 100, 1.0f, u16(C), 4, 101, 32, nullptr) == BG_ERR_SHAPE);
+    CHECK(gemm_w4a16_t(u16(A), u8(B), u8(S2), 0x7FFFFFFFu, 1.0f, u16(C), 4, 101, 0x7FFFFFF0u, nullptr) == BG_ERR_ALIAS);
     CHECK(bf16_scaled_add(u16(A), u16(A + 16), 64, 1.0f, nullptr) == BG_ERR_ALIAS);
     CHECK(bf16_scaled_add(u16(A), u16(B), (size_t)1 << 63, 1.0f, nullptr) == BG_ERR_SHAPE);
     CHECK(g_launches == valid);

@@ -131,6 +131,15 @@ def test_aliasing_outputs():
 
 def test_shape_rules():
     L = bg.lib
+    # transposed W4A16: N <= ldb, K % 16 == 0
+    assert L.gemm_w4a16_t(A, B, S2, 9, 1.0, C, 4, 10, 32, None) == bg.BG_ERR_SHAPE
+    assert L.gemm_w4a16_t(A, B, S2, 10, 1.0, C, 4, 10, 40, None) == bg.BG_ERR_SHAPE
+    assert L.gemm_w4a16_t(A, B, S2, 1 << 31, 1.0, C, 4, 10, 32, None) == bg.BG_ERR_SHAPE
+    assert L.gemm_w4a16_t(A, None, S2, 11, 1.0, C, 4, 10, 32, None) == bg.BG_ERR_NULL
+    assert L.gemm_w4a16_t(A, B + 4, S2, 11, 1.0, C, 4, 10, 32, None) == bg.BG_ERR_ALIGN
+    # C overlaps the last scale row: SFBt spans (K/16) * ldb bytes
+    assert L.gemm_w4a16_t(A, B, S2, 11, 1.0, S2 + 16, 4, 10, 32, None) == bg.BG_ERR_ALIAS
+    assert L.gemm_w4a16_t(None, None, None, 5, 1.0, None, 0, 5, 32, None) == bg.BG_OK
     assert L.gemm_fp4_blockscaled(A, S1, B, S2, C, 4, 4, 40, None) == bg.BG_ERR_SHAPE   # K % 16
     assert L.gemm_w4a16(A, B, S2, 1.0, C, 4, 4, 40, None) == bg.BG_ERR_SHAPE             # K % 16
     assert L.gemm_w4a16(A, B, S2, 1.0, C, 4, 1 << 31, 32, None) == bg.BG_ERR_SHAPE
@@ -174,6 +183,7 @@ def test_valid_arguments_reach_the_device_check():
     assert L.gemm_w4a16(A, B, S2, 0.5, C, 4, 4, 32, None) == bg.BG_ERR_DEVICE
     assert L.gemm_bf16_strided(A, 13, B, 8, C, 5, 4, 4, 8, None) == bg.BG_ERR_DEVICE
     assert L.gemm_bf16_dual(A, B, S1, C, W, 4, 4, 8, None) == bg.BG_ERR_DEVICE
+    assert L.gemm_w4a16_t(A, B, S2, 248077, 0.5, C, 4, 248077, 32, None) == bg.BG_ERR_DEVICE
     assert L.gemm_bf16_splitk_noalloc(A, B, C, 1024, 2048, 256, 4, None) == bg.BG_ERR_DEVICE
 
 

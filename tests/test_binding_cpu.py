@@ -66,6 +66,9 @@ BAD_SHAPES = [
     (lambda: bg.gemm_w4a16(bf(4, 32), u8(5, 16), u8(5, 3), 1.0), ValueError),
     (lambda: bg.gemm_w4a16(bf(4, 24), u8(5, 12), u8(5, 1), 1.0), ValueError),                   # K % 16
     (lambda: bg.gemm_w4a16(bf(4, 32), u8(5, 16), u8(5, 2), 1.0, out=bf(4, 4)), ValueError),
+    (lambda: bg.gemm_w4a16_t(bf(4, 32), u8(16, 9), u8(2, 9), 10, 1.0), ValueError),        # ldb < N
+    (lambda: bg.gemm_w4a16_t(bf(4, 32), u8(15, 11), u8(2, 11), 10, 1.0), ValueError),      # K/2 rows
+    (lambda: bg.gemm_w4a16_t(bf(4, 32), u8(16, 11), u8(2, 10), 10, 1.0), ValueError),      # SFBt
     (lambda: bg.bf16_scaled_add(bf(8), bf(9), 1.0), ValueError),
     (lambda: bg.bf16_scaled_add(bf(8), torch.zeros(8), 1.0), TypeError),
 ]
@@ -92,6 +95,7 @@ GOOD_HOST = [
     lambda: bg.fp4_scales_from_blocked(u8(128 * 4), 128, 4),
     lambda: bg.gemm_w4a16(bf(4, 32), u8(5, 16), u8(5, 2), 1.0),
     lambda: bg.bf16_scaled_add(bf(8), bf(8), 1.0),
+    lambda: bg.gemm_w4a16_t(bf(4, 32), u8(16, 11), u8(2, 11), 10, 1.0),
 ]
 
 

@@ -139,3 +139,23 @@ def test_bf16_specials_fold():
     bg.gemm_bf16_scaled_acc(to_dev_bf16(x), to_dev_bf16(b), o, 2.0)
     torch.cuda.synchronize()
     assert_values_equal(bits_of(o), want, "fold specials")
+
+
+def test_every_weight_scale_byte_and_code_w4a16_transposed():
+    """The transposed-weight entry point on the same special-code weights,
+    stored [K/2, ldb] with an odd stride (byte loads) and a multiple of 4."""
+    k = 64
+    a = synthetic.grid_bf16((96, k), -8, 8, -5, 931, 0)
+    _, _, b, sfb = _fp4_specials(k=k, seed=3)
+    nan_rows = np.isnan(oracle.e4m3fn_to_f64(sfb[:, 0]))
+    want = np.empty((96, 256), np.uint16)
+    want[:, ~nan_rows] = oracle.gemm_w4a16_exact(a, b[~nan_rows], sfb[~nan_rows], 0.75)
+    want[:, nan_rows] = 0x7FC0
+    for ldb in (257, 260):
+        bt = np.zeros((k // 2, ldb), np.uint8)
+        bt[:, :256] = b.T
+        sfbt = np.zeros((k // 16, ldb), np.uint8)
+        sfbt[:, :256] = sfb.T
+        c = bg.gemm_w4a16_t(to_dev_bf16(a), to_dev_u8(bt), to_dev_u8(sfbt), 256, 0.75)
+        torch.cuda.synchronize()
+        assert_values_equal(bits_of(c), want, f"w4a16_t special codes ldb={ldb}")

@@ -91,3 +91,73 @@ def test_w4a16_equals_fp4_gemm_on_fp4_valued_activations():
     c = bg.gemm_fp4_blockscaled(to_dev_u8(qa), to_dev_u8(one), to_dev_u8(b), to_dev_u8(sfb))
     torch.cuda.synchronize()
     assert_bits_equal(w, bits_of(c), "w4a16 vs fp4")
+
+
+# ---------------------------------------------------------------------------
+# transposed weights with an explicit row stride (gemm_w4a16_t)
+# ---------------------------------------------------------------------------
+
+def _transposed(n, k, ldb, seed, scale_choice=None):
+    """Bt [K/2, ldb] and SFBt [K/16, ldb], pad columns zero-filled (the page's
+    convention), plus the same weights in gemm_w4a16's [N, K/2] layout."""
+    b = synthetic.fp4_packed(n, k, seed, 1)
+    if scale_choice is None:
+        sfb = synthetic.e4m3_uniform(n, k // 16, 2 ** -4, 2 ** 4, seed, 5)
+    else:
+        sfb = synthetic.e4m3_choice(n, k // 16, scale_choice, seed, 5)
+    bt = np.zeros((k // 2, ldb), np.uint8)
+    bt[:, :n] = b.T
+    sfbt = np.zeros((k // 16, ldb), np.uint8)
+    sfbt[:, :n] = sfb.T
+    return b, sfb, bt, sfbt
+
+
+def _run_t(a, bt, sfbt, n, s2):
+    c = bg.gemm_w4a16_t(to_dev_bf16(a), to_dev_u8(bt), to_dev_u8(sfbt), n, s2)
+    torch.cuda.synchronize()
+    return bits_of(c)
+
+
+@pytest.mark.parametrize("ldb", [248192, 248077])
+def test_w4a16_t_lm_head_odd_vocab(ldb):
+    """lm_head-like: N = 248077 (odd), ldb = align_up(N, 128) with zero pad
+    (4-byte column loads) and ldb = N (byte loads); every output against the
+    oracle's transposed-layout definition."""
+    m, n, k = 37, 248077, 512
+    print(f"w4a16_t lm_head m={m} n={n} k={k} ldb={ldb}", flush=True)
+    a = synthetic.normal_bf16((m, k), 1.0, 120, 0)
+    bt = np.zeros((k // 2, ldb), np.uint8)
+    bt[:, :n] = synthetic.fp4_packed(k // 2, 2 * n, 120, 1)
+    sfbt = np.zeros((k // 16, ldb), np.uint8)
+    sfbt[:, :n] = synthetic.e4m3_uniform(k // 16, n, 2 ** -4, 2 ** 4, 120, 5)
+    got = _run_t(a, bt, sfbt, n, S2)
+    ref = oracle.gemm_w4a16_t_ref(a, bt, sfbt, n, S2)
+    sig_b = oracle.rms(oracle.dequant_fp4_t(bt, sfbt, n)) * abs(float(np.float32(S2)))
+    check_close(got, ref, k, oracle.rms(oracle.bf16_to_f64(a)), sig_b, f"w4a16_t lm_head ldb={ldb}")
+
+
+T_SHAPES = [(130, 1001, 256, 1004), (7, 300, 64, 301), (64, 257, 160, 257), (200, 4099, 512, 4224),
+            (1, 1, 16, 1), (33, 130, 48, 133), (300, 520, 224, 520)]
+
+
+@pytest.mark.parametrize("cfg", [-1, 0, 1, 2])
+def test_w4a16_t_exact_and_equal_to_w4a16(cfg, force):
+    """Grid activations and scales in {1, 2}: exact FP32 sums, so every output
+    is unique (bit-exact against the oracle), and with the same tile the
+    transposed entry point equals gemm_w4a16 on the same weights bit for bit."""
+    if cfg >= 0:
+        force(bg.TUNE_W4A16_TILE, cfg)
+    for m, n, k, ldb in T_SHAPES:
+        print(f"w4a16_t cfg={cfg} m={m} n={n} k={k} ldb={ldb}", flush=True)
+        a = synthetic.grid_bf16((m, k), -8, 8, -5, 121, 0)
+        b, sfb, bt, sfbt = _transposed(n, k, ldb, 121, [0x38, 0x40])
+        got = _run_t(a, bt, sfbt, n, 0.75)
+        assert_bits_equal(got, oracle.gemm_w4a16_exact(a, b, sfb, 0.75), f"w4a16_t exact {m}x{n}x{k} ldb={ldb}")
+        if cfg >= 0:
+            assert_bits_equal(got, _run(a, b, sfb, 0.75), f"w4a16_t vs w4a16 cfg {cfg}")
+        # random data within the tolerance
+        ar = synthetic.normal_bf16((m, k), 1.0, 122, 0)
+        b2, sfb2, bt2, sfbt2 = _transposed(n, k, ldb, 122)
+        ref = oracle.gemm_w4a16_t_ref(ar, bt2, sfbt2, n, S2)
+        check_close(_run_t(ar, bt2, sfbt2, n, S2), ref, k, oracle.rms(oracle.bf16_to_f64(ar)),
+                    oracle.rms(oracle.dequant_fp4_t(bt2, sfbt2, n)) * abs(S2), f"w4a16_t {m}x{n}x{k} ldb={ldb}")

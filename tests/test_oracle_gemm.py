@@ -529,3 +529,53 @@ def test_fp4_splitk_planes_sum_and_slices(k, ks):
                                    b[:, lo // 2:hi // 2], sfb[:, lo // 16:hi // 16])
         assert np.array_equal(planes[s], want)
     assert np.array_equal(planes.sum(axis=0), oracle.gemm_fp4_ref(a, sfa, b, sfb))
+
+
+# ---------------------------------------------------------------------------
+# W4A16 with transposed weights (row stride ldb >= N)
+# ---------------------------------------------------------------------------
+
+def test_w4a16_t_brute_force_exact_rationals():
+    """Bytes read straight from the transposed layout by index: byte (k // 2, j)
+    of Bt, low nibble for even k; scale byte (k // 16, j) of SFBt; pad columns
+    j >= N hold junk that must not matter."""
+    tab = _e2m1_table()
+    m, n, k, ldb = 3, 5, 48, 7
+    a = rand_bf16((m, k), 96)
+    bt = synthetic.fp4_packed(k // 2, 2 * ldb, 96, 1)            # [K/2, ldb] bytes
+    sfbt = synthetic.e4m3_uniform(k // 16, ldb, 2 ** -4, 2 ** 4, 96, 5)
+    s2 = 0.0123
+    s2_exact = Fraction(struct.unpack("<f", struct.pack("<f", s2))[0])
+    got = oracle.gemm_w4a16_t_ref(a, bt, sfbt, n, s2)
+    assert got.shape == (m, n)
+    for i in range(m):
+        for j in range(n):
+            dot = Fraction(0)
+            for kk in range(k):
+                byte = int(bt[kk // 2, j])
+                code = byte & 0xF if kk % 2 == 0 else byte >> 4
+                dot += bf16_exact(int(a[i, kk])) * tab[code] * _e4m3_exact(int(sfbt[kk // 16, j]))
+            exact = s2_exact * dot
+            assert abs(Fraction(got[i, j]) - exact) <= abs(exact) * Fraction(2) ** -52
+
+
+def test_w4a16_t_equals_w4a16_on_the_same_weights():
+    """The same weights in both layouts give the same FP64 result: B[j, t] =
+    Bt[t, j] and SFB[j, g] = SFBt[g, j], built with explicit loops."""
+    m, n, k, ldb = 4, 9, 64, 12
+    a = rand_bf16((m, k), 97)
+    bt = synthetic.fp4_packed(k // 2, 2 * ldb, 97, 1)
+    sfbt = synthetic.e4m3_uniform(k // 16, ldb, 2 ** -4, 2 ** 4, 97, 5)
+    b = np.zeros((n, k // 2), np.uint8)
+    sfb = np.zeros((n, k // 16), np.uint8)
+    for j in range(n):
+        for t in range(k // 2):
+            b[j, t] = bt[t, j]
+        for g in range(k // 16):
+            sfb[j, g] = sfbt[g, j]
+    assert np.array_equal(oracle.gemm_w4a16_t_ref(a, bt, sfbt, n, 0.7), oracle.gemm_w4a16_ref(a, b, sfb, 0.7))
+    # the pad columns are ignored
+    bt2, sfbt2 = bt.copy(), sfbt.copy()
+    bt2[:, n:] = 0xFF
+    sfbt2[:, n:] = 0x7F
+    assert np.array_equal(oracle.gemm_w4a16_t_ref(a, bt2, sfbt2, n, 0.7), oracle.gemm_w4a16_t_ref(a, bt, sfbt, n, 0.7))
