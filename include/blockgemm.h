@@ -308,11 +308,12 @@ bg_status gemm_w4a16(const uint16_t* A, const uint8_t* B, const uint8_t* SFB, fl
  * (the vocabulary-sized lm_head).
  *
  * gemm_dense.rs page, doc comments of w4a16_gemm_n128_ldb and
- * w4a16_gemm_n128_m128_bf16_ldb: the transposed weight's row r sits at
- * r * ldb; with N odd (248077) an unpadded stride misaligns 15 of every 16
- * rows for 16-byte loads, so the caller passes ldb = align_up(N, 128) with
- * the pad columns zero-filled. Here any ldb >= N is accepted: ldb % 4 == 0
- * takes 4-byte column loads, any other stride byte loads; neither faults.
+ * w4a16_gemm_n128_m128_bf16_ldb: the transposed weight is addressed through
+ * a row stride; with the odd vocabulary size 248077 as the stride, most rows
+ * start off a 16-byte boundary and 16-byte loads fault, so the page pads the
+ * stride to a multiple of 128 with zero-filled columns. Here any ldb >= N is
+ * accepted: ldb % 4 == 0 takes 4-byte column loads, any other stride byte
+ * loads; neither faults.
  *
  *  A:    [M, K] BF16 activations.
  *  Bt:   [K/2, ldb] bytes: byte (r, n) holds weight row n's E2M1 codes for

@@ -50,7 +50,10 @@ def _want_fp4(a, sfa, b, sfb):
     return oracle.f32_to_bf16(ref.astype(np.float32))
 
 
-def test_every_scale_byte_and_code_fp4():
+@pytest.mark.parametrize("cfg", [-1, 0, 2])
+def test_every_scale_byte_and_code_fp4(cfg, force):
+    if cfg >= 0:
+        force(bg.TUNE_FP4_TILE, cfg)
     a, sfa, b, sfb = _fp4_specials()
     # the construction covers every byte on both sides and every nibble code
     assert set(np.unique(sfa)) == set(range(256)) and set(np.unique(sfb)) == set(range(256))
@@ -62,8 +65,10 @@ def test_every_scale_byte_and_code_fp4():
     assert_values_equal(bits_of(c), want, "fp4 special codes")
 
 
-@pytest.mark.parametrize("ks", [2, 4])
-def test_every_scale_byte_and_code_fp4_splitk(ks):
+@pytest.mark.parametrize("ks,tile", [(2, -1), (4, -1), (4, 0), (2, 1)])
+def test_every_scale_byte_and_code_fp4_splitk(ks, tile, force):
+    if tile >= 0:
+        force(bg.TUNE_FP4_SPLITK_TILE, tile)
     a, sfa, b, sfb = _fp4_specials(k=256, seed=1)
     want = _want_fp4(a, sfa, b, sfb)
     c = bg.gemm_fp4_blockscaled_splitk(to_dev_u8(a), to_dev_u8(sfa), to_dev_u8(b), to_dev_u8(sfb), ks)
@@ -71,11 +76,13 @@ def test_every_scale_byte_and_code_fp4_splitk(ks):
     assert_values_equal(bits_of(c), want, f"fp4 split-K {ks} special codes")
 
 
-@pytest.mark.parametrize("s2", [1.0, 0.0123, -3.0])
-def test_every_weight_scale_byte_and_code_w4a16(s2):
+@pytest.mark.parametrize("s2,cfg", [(1.0, -1), (0.0123, -1), (-3.0, -1), (0.0123, 0), (-3.0, 2)])
+def test_every_weight_scale_byte_and_code_w4a16(s2, cfg, force):
     """Grid activations j * 2^-5 (|j| <= 8) times weights with every scale
     byte: each dot product is t_j * T with 64*T an integer below 2^13, exact
     in FP32; C = bf16(fl32(s2 * acc)), NaN rows where the scale is NaN."""
+    if cfg >= 0:
+        force(bg.TUNE_W4A16_TILE, cfg)
     k = 64
     a = synthetic.grid_bf16((96, k), -8, 8, -5, 930, 0)
     _, _, b, sfb = _fp4_specials(k=k, seed=2)
