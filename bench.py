@@ -60,6 +60,9 @@ def parse():
                    help="only run a plain 1 GiB device copy (counter calibration) and exit")
     p.add_argument("--profile-rows", action="store_true",
                    help="only run every row's call 3 times, untimed (for counter passes), and exit")
+    p.add_argument("--data-ceiling", action="store_true",
+                   help="only time the gate+up dual call on random, constant and zero operands (same "
+                        "kernels, different switching activity) with the engine clock, print JSON and exit")
     return p.parse_args()
 
 
@@ -100,6 +103,10 @@ def main():
 
     if args.profile_rows:
         profile_rows(bg, synthetic, torch, up16, u8, dev)
+        return
+
+    if args.data_ceiling:
+        print(json.dumps(data_ceiling(bg, synthetic, torch, np, up16, dev)), flush=True)
         return
 
     t_gen = time.time()
@@ -327,6 +334,60 @@ def traffic_for_current_kernel():
         return rec.get("traffic_bytes_per_launch")
     except (OSError, ValueError):
         return None
+
+
+def data_ceiling(bg, synthetic, torch, np, up16, dev):
+    """The gate+up dual call (2 x 5120x11008x2048) timed on three operand
+    sets that run the identical instruction stream: the workload's random
+    BF16 values, a constant (every element 1.0, so each MFMA sees the same
+    operands) and all zeros. A GEMM whose time depends on the values it
+    multiplies is limited by power (the engine clock falls with switching
+    activity), not by its schedule. Each set: 5 warm-up calls, then 40 calls
+    in 4 interleaved rounds of 10, while the engine clock is sampled."""
+    x, wg = synthetic.mlp_gate_up()
+    wu = synthetic.normal_bf16((INTER, HID), 0.02, 2, synthetic.TID_B2 + 10)
+    sets = {
+        "random": (up16(x), up16(wg), up16(wu)),
+        "constant_one": tuple(torch.ones(s, dtype=torch.bfloat16, device=dev)
+                              for s in ((M, HID), (INTER, HID), (INTER, HID))),
+        "zero": tuple(torch.zeros(s, dtype=torch.bfloat16, device=dev)
+                      for s in ((M, HID), (INTER, HID), (INTER, HID))),
+    }
+    G = torch.empty((M, INTER), dtype=torch.bfloat16, device=dev)
+    U = torch.empty((M, INTER), dtype=torch.bfloat16, device=dev)
+    flops = 2 * 2.0 * M * INTER * HID
+    stream = torch.cuda.current_stream()
+    times = {k: [] for k in sets}
+    clocks = {}
+    gc.collect()
+    gc.disable()
+    for name, (X, Wg, Wu) in sets.items():
+        for _ in range(5):
+            bg.gemm_bf16_dual(X, Wg, Wu, out0=G, out1=U)
+        torch.cuda.synchronize()
+        clocks[name] = sample_sclk(lambda: bg.gemm_bf16_dual(X, Wg, Wu, out0=G, out1=U), seconds=0.3,
+                                   sync=torch.cuda.synchronize)
+    for r in range(4):
+        for name in (list(sets) if r % 2 == 0 else list(sets)[::-1]):
+            X, Wg, Wu = sets[name]
+            bg.gemm_bf16_dual(X, Wg, Wu, out0=G, out1=U)
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            for _ in range(10):
+                bg.gemm_bf16_dual(X, Wg, Wu, out0=G, out1=U)
+            e.record(stream)
+            torch.cuda.synchronize()
+            times[name].append(s.elapsed_time(e) / 10 * 1e3)
+    gc.enable()
+    out = {"call": "gemm_bf16_dual 2 x 5120x11008x2048 (gate+up)"}
+    for name in sets:
+        us = float(np.median(times[name]))
+        out[name] = {"us": round(us, 1), "tflops": round(flops / us / 1e6, 1),
+                     "frac_bf16_peak": round(flops / us / 1e6 / BF16_PEAK_TFLOPS, 4),
+                     "sclk_mhz_mean": None if clocks[name] is None else clocks[name]["sclk_mhz_mean"]}
+        log(f"data ceiling {name}: {out[name]}")
+    return out
 
 
 def profile_rows(bg, synthetic, torch, up16, u8, dev):
