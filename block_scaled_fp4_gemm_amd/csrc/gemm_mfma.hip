@@ -771,7 +771,7 @@ __device__ __forceinline__ void staged_epilogue(const KParams& p, const f32x16 (
                     if constexpr (NPRE > 0)
                         o = pre[it];   // loaded at kernel start (single pass)
                     else
-                        o = *reinterpret_cast<const u32x4*>(O + off);
+                        o = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(O + off));
                     const uint32_t o4[4] = {o.x, o.y, o.z, o.w};
                     uint32_t r4[4];
 #pragma unroll
@@ -780,7 +780,8 @@ __device__ __forceinline__ void staged_epilogue(const KParams& p, const f32x16 (
                         const float hi = bf16_hi(o4[e]) + sc * bf16_hi(d4[e]);
                         r4[e] = pack_bf16x2(lo, hi);
                     }
-                    *reinterpret_cast<u32x4*>(O + off) = u32x4{r4[0], r4[1], r4[2], r4[3]};
+                    // `out` is streamed once: non-temporal, so it does not displace cached data
+                    __builtin_nontemporal_store(u32x4{r4[0], r4[1], r4[2], r4[3]}, reinterpret_cast<u32x4*>(O + off));
                 } else {
                     for (int e = 0; e < 8 && n + e < N; ++e) {
                         const uint32_t dh = (d4[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
@@ -1220,7 +1221,7 @@ gemm_mfma_direct_kernel(KParams p) {
                     const int row = piece / PCPR, chunk = piece % PCPR;
                     const int m = m0 + row, n = n0 + chunk * 8;
                     if (m < p.M && vec_ok && n + 8 <= p.N)
-                        pre[it] = *reinterpret_cast<const u32x4*>(O + (int64_t)m * p.ldc + n);
+                        pre[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(O + (int64_t)m * p.ldc + n));
                 }
                 // edge tiles skip some prefetch loads: uniform per workgroup
                 return vec_ok && m0 + BM <= p.M && n0 + BN <= p.N;
