@@ -423,6 +423,11 @@ def profile_rows(bg, synthetic, torch, up16, u8, dev):
     DA, DSA, DB, DSB = u8(da), u8(dsa), u8(db), u8(dsb)
     WS = torch.empty(8 * 128 * 7168, dtype=torch.float32, device=dev)
     calls.append(("fp4_decode_k8", lambda: bg.gemm_fp4_blockscaled_splitk(DA, DSA, DB, DSB, 8, workspace=WS)))
+    ea, esa, eb, esb = synthetic.fp4_decode(m=128, n=4096, k=7168)
+    EA, ESA, EB, ESB = u8(ea), u8(esa), u8(eb), u8(esb)
+    WS2 = torch.empty(12 * 128 * 4096, dtype=torch.float32, device=dev)
+    calls.append(("fp4_decode_4096_k12",
+                  lambda: bg.gemm_fp4_blockscaled_splitk(EA, ESA, EB, ESB, 12, workspace=WS2)))
     wa, wb, wsb, s2 = synthetic.w4a16_gemm()
     WA, WB, WSB = up16(wa), u8(wb), u8(wsb)
     calls.append(("w4a16", lambda: bg.gemm_w4a16(WA, WB, WSB, s2)))
