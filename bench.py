@@ -514,6 +514,25 @@ def measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream, oracle_seconds
     dense_row("attn_qo_5120x2048x2048", 5120, 2048, 2048, a, b)
     a, b = synthetic.attn_proj(n=512)
     dense_row("attn_kv_5120x512x2048", 5120, 512, 2048, a, b)
+
+    def streamk_row(name, m, n, k, a, b):
+        """The same product through the stream-K entry point (its workspace
+        allocated once, outside the timed calls)."""
+        A, B = up16(a), up16(b)
+        C = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        need = bg.gemm_bf16_streamk_workspace(m, n, k)
+        WS = torch.empty(need, dtype=torch.uint8, device=dev)
+        w, c = timed(lambda: bg.gemm_bf16_streamk(A, B, workspace=WS, out=C))
+        fl = 2.0 * m * n * k
+        rows[name] = with_spread({"shape": [m, n, k], "us_warm": round(w, 2), "us_cold": round(c, 2),
+                                  "tflops_warm": round(fl / w / 1e6, 1), "tflops_cold": round(fl / c / 1e6, 1),
+                                  "frac_bf16_peak_warm": round(fl / w / 1e6 / BF16_PEAK_TFLOPS, 4),
+                                  "workspace_bytes": need})
+        log(name, rows[name])
+
+    streamk_row("attn_kv_5120x512x2048_streamk", 5120, 512, 2048, a, b)
+    a, b = synthetic.attn_proj(n=2048)
+    streamk_row("attn_qo_5120x2048x2048_streamk", 5120, 2048, 2048, a, b)
     a, b = synthetic.mlp_gate_up()
     dense_row("mlp_gate_up_5120x11008x2048", 5120, 11008, 2048, a, b)
     # both projections in one launch (the step's form)
@@ -546,7 +565,9 @@ def measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream, oracle_seconds
     rows["mlp_down_5120x2048x11008_k8"].update(oracle_timing(
         lambda r0, r1: oracle.splitk_reduce(oracle.gemm_splitk_planes_ref(h[r0:r1], wd, 8).astype(np.float32)),
         5120, 16, oracle_seconds))
-    del H, WD, D, WS
+    del D, WS
+    streamk_row("mlp_down_5120x2048x11008_streamk", 5120, 2048, 11008, h, wd)
+    del H, WD
 
     out, x, bl, scale = synthetic.lora_fold()
     O, X, BL = up16(out), up16(x), up16(bl)

@@ -34,6 +34,9 @@ _SIGS = {
     "gemm_bf16_scaled_acc": [_p, _p, _p, _u32, _u32, _u32, _f32, _p],
     "gemm_bf16_splitk": [_p, _p, _p, _p, _sz, _u32, _u32, _u32, _u32, _p],
     "gemm_bf16_splitk_noalloc": [_p, _p, _p, _u32, _u32, _u32, _u32, _p],
+    "gemm_bf16_streamk": [_p, _p, _p, _p, _sz, _u32, _u32, _u32, _p],
+    "gemm_bf16_streamk_workspace": [_u32, _u32, _u32, _p],
+    "bg_streamk_plan": [_u32, _u32, _u32, _p, _sz, _p],
     "gemm_bf16_ordered": [_p, _p, _p, _u32, _u32, _u32, _p],
     "gemm_bf16_ordered_f32": [_p, _p, _p, _u32, _u32, _u32, _p],
     "gemm_fp4_blockscaled": [_p, _p, _p, _p, _p, _u32, _u32, _u32, _p],
@@ -297,6 +300,45 @@ def gemm_bf16_splitk_noalloc(a: torch.Tensor, b: torch.Tensor, k_splits: int, ou
     return out
 
 
+def gemm_bf16_streamk_workspace(m: int, n: int, k: int) -> int:
+    """Bytes of workspace gemm_bf16_streamk needs for (M, N, K) on the current device."""
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.gemm_bf16_streamk_workspace(m, n, k, ctypes.byref(nbytes)), "gemm_bf16_streamk_workspace")
+    return int(nbytes.value)
+
+
+def gemm_bf16_streamk(a: torch.Tensor, b: torch.Tensor, workspace: torch.Tensor | None = None,
+                      out: torch.Tensor | None = None, stream=None):
+    """C = bf16(A @ B^T) with the stream-K schedule. `workspace` is a byte
+    tensor of at least gemm_bf16_streamk_workspace(M, N, K) bytes (allocated
+    if None); it needs no initialization."""
+    m, k = _dims(_bits16(a, "A"), 2, "A")
+    n, _ = _dims(_bits16(b, "B"), 2, "B")
+    _shape(b, (n, k), "B")
+    out = _out16(out, (m, n), a)
+    _on_device(a, b, out, workspace)
+    if workspace is None:
+        need = gemm_bf16_streamk_workspace(m, n, k) if m and n else 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=a.device) if need else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.gemm_bf16_streamk(_ptr(a), _ptr(b), _ptr(out), _ptr(workspace), ws_bytes, m, n, k,
+                                 _stream(stream)), "gemm_bf16_streamk")
+    return out
+
+
+def streamk_plan(tiles: int, steps: int, wgs_per_xcd: int):
+    """The stream-K plan (host only): an int32 array of rows (workgroup, grid
+    tile, first step, end step, partial, lowest source or -1), one per piece
+    of work, in the order the kernel runs them."""
+    import numpy as np
+    count = ctypes.c_size_t(0)
+    _check(lib.bg_streamk_plan(tiles, steps, wgs_per_xcd, None, 0, ctypes.byref(count)), "bg_streamk_plan")
+    rows = np.zeros((count.value, 6), np.int32)
+    _check(lib.bg_streamk_plan(tiles, steps, wgs_per_xcd, rows.ctypes.data if count.value else None,
+                               count.value, ctypes.byref(count)), "bg_streamk_plan")
+    return rows
+
+
 def gemm_bf16_ordered(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None,
                       stream=None):
     """Strict k = 0..K-1 FP32 recurrence per output (no FMA), BF16 out."""
@@ -429,7 +471,8 @@ def bf16_scaled_add(out: torch.Tensor, delta: torch.Tensor, scale: float, stream
 # Tuning overrides and the tile-order helper (host only)
 # ---------------------------------------------------------------------------
 
-TUNE_TILE, TUNE_COLSPLIT, TUNE_ORDERED, TUNE_FP4_TILE, TUNE_FP4_SPLITK_TILE, TUNE_W4A16_TILE = range(6)
+TUNE_TILE, TUNE_COLSPLIT, TUNE_ORDERED, TUNE_FP4_TILE, TUNE_FP4_SPLITK_TILE, TUNE_W4A16_TILE, \
+    TUNE_STREAMK_TILE = range(7)
 
 
 def tune_set(key: int, value: int) -> None:

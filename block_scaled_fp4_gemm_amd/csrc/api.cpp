@@ -4,9 +4,12 @@
 // is reachable without a GPU; the device check runs only once the arguments
 // are known to be good. Nothing is enqueued unless every check passes.
 #include <atomic>
+#include <chrono>
 #include <cstring>
+#include <random>
 
 #include "bg_internal.hpp"
+#include "streamk_plan.hpp"
 #include "tile_order.hpp"
 
 namespace {
@@ -69,7 +72,20 @@ bg_status check_device() {
 
 bg_status launched(hipError_t e) { return e == hipSuccess ? BG_OK : BG_ERR_LAUNCH; }
 
-std::atomic<int> g_tune[BG_TUNE_COUNT] = {{-1}, {-1}, {-1}, {-1}, {-1}, {-1}};
+std::atomic<int> g_tune[BG_TUNE_COUNT] = {{-1}, {-1}, {-1}, {-1}, {-1}, {-1}, {-1}};
+
+// Stream-K call numbers: a random 64-bit start per process, then one per
+// call, so a flag left in reused memory by another call or process matches
+// the current call's number only by a 2^-64 chance.
+uint64_t next_epoch() {
+    static std::atomic<uint64_t> counter{[] {
+        std::random_device rd;
+        const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+        return (((uint64_t)rd() << 32) ^ (uint64_t)rd() ^ (t * 0x9E3779B97F4A7C15ull)) | 1u;
+    }()};
+    uint64_t e = counter.fetch_add(1, std::memory_order_relaxed);
+    return e != 0 ? e : counter.fetch_add(1, std::memory_order_relaxed);
+}
 
 // Common checks of a dense BF16 problem A[M,K], B[N,K] -> out[M,N] of
 // `out_elem` bytes per element.
@@ -152,7 +168,7 @@ const char* bg_status_string(bg_status s) {
         case BG_ERR_NULL: return "a required pointer is NULL";
         case BG_ERR_SHAPE: return "invalid dimensions for this operation";
         case BG_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
-        case BG_ERR_WORKSPACE: return "split-K workspace missing or too small";
+        case BG_ERR_WORKSPACE: return "workspace (or output rows) missing or too small";
         case BG_ERR_ALIAS: return "an output overlaps an input";
         case BG_ERR_DEVICE: return "no current HIP device, or it is not gfx950";
         case BG_ERR_LAUNCH: return "kernel launch failed";
@@ -275,6 +291,63 @@ bg_status gemm_bf16_splitk_noalloc(const uint16_t* A, const uint16_t* B, uint16_
     hipError_t e = bg::launch_dense(p, bg::EPI_STORE_F32, st);
     if (e != hipSuccess) return BG_ERR_LAUNCH;
     return launched(bg::launch_splitk_reduce(static_cast<const float*>(ws), C, M, N, k_splits, st));
+}
+
+bg_status gemm_bf16_streamk_workspace(uint32_t M, uint32_t N, uint32_t K, size_t* bytes) {
+    if (bytes == nullptr) return BG_ERR_NULL;
+    if (!dims_ok(M, N, K)) return BG_ERR_SHAPE;
+    uint32_t cus = 0;
+    bg_status s = check_device(&cus);
+    if (s != BG_OK) return s;
+    bg::streamk_choose(M, N, K, cus, bg::tune(BG_TUNE_STREAMK_TILE), bytes);
+    return BG_OK;
+}
+
+bg_status gemm_bf16_streamk(const uint16_t* A, const uint16_t* B, uint16_t* C, void* workspace,
+                            size_t workspace_bytes, uint32_t M, uint32_t N, uint32_t K, void* stream) {
+    bg_status s = check_dense(A, B, C, M, N, K, 2);
+    if (s != BG_OK || M == 0 || N == 0) return s;
+    const bool sk = bg::streamk_applies(M, N, K);
+    if (sk && workspace == nullptr) return BG_ERR_WORKSPACE;
+    if (sk && misaligned(workspace, 1)) return BG_ERR_ALIGN;
+    uint32_t cus = 0;
+    if ((s = check_device(&cus)) != BG_OK) return s;
+    bg::DenseProblem p{A, B, C, M, N, K, K, K, N, K, 1, 0.0f, cus};
+    if (!sk) return launched(bg::launch_dense(p, bg::EPI_STORE_BF16, (hipStream_t)stream));
+    size_t need = 0;
+    const int cfg = bg::streamk_choose(M, N, K, cus, bg::tune(BG_TUNE_STREAMK_TILE), &need);
+    if (workspace_bytes < need) return BG_ERR_WORKSPACE;
+    const Range rw = range_of(workspace, need);
+    if (overlap(rw, range_of(A, (uint64_t)M * K * 2)) || overlap(rw, range_of(B, (uint64_t)N * K * 2)) ||
+        overlap(rw, range_of(C, (uint64_t)M * N * 2)))
+        return BG_ERR_ALIAS;
+    return launched(bg::launch_streamk(p, workspace, cfg, next_epoch(), (hipStream_t)stream));
+}
+
+bg_status bg_streamk_plan(uint32_t tiles, uint32_t steps, uint32_t wgs_per_xcd, int32_t* rows,
+                          size_t max_rows, size_t* n_rows) {
+    if (n_rows == nullptr) return BG_ERR_NULL;
+    if (tiles >= (1u << 30) || steps >= (1u << 30) || wgs_per_xcd == 0 || wgs_per_xcd > 4096 ||
+        (uint64_t)(tiles / bg::SK_XCDS + 1) * steps >= (uint64_t(1) << 30))
+        return BG_ERR_SHAPE;
+    size_t n = 0;
+    for (uint32_t b = 0; b < bg::SK_XCDS * wgs_per_xcd; ++b) {
+        bg::SkWorkgroup wg;
+        wg.init((int)tiles, (int)steps, (int)wgs_per_xcd, (int)(b % bg::SK_XCDS), (int)(b / bg::SK_XCDS));
+        for (int q = 0; q < wg.count(); ++q, ++n) {
+            if (rows == nullptr || n >= max_rows) continue;
+            const bg::SkPiece pc = wg.piece(q);
+            int32_t* r = rows + 6 * n;
+            r[0] = (int32_t)b;
+            r[1] = wg.t0 + pc.tile;
+            r[2] = pc.s_begin;
+            r[3] = pc.s_end;
+            r[4] = pc.partial;
+            r[5] = pc.src_first;
+        }
+    }
+    *n_rows = n;
+    return rows != nullptr && n > max_rows ? BG_ERR_WORKSPACE : BG_OK;
 }
 
 bg_status gemm_bf16_ordered(const uint16_t* A, const uint16_t* B, uint16_t* C, uint32_t M,

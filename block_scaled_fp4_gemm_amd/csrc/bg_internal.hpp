@@ -71,6 +71,10 @@ hipError_t launch_dense(const DenseProblem& p, Epilogue epi, hipStream_t stream)
 // same shape, in one launch when the direct kernels apply.
 hipError_t launch_dense_dual(const DenseProblem& p, const uint16_t* B1, uint16_t* C1, hipStream_t stream);
 hipError_t launch_fp4(const Fp4Problem& p, hipStream_t stream);
+// Stream-K (gemm_bf16_streamk; the plan and the tile choice are in
+// streamk_plan.hpp): p.C is the BF16 output, ws the workspace of
+// streamk_choose's size for configuration cfg.
+hipError_t launch_streamk(const DenseProblem& p, void* ws, int cfg, uint64_t epoch, hipStream_t stream);
 hipError_t launch_scales_from_blocked(const uint8_t* src, uint8_t* dst, uint32_t rows, uint32_t k_groups,
                                       uint32_t batch, hipStream_t stream);
 hipError_t launch_w4a16(const W4a16Problem& p, hipStream_t stream);

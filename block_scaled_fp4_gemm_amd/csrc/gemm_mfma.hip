@@ -29,6 +29,7 @@
 #include <type_traits>
 
 #include "bg_internal.hpp"
+#include "streamk_plan.hpp"
 #include "tile_order.hpp"
 
 #pragma clang fp contract(off)
@@ -1233,6 +1234,221 @@ gemm_mfma_direct_kernel(KParams p) {
         p, acc, reinterpret_cast<uint8_t*>(smem), m0, n0, wm, wn, lane, tid, split, pre, Cop);
 }
 
+// ---------------------------------------------------------------------------
+// Stream-K: K steps dealt out evenly over one workgroup per CU slot instead
+// of whole tiles (streamk_plan.hpp has the plan). Each piece of a workgroup's
+// range runs the direct main loop over its K steps. An unfinished tile's
+// piece is written to the workgroup's FP32 partial slot and published with
+// the call's epoch in its flag; the workgroup that runs a tile's last step
+// adds the partials of the lower workgroups that ran its earlier steps
+// (fixed order, so repeated calls give identical bits) and stores BF16.
+// ---------------------------------------------------------------------------
+
+struct SkArgs {
+    float* ws;            // partial slots: one BM x BN FP32 tile per workgroup
+    uint64_t* flags;      // one per workgroup: the epoch of its last published partial
+    uint64_t epoch;       // unique per call
+    int steps;            // K steps per tile
+    int wgs_per_xcd;      // workgroups per XCD (the grid is 8 times this)
+    int tiles;
+};
+
+// polls of a flag before a wait gives up (about a second): the output of a
+// tile whose partials never arrive is NaN instead of a hang
+constexpr int kSkSpinLimit = 1 << 20;
+
+// Owner epilogue of a tile whose earlier K steps other workgroups ran: the
+// FP32 accumulator tile is staged in LDS (in passes of whole rows when it
+// does not fit), and the threads streaming each row add the sources'
+// row-major FP32 partials to it, nearest source first, then round to BF16
+// and store. `src` is the nearest source's slot, the others lie
+// `src_stride` floats apart below it.
+template <int BM, int BN, int WM, int WN, int FM, int FN, int NT, int CAP>
+__device__ __forceinline__ void sk_fixup_epilogue(const KParams& p, const f32x16 (&acc)[FM][FN], uint8_t* lds,
+                                                  int m0, int n0, int wm, int wn, int lane, int tid,
+                                                  const float* src, int64_t src_stride, int nsrc, bool late) {
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int ROWB = BN * 4;
+    constexpr int CPR16 = ROWB / 16;   // four FP32 values per chunk
+    constexpr int ROWS_FIT = CAP / ROWB;
+    constexpr int RP = (ROWS_FIT >= BM) ? BM : (ROWS_FIT / 32) * 32;
+    static_assert(RP >= 32, "a pass holds at least one 32-row MFMA block");
+    constexpr int NPASS = (BM + RP - 1) / RP;
+    const int M = p.M, N = p.N, ldc = p.ldc;
+    uint16_t* C = reinterpret_cast<uint16_t*>(p.C);
+    const bool vec_ok = (N % 4) == 0 && (ldc % 4) == 0;
+    auto slot = [](int row, int chunk) { return row * ROWB + (((chunk + row) % CPR16) << 4); };
+
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int blk = wm * TM + i * 32;
+            if (blk < pass * RP || blk >= (pass + 1) * RP) continue;
+            const int row = blk + (lane & 31) - pass * RP;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int n_local = wn * TN + j * 32 + g * 8 + (lane >> 5) * 4;
+                    *reinterpret_cast<f32x4*>(lds + slot(row, n_local >> 2)) =
+                        f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                }
+        }
+        lds_barrier();
+        // groups of GRP chunks per thread: the group's chunks, then one
+        // uniform loop over the sources (no loop inside lane-dependent
+        // control flow); a partial slot holds the whole tile, so its reads
+        // need no bound
+        const int lim = min(RP, BM - pass * RP) * CPR16;
+        constexpr int ITER = (RP * CPR16 + NT - 1) / NT;
+        constexpr int GRP = ITER < 4 ? ITER : 4;
+        static_assert(ITER % GRP == 0, "whole groups");
+        const float* srcp0 = src + (int64_t)pass * RP * BN;
+#pragma unroll
+        for (int g0 = 0; g0 < ITER; g0 += GRP) {
+            f32x4 v[GRP];
+#pragma unroll
+            for (int g = 0; g < GRP; ++g) {
+                const int qi = tid + (g0 + g) * NT;
+                if (qi < lim) v[g] = *reinterpret_cast<const f32x4*>(lds + slot(qi / CPR16, qi % CPR16));
+            }
+            const float* srcp = srcp0;
+            for (int k = 0; k < nsrc; ++k, srcp -= src_stride) {
+#pragma unroll
+                for (int g = 0; g < GRP; ++g) {
+                    const int qi = tid + (g0 + g) * NT;
+                    if (qi < lim) {
+                        const f32x4 w =
+                            *reinterpret_cast<const f32x4*>(srcp + (qi / CPR16) * BN + (qi % CPR16) * 4);
+                        v[g][0] += w[0];
+                        v[g][1] += w[1];
+                        v[g][2] += w[2];
+                        v[g][3] += w[3];
+                    }
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < GRP; ++g) {
+                const int qi = tid + (g0 + g) * NT;
+                const int row = qi / CPR16, chunk = qi % CPR16;
+                const int m = m0 + pass * RP + row;
+                const int n = n0 + chunk * 4;
+                if (qi >= lim || m >= M || n >= N) continue;
+                const f32x4 r = late ? f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                                             __builtin_nanf("")}
+                                     : v[g];
+                const int64_t off = (int64_t)m * ldc + n;
+                const uint32_t lo = pack_bf16x2(r[0], r[1]), hi = pack_bf16x2(r[2], r[3]);
+                if (vec_ok && n + 4 <= N) {
+                    *reinterpret_cast<u32x2*>(C + off) = u32x2{lo, hi};
+                } else {
+                    const uint32_t e2[2] = {lo, hi};
+                    for (int e = 0; e < 4 && n + e < N; ++e) C[off + e] = (uint16_t)(e2[e >> 1] >> ((e & 1) * 16));
+                }
+            }
+        }
+    }
+}
+
+template <int BM, int BN, int BKS, int WM, int WN, int STAGES>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_streamk_kernel(KParams p, SkArgs q) {
+    constexpr int NT = WM * WN * 64;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    static_assert(FM * 32 * WM == BM && FN * 32 * WN == BN, "bad tile split");
+    constexpr int STAGE = (BM + BN) * BKS;
+    constexpr int SMEM_ELEMS = STAGES * STAGE;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM_ELEMS];
+    __shared__ int s_late;
+
+    const int tid0 = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int b = blockIdx.x;
+    const int x = b % SK_XCDS, u = b / SK_XCDS;
+
+    SkWorkgroup wg;
+    wg.init(q.tiles, q.steps, q.wgs_per_xcd, x, u);
+    const int pieces = wg.count();
+    // a partial slot is one BM x BN FP32 tile, row-major
+    KParams ps = p;
+    ps.M = BM;
+    ps.N = BN;
+    ps.ldc = BN;
+
+    for (int pi = 0; pi < pieces; ++pi) {
+        // the thread index plus an opaque (uniform) zero: otherwise the
+        // compiler hoists every lane-dependent LDS and global offset of the
+        // main loop and the epilogues out of the piece loop and keeps them
+        // all live at once (up to 256 VGPRs with scratch spills)
+        int opaque_zero = 0;
+        asm volatile("" : "+s"(opaque_zero));
+        const int tid = tid0 + opaque_zero;
+        const int lane = tid & 63;
+        const SkPiece pc = wg.piece(pi);
+        int tm, tn;
+        grouped_tile(wg.t0 + pc.tile, p.tiles_m, p.tiles_n, tm, tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+        const int kb = sk_kpos(pc.s_begin, p.K, q.steps), ke = sk_kpos(pc.s_end, p.K, q.steps);
+
+        f32x16 acc[FM][FN];
+        zero_acc(acc);
+        if (pi > 0) lds_barrier();   // the previous piece's epilogue is done with LDS
+        direct_mainloop<BM, BN, BKS, WM, WN, STAGES, 0>(p, p.B, smem, m0, n0, kb, ke, wave, lane, tid, acc,
+                                                        []() { return true; });
+
+        if (pc.partial) {
+            staged_epilogue<EPI_STORE_F32, BM, BN, WM, WN, FM, FN, NT, SMEM_ELEMS * 2>(
+                ps, acc, reinterpret_cast<uint8_t*>(smem), 0, 0, wm, wn, lane, tid, 0, nullptr,
+                q.ws + (int64_t)b * (BM * BN));
+            // Each wave waits until its stores are performed; after the
+            // barrier one device-scope release (one L2 writeback for the
+            // workgroup instead of one per wave: 60 -> 35 us on 5120 x 512 x
+            // 2048) publishes the whole tile with the flag.
+            wait_vmcnt<0>();
+            __syncthreads();
+            if (tid == 0) __hip_atomic_store(q.flags + b, q.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        } else if (pc.src_first >= 0) {
+            if (wave == 0) {
+                // the whole wave polls (one request per poll) and takes the
+                // loaded value from lane 0, so the loop is uniform
+                int late = 0;
+                for (int su = pc.src_first; su < u; ++su) {
+                    const uint64_t* f = q.flags + su * SK_XCDS + x;
+                    for (int polls = 0;; ++polls) {
+                        const uint64_t v = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+                        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+                        if ((((uint64_t)hi << 32) | lo) == q.epoch) break;
+                        if (polls >= kSkSpinLimit) {
+                            late = 1;
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(2);
+                    }
+                }
+                s_late = late;
+                // one device-scope acquire for the workgroup (the CU's L1 and
+                // the XCD's L2 are shared by its waves), ordered before the
+                // other waves' reads by the barrier
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            }
+            __syncthreads();
+            const int late = s_late;
+            sk_fixup_epilogue<BM, BN, WM, WN, FM, FN, NT, SMEM_ELEMS * 2>(
+                p, acc, reinterpret_cast<uint8_t*>(smem), m0, n0, wm, wn, lane, tid,
+                q.ws + (int64_t)((u - 1) * SK_XCDS + x) * (BM * BN), (int64_t)SK_XCDS * BM * BN,
+                u - pc.src_first, late != 0);
+        } else {
+            staged_epilogue<EPI_STORE_BF16, BM, BN, WM, WN, FM, FN, NT, SMEM_ELEMS * 2>(
+                p, acc, reinterpret_cast<uint8_t*>(smem), m0, n0, wm, wn, lane, tid, 0, nullptr, p.C);
+        }
+    }
+}
+
 template <int BM, int BN, int WM, int WN, int EPI, int SRC, int RSETS = 2>
 hipError_t launch_cfg(const KParams& kp, int splits, hipStream_t stream, int batch = 1) {
     KParams q = kp;
@@ -1428,6 +1644,21 @@ hipError_t launch_dense_vec(const KParams& kp, int splits, hipStream_t stream) {
     return launch_tile_cfg<EPI>(right, splits, sch.cfg2, stream);
 }
 
+template <int BM, int BN, int BKS, int WM, int WN, int STAGES>
+hipError_t launch_sk(const KParams& kp, SkArgs q, hipStream_t stream) {
+    KParams p = kp;
+    p.tiles_m = (kp.M + BM - 1) / BM;
+    p.tiles_n = (kp.N + BN - 1) / BN;
+    p.dual_tiles_n = 0;
+    q.tiles = p.tiles_m * p.tiles_n;
+    q.steps = (kp.K + 63) / 64;
+    const int grid = SK_XCDS * q.wgs_per_xcd;
+    q.flags = reinterpret_cast<uint64_t*>(q.ws + (int64_t)grid * BM * BN);
+    hipLaunchKernelGGL((gemm_streamk_kernel<BM, BN, BKS, WM, WN, STAGES>), dim3((unsigned)grid),
+                       dim3(WM * WN * 64), 0, stream, p, q);
+    return hipGetLastError();
+}
+
 template <int EPI, int SRC>
 hipError_t launch_dense_src(const KParams& kp, int splits, hipStream_t stream) {
     if constexpr (SRC == SRC_BF16_VEC) return launch_dense_vec<EPI>(kp, splits, stream);
@@ -1470,6 +1701,27 @@ hipError_t launch_dense(const DenseProblem& p, Epilogue epi, hipStream_t stream)
             break;
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_streamk(const DenseProblem& p, void* ws, int cfg, uint64_t epoch, hipStream_t stream) {
+    KParams kp{};
+    kp.A = p.A;
+    kp.B = p.B;
+    kp.C = p.C;
+    kp.M = (int)p.M;
+    kp.N = (int)p.N;
+    kp.K = (int)p.K;
+    kp.lda = kp.ldb = (int)p.K;
+    kp.ldc = (int)p.N;
+    kp.k_chunk = (int)p.K;
+    kp.cus = p.cus > 0 ? (int)p.cus : 256;
+    SkArgs q{};
+    q.ws = static_cast<float*>(ws);
+    q.epoch = epoch;
+    q.wgs_per_xcd = sk_wgs_per_xcd((uint32_t)kp.cus);
+    //                                       BM   BN  BK WM WN ST
+    if (cfg == 10) return launch_sk<256, 128, 64, 4, 2, 3>(kp, q, stream);
+    return launch_sk<128, 128, 64, 2, 2, 3>(kp, q, stream);   // 23
 }
 
 // Two products of one A: the second problem's column tiles follow the first's

@@ -10,7 +10,8 @@
  *    A [M, K] activations, B [N, K] weights in HuggingFace layout, C [M, N]).
  *  - BF16 values travel as their raw 16-bit patterns (uint16_t).
  *  - Every data pointer is a DEVICE pointer on the current HIP device. The
- *    caller allocates and owns every buffer (including the split-K workspace);
+ *    caller allocates and owns every buffer (including the split-K and
+ *    stream-K workspaces);
  *    the library never allocates, frees or retains device memory and never
  *    synchronizes. Buffers must stay alive until the enqueued work finishes.
  *  - `stream` is a hipStream_t passed as void*; NULL means the null stream.
@@ -47,7 +48,7 @@ typedef enum bg_status {
     BG_ERR_NULL = 1,      /* a required pointer is NULL                         */
     BG_ERR_SHAPE = 2,     /* dimensions invalid for this entry point            */
     BG_ERR_ALIGN = 3,     /* a base pointer is not 16-byte aligned              */
-    BG_ERR_WORKSPACE = 4, /* split-K workspace missing or too small             */
+    BG_ERR_WORKSPACE = 4, /* workspace (or output rows) missing or too small    */
     BG_ERR_ALIAS = 5,     /* an output overlaps an input                        */
     BG_ERR_DEVICE = 6,    /* no current HIP device, or it is not gfx950         */
     BG_ERR_LAUNCH = 7     /* the HIP runtime rejected a kernel launch           */
@@ -176,6 +177,66 @@ size_t gemm_bf16_splitk_workspace_bytes(uint32_t M, uint32_t N, uint32_t k_split
 bg_status gemm_bf16_splitk_noalloc(const uint16_t* A, const uint16_t* B, uint16_t* C,
                                    uint32_t M, uint32_t N, uint32_t K, uint32_t k_splits,
                                    void* stream);
+
+/*
+ * gemm_bf16_streamk: C = bf16(A * B^T), FP32 accumulation, computed with a
+ * stream-K schedule for problems whose tiles do not fill the compute units in
+ * whole rounds (5120 x 512 x 2048: 160 tiles of 128 x 128 on 256 CUs).
+ *
+ * Prior art: the kernelbot NVFP4 GEMM page's persistent kernel (one program
+ * per SM walking the tiles in a grouped order) and the gemm_dense.rs page's
+ * dense_gemm_splitk (FP32 partial sums over K ranges combined into BF16).
+ * Here one workgroup per compute unit takes an equal share of the problem's
+ * (tile, 64-wide K step) pairs: the 8 XCDs each take a contiguous share of
+ * the tiles in the grouped order, and the workgroups of an XCD split its
+ * steps evenly, so a tile's steps may be spread over neighbouring workgroups.
+ * A workgroup that runs the first steps of a tile without its last writes
+ * the FP32 partial sum of its steps to its workspace slot; the workgroup that
+ * runs the tile's last step adds those partials to its own sum in a fixed
+ * order and stores the BF16 tile. The plan depends only on (M, N, K), the
+ * tile configuration and the device's compute-unit count, so repeated calls
+ * return identical bits. The FP32 sum is split differently from gemm_bf16's,
+ * so the two agree to FP32 rounding, not bit for bit (exactly where every
+ * partial sum is exact).
+ *
+ *  A: [M, K] BF16.  B: [N, K] BF16.  C: [M, N] BF16, written.
+ *  workspace: device buffer of at least gemm_bf16_streamk_workspace(M, N, K)
+ *             bytes (BG_ERR_WORKSPACE otherwise), 16-byte aligned, not
+ *             overlapping A, B or C. It needs no initialization: the call
+ *             marks each partial it publishes with a number unique to the
+ *             call. Calls that may run concurrently need separate workspaces.
+ *  K == 0, K not a multiple of 8, or K >= 2^31 / 640 (beyond the kernel's
+ *  32-bit operand offsets): the data-parallel kernel of gemm_bf16 computes C
+ *  (the same bits gemm_bf16 returns) and the workspace is unused (it may be
+ *  NULL); otherwise a NULL workspace is BG_ERR_WORKSPACE.
+ *  Other rules as gemm_bf16. The tile configuration is chosen from the shape
+ *  (bg_tune_set(BG_TUNE_STREAMK_TILE, ...) overrides it); the workspace size
+ *  depends on it, so query the size after any override.
+ */
+bg_status gemm_bf16_streamk(const uint16_t* A, const uint16_t* B, uint16_t* C,
+                            void* workspace, size_t workspace_bytes,
+                            uint32_t M, uint32_t N, uint32_t K, void* stream);
+
+/* Bytes of workspace gemm_bf16_streamk needs for (M, N, K) on the current
+ * device (one partial tile and one 8-byte flag per workgroup, one workgroup
+ * per compute unit), in *bytes. BG_ERR_DEVICE without a gfx950 device. */
+bg_status gemm_bf16_streamk_workspace(uint32_t M, uint32_t N, uint32_t K, size_t* bytes);
+
+/*
+ * bg_streamk_plan: the stream-K plan as the kernel computes it (the same host
+ * and device code), for `tiles` output tiles of `steps` K steps each and
+ * `wgs_per_xcd` workgroups on each of the 8 XCDs (workgroup b = u * 8 + x
+ * runs on XCD x). Writes one row of 6 int32 per piece of work, workgroups in
+ * ascending b, each workgroup's pieces in the order it runs them:
+ *   b, grid tile index (grouped order), first step, end step (within the
+ *   tile), 1 if the piece is published as a partial else 0, and for a tile
+ *   whose earlier steps other workgroups ran, the lowest such workgroup's u
+ *   (the sources are u' = that .. u-1 on the same XCD), else -1.
+ * *n_rows receives the number of pieces; rows may be NULL to count only, else
+ * it holds max_rows rows (BG_ERR_WORKSPACE if fewer than needed). Host only.
+ */
+bg_status bg_streamk_plan(uint32_t tiles, uint32_t steps, uint32_t wgs_per_xcd, int32_t* rows,
+                          size_t max_rows, size_t* n_rows);
 
 /*
  * gemm_bf16_ordered: order-preserving GEMM for router logits.
@@ -360,6 +421,8 @@ const char* bg_status_string(bg_status status);
  *  BG_TUNE_FP4_TILE:   tile of gemm_fp4_blockscaled(_batched)
  *  BG_TUNE_FP4_SPLITK_TILE: tile of gemm_fp4_blockscaled_splitk's planes
  *  BG_TUNE_W4A16_TILE: tile of gemm_w4a16
+ *  BG_TUNE_STREAMK_TILE: tile of gemm_bf16_streamk (23: 128 x 128, 10: 256 x 128;
+ *                      other values select 128 x 128)
  * Returns BG_ERR_SHAPE for an unknown key or v < -1; an index past a table
  * selects that table's default entry.
  */
@@ -370,7 +433,8 @@ typedef enum bg_tune_key {
     BG_TUNE_FP4_TILE = 3,
     BG_TUNE_FP4_SPLITK_TILE = 4,
     BG_TUNE_W4A16_TILE = 5,
-    BG_TUNE_COUNT = 6
+    BG_TUNE_STREAMK_TILE = 6,
+    BG_TUNE_COUNT = 7
 } bg_tune_key;
 
 bg_status bg_tune_set(int key, int value);

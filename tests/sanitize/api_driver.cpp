@@ -9,8 +9,11 @@
 #include <vector>
 
 #include "../../block_scaled_fp4_gemm_amd/csrc/bg_internal.hpp"
+#include "../../block_scaled_fp4_gemm_amd/csrc/streamk_plan.hpp"
 
 static int g_dev = 0;
+static int g_sk_cfg = -1;
+static size_t g_sk_need = 0;
 static int g_launches = 0;
 static bg::DenseProblem g_last{};
 
@@ -87,6 +90,16 @@ hipError_t launch_scaled_add(uint16_t* out, const uint16_t* delta, size_t count,
     ++g_launches;
     return hipSuccess;
 }
+hipError_t launch_streamk(const DenseProblem& p, void* ws, int cfg, uint64_t epoch, hipStream_t) {
+    CHECK(ws != nullptr && epoch != 0 && (cfg == 23 || cfg == 10));
+    CHECK(p.K > 0 && p.K % 8 == 0 && p.lda == p.K && p.ldb == p.K && p.ldc == p.N);
+    size_t need = 0;
+    CHECK(streamk_choose(p.M, p.N, p.K, p.cus, -1, &need) == cfg || g_sk_cfg >= 0);
+    g_sk_cfg = cfg;
+    g_sk_need = need;
+    record_dense(p);
+    return hipSuccess;
+}
 static float g_fake_scratch[4];
 hipError_t noalloc_scratch(void** ptr) {
     *ptr = g_fake_scratch;
@@ -127,6 +140,27 @@ int main() {
     CHECK(gemm_w4a16(u16(A), u8(B), u8(S2), 0.5f, u16(C), 1016, 12288, 2048, nullptr) == BG_OK);
     CHECK(bf16_scaled_add(u16(A), u16(B), 1000, 0.5f, nullptr) == BG_OK);
     CHECK(gemm_w4a16_t(u16(A), u8(B), u8(S2), 248192, 0.5f, u16(C), 37, 248077, 2048, nullptr) == BG_OK);
+    size_t sk_need = 0;
+    CHECK(gemm_bf16_streamk_workspace(5120, 512, 2048, &sk_need) == BG_OK);
+    CHECK(sk_need == (size_t)256 * (128 * 128 * 4 + 8) || sk_need == (size_t)256 * (256 * 128 * 4 + 8));
+    CHECK(gemm_bf16_streamk(u16(A), u16(B), u16(C), u8(W), sk_need, 5120, 512, 2048, nullptr) == BG_OK);
+    CHECK(g_sk_need == sk_need);
+    CHECK(gemm_bf16_streamk(u16(A), u16(B), u16(C), nullptr, 0, 70, 90, 100, nullptr) == BG_OK);   // K % 8
+    CHECK(gemm_bf16_streamk(u16(A), u16(B), u16(C), nullptr, 0, 40, 30, 0, nullptr) == BG_OK);     // K == 0
+    for (uint32_t m : {0u, 1u, 40u, 5120u})
+        for (uint32_t k : {0u, 1u, 8u, 64u, 2048u}) CHECK(gemm_bf16_streamk_workspace(m, 30, k, &sk_need) == BG_OK);
+    CHECK(gemm_bf16_streamk_workspace(5120, 512, 2048, &sk_need) == BG_OK);
+    {
+        size_t rows = 0;
+        CHECK(bg_streamk_plan(160, 32, 32, nullptr, 0, &rows) == BG_OK && rows == 384);
+        std::vector<int32_t> plan(6 * rows);
+        CHECK(bg_streamk_plan(160, 32, 32, plan.data(), rows, &rows) == BG_OK);
+        CHECK(bg_streamk_plan(1720, 32, 32, nullptr, 0, &rows) == BG_OK);
+        std::vector<int32_t> big_plan(6 * rows);
+        CHECK(bg_streamk_plan(1720, 32, 32, big_plan.data(), rows, &rows) == BG_OK);
+        CHECK(bg_streamk_plan(3, 100, 1, nullptr, 0, &rows) == BG_OK);
+        CHECK(bg_streamk_plan(7, 1, 32, nullptr, 0, &rows) == BG_OK && rows == 7);
+    }
     const int valid = g_launches;
 
     // invalid calls return their status and launch nothing
@@ -151,6 +185,18 @@ int main() {
     CHECK(gemm_w4a16_t(u16(A), u8(B), u8(S2), 0x7FFFFFFFu, 1.0f, u16(C), 4, 101, 0x7FFFFFF0u, nullptr) == BG_ERR_ALIAS);
     CHECK(bf16_scaled_add(u16(A), u16(A + 16), 64, 1.0f, nullptr) == BG_ERR_ALIAS);
     CHECK(bf16_scaled_add(u16(A), u16(B), (size_t)1 << 63, 1.0f, nullptr) == BG_ERR_SHAPE);
+    CHECK(gemm_bf16_streamk(u16(A), u16(B), u16(C), u8(W), sk_need - 1, 5120, 512, 2048, nullptr) == BG_ERR_WORKSPACE);
+    CHECK(gemm_bf16_streamk(u16(A), u16(B), u16(C), nullptr, sk_need, 5120, 512, 2048, nullptr) == BG_ERR_WORKSPACE);
+    CHECK(gemm_bf16_streamk(u16(A), u16(B), u16(C), u8(A + 16), sk_need, 5120, 512, 2048, nullptr) == BG_ERR_ALIAS);
+    CHECK(gemm_bf16_streamk(u16(A), u16(B), u16(C), u8(W + 4), sk_need, 5120, 512, 2048, nullptr) == BG_ERR_ALIGN);
+    CHECK(gemm_bf16_streamk_workspace(4, 4, big, &sk_need) == BG_ERR_SHAPE);
+    {
+        size_t rows = 0;
+        int32_t one[6];
+        CHECK(bg_streamk_plan(160, 32, 32, one, 1, &rows) == BG_ERR_WORKSPACE && rows == 384);
+        CHECK(bg_streamk_plan(1u << 30, 1, 32, nullptr, 0, &rows) == BG_ERR_SHAPE);
+        CHECK(bg_streamk_plan(4, 4, 0, nullptr, 0, &rows) == BG_ERR_SHAPE);
+    }
     CHECK(g_launches == valid);
 
     // a device of another architecture is refused

@@ -175,6 +175,28 @@ def test_workspace_rules():
     assert L.gemm_fp4_blockscaled_splitk(A, S1, B, S2, C, None, need, 4, 4, 128, 2, None) == bg.BG_ERR_WORKSPACE
 
 
+def test_streamk_argument_rules():
+    L = bg.lib
+    assert L.gemm_bf16_streamk(None, None, None, None, 0, 0, 4, 64, None) == bg.BG_OK
+    assert L.gemm_bf16_streamk(None, None, None, None, 0, 4, 0, 64, None) == bg.BG_OK
+    assert L.gemm_bf16_streamk(A, B, None, W, 1 << 20, 4, 4, 64, None) == bg.BG_ERR_NULL
+    assert L.gemm_bf16_streamk(A, B, A + 16, W, 1 << 20, 4, 4, 64, None) == bg.BG_ERR_ALIAS
+    assert L.gemm_bf16_streamk(A + 2, B, C, W, 1 << 20, 4, 4, 64, None) == bg.BG_ERR_ALIGN
+    # the stream-K kernel takes K % 8 == 0: it needs a workspace, 16-byte aligned
+    assert L.gemm_bf16_streamk(A, B, C, None, 1 << 20, 4, 4, 64, None) == bg.BG_ERR_WORKSPACE
+    assert L.gemm_bf16_streamk(A, B, C, W + 8, 1 << 20, 4, 4, 64, None) == bg.BG_ERR_ALIGN
+    assert L.gemm_bf16_streamk(A, B, C, None, 0, 4, 4, 2 ** 32 - 1, None) == bg.BG_ERR_SHAPE
+    n = ctypes.c_size_t(7)
+    assert L.gemm_bf16_streamk_workspace(4, 4, 64, None) == bg.BG_ERR_NULL
+    assert L.gemm_bf16_streamk_workspace(4, 4, 2 ** 32 - 1, ctypes.byref(n)) == bg.BG_ERR_SHAPE
+    rows = ctypes.c_size_t(0)
+    assert L.bg_streamk_plan(160, 32, 32, None, 0, None) == bg.BG_ERR_NULL
+    assert L.bg_streamk_plan(160, 32, 0, None, 0, ctypes.byref(rows)) == bg.BG_ERR_SHAPE
+    assert L.bg_streamk_plan(160, 32, 32, None, 0, ctypes.byref(rows)) == bg.BG_OK and rows.value == 384
+    buf = (ctypes.c_int32 * 6)()
+    assert L.bg_streamk_plan(160, 32, 32, buf, 1, ctypes.byref(rows)) == bg.BG_ERR_WORKSPACE
+
+
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="valid call would launch on fake pointers")
 def test_valid_arguments_reach_the_device_check():
     L = bg.lib
@@ -185,6 +207,10 @@ def test_valid_arguments_reach_the_device_check():
     assert L.gemm_bf16_dual(A, B, S1, C, W, 4, 4, 8, None) == bg.BG_ERR_DEVICE
     assert L.gemm_w4a16_t(A, B, S2, 248077, 0.5, C, 4, 248077, 32, None) == bg.BG_ERR_DEVICE
     assert L.gemm_bf16_splitk_noalloc(A, B, C, 1024, 2048, 256, 4, None) == bg.BG_ERR_DEVICE
+    assert L.gemm_bf16_streamk(A, B, C, W, 1 << 20, 4, 4, 64, None) == bg.BG_ERR_DEVICE
+    assert L.gemm_bf16_streamk(A, B, C, None, 0, 4, 4, 100, None) == bg.BG_ERR_DEVICE
+    n = ctypes.c_size_t(0)
+    assert L.gemm_bf16_streamk_workspace(5120, 512, 2048, ctypes.byref(n)) == bg.BG_ERR_DEVICE
 
 
 def test_python_binding_raises_on_status():

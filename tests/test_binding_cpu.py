@@ -108,7 +108,7 @@ def test_host_tensors_are_rejected(i, nolib):
 
 
 def test_tuning_overrides_set_get_reset():
-    for key in range(6):
+    for key in range(7):
         assert bg.tune_get(key) == -1
     with bg.tuned(bg.TUNE_TILE, 3):
         assert bg.tune_get(bg.TUNE_TILE) == 3
@@ -117,7 +117,7 @@ def test_tuning_overrides_set_get_reset():
         assert bg.tune_get(bg.TUNE_TILE) == 3
     assert bg.tune_get(bg.TUNE_TILE) == -1
     with pytest.raises(bg.BlockGemmError):
-        bg.tune_set(6, 0)
+        bg.tune_set(7, 0)
     with pytest.raises(bg.BlockGemmError):
         bg.tune_set(bg.TUNE_TILE, -2)
     assert bg.tune_get(99) == -1
