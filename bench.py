@@ -63,6 +63,9 @@ def parse():
     p.add_argument("--data-ceiling", action="store_true",
                    help="only time the gate+up dual call on random, constant and zero operands (same "
                         "kernels, different switching activity) with the engine clock, print JSON and exit")
+    p.add_argument("--streamk", action="store_true",
+                   help="only time gemm_bf16, gemm_bf16_streamk (both tiles) and gemm_bf16_splitk on the "
+                        "attention, MLP and deep-K shapes, print JSON and exit")
     return p.parse_args()
 
 
@@ -107,6 +110,10 @@ def main():
 
     if args.data_ceiling:
         print(json.dumps(data_ceiling(bg, synthetic, torch, np, up16, dev)), flush=True)
+        return
+
+    if args.streamk:
+        print(json.dumps(streamk_compare(bg, synthetic, torch, np, up16, dev)), flush=True)
         return
 
     t_gen = time.time()
@@ -387,6 +394,68 @@ def data_ceiling(bg, synthetic, torch, np, up16, dev):
                      "frac_bf16_peak": round(flops / us / 1e6 / BF16_PEAK_TFLOPS, 4),
                      "sclk_mhz_mean": None if clocks[name] is None else clocks[name]["sclk_mhz_mean"]}
         log(f"data ceiling {name}: {out[name]}")
+    return out
+
+
+def streamk_compare(bg, synthetic, torch, np, up16, dev):
+    """The stream-K entry point against the data-parallel one (and split-K
+    with k = 2, 4, 8) on the attention and MLP shapes and two deep-K shapes
+    with fewer tiles than CUs. Random BF16 operands (X ~ N(0,1), W ~
+    N(0,0.02)); per variant the median of four interleaved rounds of 20
+    back-to-back calls."""
+    shapes = [(5120, 512, 2048), (5120, 2048, 2048), (5120, 2048, 11008), (5120, 11008, 2048),
+              (1024, 1024, 8192), (512, 1024, 16384), (2048, 4096, 4096)]
+    out = {"unit": "us per call (TFLOP/s)"}
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n=20):
+        fn()
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for _ in range(n):
+            fn()
+        e.record(stream)
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / n * 1e3
+
+    for m, n, k in shapes:
+        A = up16(synthetic.normal_bf16((m, k), 1.0, 1, 0))
+        B = up16(synthetic.normal_bf16((n, k), 0.02, 2, 1))
+        C = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        wss = {}
+        for cfg in (23, 10):
+            bg.tune_set(bg.TUNE_STREAMK_TILE, cfg)
+            wss[cfg] = torch.empty(bg.gemm_bf16_streamk_workspace(m, n, k), dtype=torch.uint8, device=dev)
+        bg.tune_set(bg.TUNE_STREAMK_TILE, -1)
+        planes = torch.empty((8, m, n), dtype=torch.float32, device=dev)
+
+        def sk(cfg):
+            def f():
+                bg.tune_set(bg.TUNE_STREAMK_TILE, cfg)
+                bg.gemm_bf16_streamk(A, B, workspace=wss[cfg], out=C)
+            return f
+
+        variants = {"data_parallel": lambda: bg.gemm_bf16(A, B, out=C),
+                    "streamk_128x128": sk(23), "streamk_256x128": sk(10)}
+        for ks in (2, 4, 8):
+            variants[f"splitk_{ks}"] = (lambda ks=ks: bg.gemm_bf16_splitk(A, B, ks, workspace=planes, out=C))
+        res = {v: [] for v in variants}
+        gc.collect()
+        gc.disable()
+        for r in range(4):
+            for v in (list(variants) if r % 2 == 0 else list(variants)[::-1]):
+                res[v].append(timed(variants[v]))
+        gc.enable()
+        bg.tune_set(bg.TUNE_STREAMK_TILE, -1)
+        fl = 2.0 * m * n * k
+        row = {v: f"{np.median(t):.1f} ({fl / np.median(t) / 1e6:.0f})" for v, t in res.items()}
+        ws_default = bg.gemm_bf16_streamk_workspace(m, n, k)
+        row["streamk_default_tile"] = "128x128" if ws_default == wss[23].numel() else "256x128"
+        out[f"{m}x{n}x{k}"] = row
+        log(f"streamk compare {m}x{n}x{k}: {row}")
+        del A, B, C, wss, planes
     return out
 
 
