@@ -529,13 +529,13 @@ def measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream, oracle_seconds
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     spread = {}
 
-    def timed(fn, reps=20):
-        """Median per-call time in us, warm and cold (p20/p80 kept in
-        `spread`). Calls are enqueued back to back (no host synchronisation
-        between them), each inside its own pair of events on the stream; cold
-        calls are preceded by a 1 GiB write that evicts the L2s and the
-        256 MB Infinity Cache."""
-        for _ in range(3):
+    def timed(fn, reps=50):
+        """Median per-call time in us over `reps` calls, warm and cold
+        (p20/p80 kept in `spread`), after 5 untimed calls. Calls are
+        enqueued back to back (no host synchronisation between them), each
+        inside its own pair of events on the stream; cold calls are preceded
+        by a 1 GiB write that evicts the L2s and the 256 MB Infinity Cache."""
+        for _ in range(5):
             fn()
         torch.cuda.synchronize()
         res = {}
