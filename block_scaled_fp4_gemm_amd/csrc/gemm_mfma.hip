@@ -687,7 +687,10 @@ template <int EPI, int BM, int BN, int WM, int WN, int FM, int FN, int NT, int C
 __device__ __forceinline__ void staged_epilogue(const KParams& p, const f32x16 (&acc)[FM][FN],
                                                 uint8_t* lds, int m0, int n0, int wm, int wn,
                                                 int lane, int tid, int split,
-                                                const u32x4* pre = nullptr, void* c_base = nullptr) {
+                                                const u32x4* pre = nullptr, void* c_base = nullptr,
+                                                bool writer = true) {
+    // `writer` false: this wave holds no part of the tile (the second K half
+    // of a sliced-K workgroup) and only helps stream the staged rows
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int ELEM = (EPI == EPI_STORE_F32) ? 4 : 2;
     constexpr int ROWB = BN * ELEM;            // bytes per staged row
@@ -711,7 +714,7 @@ __device__ __forceinline__ void staged_epilogue(const KParams& p, const f32x16 (
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int blk = wm * TM + i * 32;            // first row of this MFMA row block
-            if (blk < pass * RP || blk >= (pass + 1) * RP) continue;
+            if (!writer || blk < pass * RP || blk >= (pass + 1) * RP) continue;
             const int row = blk + (lane & 31) - pass * RP;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
@@ -1449,6 +1452,90 @@ gemm_streamk_kernel(KParams p, SkArgs q) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Sliced K: two groups of WM x WN waves share one BM x BN tile, group g
+// walking the g-th half of K through its own ring of LDS stages, so each SIMD
+// holds one wave of each group and the two overlap each other's waits (a
+// problem with no more tiles than CUs runs one workgroup per CU, and a single
+// wave per SIMD leaves the matrix core idle during its barriers and loads).
+// Both halves have the same number of steps, so every wave passes the same
+// barriers. The second group's FP32 sums are then added to the first's
+// through LDS (always first half + second half) and the workgroup stores the
+// tile. K must be a multiple of 128.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, int STAGES>
+__global__ void __launch_bounds__(2 * WM * WN * 64)
+gemm_slicedk_kernel(KParams p) {
+    constexpr int NTG = WM * WN * 64;   // threads per group
+    constexpr int NT = 2 * NTG;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    static_assert(FM * 32 * WM == BM && FN * 32 * WN == BN, "bad tile split");
+    constexpr int STAGE = (BM + BN) * BK;
+    constexpr int SMEM_ELEMS = 2 * STAGES * STAGE;
+    static_assert(SMEM_ELEMS * 2 >= NTG * FM * FN * 16 * 4, "the second half's sums fit the stages");
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM_ELEMS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = wave / (WM * WN);                  // K half of this wave
+    const int gw = wave % (WM * WN), gtid = tid % NTG;
+    const int wm = gw / WN, wn = gw % WN;
+
+    int tm, tn;
+    tile_of_block(p.tiles_m, p.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int half = p.K / 2;
+
+    f32x16 acc[FM][FN];
+    zero_acc(acc);
+    direct_mainloop<BM, BN, BK, WM, WN, STAGES, 0>(p, p.B, smem + g * STAGES * STAGE, m0, n0, g * half,
+                                                   (g + 1) * half, gw, lane, gtid, acc, []() { return true; });
+
+    // second half -> LDS in each lane's accumulator order, first half adds it
+    float* xs = reinterpret_cast<float*>(smem) + (int64_t)gw * (FM * FN * 16 * 64);
+    lds_barrier();
+    if (g == 1) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    *reinterpret_cast<f32x4*>(xs + ((i * FN + j) * 4 + c) * 256 + lane * 4) =
+                        f32x4{acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
+    }
+    lds_barrier();
+    if (g == 0) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(xs + ((i * FN + j) * 4 + c) * 256 + lane * 4);
+                    acc[i][j][4 * c] += v[0];
+                    acc[i][j][4 * c + 1] += v[1];
+                    acc[i][j][4 * c + 2] += v[2];
+                    acc[i][j][4 * c + 3] += v[3];
+                }
+    }
+    staged_epilogue<EPI_STORE_BF16, BM, BN, WM, WN, FM, FN, NT, SMEM_ELEMS * 2>(
+        p, acc, reinterpret_cast<uint8_t*>(smem), m0, n0, wm, wn, lane, tid, 0, nullptr, p.C, g == 0);
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES>
+hipError_t launch_slicedk(const KParams& kp, hipStream_t stream) {
+    KParams q = kp;
+    q.tiles_m = (kp.M + BM - 1) / BM;
+    q.tiles_n = (kp.N + BN - 1) / BN;
+    q.dual_tiles_n = 0;
+    hipLaunchKernelGGL((gemm_slicedk_kernel<BM, BN, WM, WN, STAGES>), dim3((unsigned)(q.tiles_m * q.tiles_n)),
+                       dim3(2 * WM * WN * 64), 0, stream, q);
+    return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN, int EPI, int SRC, int RSETS = 2>
 hipError_t launch_cfg(const KParams& kp, int splits, hipStream_t stream, int batch = 1) {
     KParams q = kp;
@@ -1533,6 +1620,17 @@ hipError_t launch_tile_cfg(const KParams& kp, int splits, int cfg, hipStream_t s
         case 16: return launch_direct<320, 128, 64, 2, 2, 2, EPI>(kp, splits, stream);
         case 17: return launch_direct<160, 128, 64, 1, 4, 3, EPI>(kp, splits, stream);
         case 23: return launch_direct<128, 128, 64, 2, 2, 3, EPI>(kp, splits, stream);
+        case 27:
+        case 28:
+            // sliced K (two K halves per tile): BF16 store of one problem with
+            // K % 128 == 0; anything else takes the 128 x 128 three-stage tile
+            if constexpr (EPI == EPI_STORE_BF16) {
+                if (splits == 1 && !kp.dual && kp.k_chunk == kp.K && kp.K % 128 == 0) {
+                    if (cfg == 27) return launch_slicedk<128, 128, 2, 2, 2>(kp, stream);
+                    return launch_slicedk<64, 128, 2, 2, 3>(kp, stream);
+                }
+            }
+            return launch_direct<128, 128, 64, 2, 2, 3, EPI>(kp, splits, stream);
         default: return launch_direct<256, 128, 64, 4, 2, 3, EPI>(kp, splits, stream);   // 10
     }
 }
@@ -1564,7 +1662,13 @@ constexpr TileChoice kTileChoices[] = {
     {9, 160, 128, 2, 884.0, 819.0},
     {6, 128, 128, 2, 808.0, 671.0},
     {23, 128, 128, 1, 763.0, 763.0},   // three stages: 5120 x 512, 160 tiles
+    // sliced K, 64 x 128 (two K halves per tile, rates counted on the whole
+    // K): deep-K problems with few tiles, e.g. 1024 x 1024 x 8192 33.5 us
+    // against 50.0 us for the 128 x 128 tile. BF16 store of one problem
+    // with K % 128 == 0 only (kSlicedCfg).
+    {28, 64, 128, 1, 700.0, 950.0},
 };
+constexpr int kSlicedCfg = 28;
 constexpr double kLaunchGapUs = 2.0;   // second launch of a column split
 
 struct Schedule {
@@ -1582,10 +1686,11 @@ double dp_us(const TileChoice& c, int M, int N, int K, int splits, int cus) {
     return rounds * occ * 2.0 * c.bm * c.bn * ((double)K / splits) * cus / (rate * 1e6);
 }
 
-const TileChoice* best_single(int M, int N, int K, int splits, int cus, double* t_out) {
+const TileChoice* best_single(int M, int N, int K, int splits, int cus, double* t_out, bool sliced_ok = false) {
     const TileChoice* best = &kTileChoices[0];
     double best_t = 1e300;
     for (const TileChoice& c : kTileChoices) {
+        if (c.cfg == kSlicedCfg && !sliced_ok) continue;
         const double t = dp_us(c, M, N, K, splits, cus);
         if (t < best_t) {
             best_t = t;
@@ -1605,7 +1710,8 @@ Schedule choose_schedule(int M, int N, int K, int splits, int cus, int epi) {
         return {cfg, N, cfg};
     }
     double best_t;
-    const TileChoice* one = best_single(M, N, K, splits, cus, &best_t);
+    const bool sliced_ok = epi == EPI_STORE_BF16 && splits == 1 && K % 128 == 0;
+    const TileChoice* one = best_single(M, N, K, splits, cus, &best_t, sliced_ok);
     Schedule best{one->cfg, N, one->cfg};
     if (epi != EPI_STORE_BF16 || splits != 1) return best;
     const TileChoice& big = kTileChoices[0];

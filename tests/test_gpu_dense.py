@@ -99,7 +99,7 @@ def test_mlp_gate_up_sampled_rows_and_determinism():
 
 
 # every entry of the tile table (the BG_TUNE_TILE override forces one)
-TILE_CFGS = list(range(0, 24))
+TILE_CFGS = list(range(0, 24)) + [27, 28]
 CFG_SHAPES = [(1, 1, 8), (65, 129, 72), (161, 257, 136), (257, 225, 1000), (320, 448, 520), (33, 70, 64)]
 
 
@@ -124,3 +124,26 @@ def test_every_tile_config_edge_shapes(cfg, force):
         torch.cuda.synchronize()
         assert_bits_equal(bits_of(o), oracle.gemm_scaled_acc_exact(out, ga, gb, 2.0), f"cfg {cfg} fold")
         assert_bits_equal(bits_of(c3), want, f"cfg {cfg} splitk3")
+
+
+# sliced K (cfg 27: 128 x 128, cfg 28: 64 x 128; two K halves per tile, added
+# in a fixed order) takes K % 128 == 0; ragged M and N, one and many steps per half
+SLICED_SHAPES = [(1, 1, 128), (65, 129, 128), (161, 257, 1024), (300, 200, 2048), (33, 70, 256), (257, 513, 640)]
+
+
+@pytest.mark.parametrize("cfg", [27, 28])
+def test_slicedk_tiles(cfg, force):
+    force(bg.TUNE_TILE, cfg)
+    for m, n, k in SLICED_SHAPES:
+        print(f"slicedk cfg={cfg} m={m} n={n} k={k}", flush=True)
+        a = synthetic.normal_bf16((m, k), 1.0, 3500 + m, 0)
+        b = synthetic.normal_bf16((n, k), 0.5, 3500 + n, 1)
+        got = _run(a, b)
+        check_close(got, oracle.gemm_bf16_ref(a, b), k, oracle.rms(oracle.bf16_to_f64(a)),
+                    oracle.rms(oracle.bf16_to_f64(b)), f"slicedk cfg {cfg} {m}x{n}x{k}")
+        assert_bits_equal(_run(a, b), got, f"slicedk repeat cfg {cfg} {m}x{n}x{k}")
+        ga = synthetic.grid_bf16((m, k), -8, 8, -5, 3501, 0)
+        gb = synthetic.grid_bf16((n, k), -8, 8, -5, 3501, 1)
+        want = oracle.f32_to_bf16(oracle.gemm_bf16_ref(ga, gb).astype(np.float32))
+        assert_bits_equal(_run(ga, gb), want, f"slicedk exact cfg {cfg} {m}x{n}x{k}")
+
