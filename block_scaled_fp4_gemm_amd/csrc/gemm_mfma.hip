@@ -1463,7 +1463,7 @@ gemm_streamk_kernel(KParams p, SkArgs q) {
 // through LDS (always first half + second half) and the workgroup stores the
 // tile. K must be a multiple of 128.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int STAGES>
+template <int BM, int BN, int WM, int WN, int STAGES, int BKS = BK>
 __global__ void __launch_bounds__(2 * WM * WN * 64)
 gemm_slicedk_kernel(KParams p) {
     constexpr int NTG = WM * WN * 64;   // threads per group
@@ -1471,9 +1471,13 @@ gemm_slicedk_kernel(KParams p) {
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
     static_assert(FM * 32 * WM == BM && FN * 32 * WN == BN, "bad tile split");
-    constexpr int STAGE = (BM + BN) * BK;
+    constexpr int STAGE = (BM + BN) * BKS;
     constexpr int SMEM_ELEMS = 2 * STAGES * STAGE;
-    static_assert(SMEM_ELEMS * 2 >= NTG * FM * FN * 16 * 4, "the second half's sums fit the stages");
+    // the exchange moves PB accumulator blocks (of every wave of the group)
+    // per pass through the stages
+    constexpr int NB = FM * FN;
+    constexpr int PB = (SMEM_ELEMS * 2) / (NTG * 16 * 4) < NB ? (SMEM_ELEMS * 2) / (NTG * 16 * 4) : NB;
+    static_assert(PB >= 1, "one accumulator block of the group fits the stages");
     __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM_ELEMS];
 
     const int tid = threadIdx.x;
@@ -1490,48 +1494,51 @@ gemm_slicedk_kernel(KParams p) {
 
     f32x16 acc[FM][FN];
     zero_acc(acc);
-    direct_mainloop<BM, BN, BK, WM, WN, STAGES, 0>(p, p.B, smem + g * STAGES * STAGE, m0, n0, g * half,
-                                                   (g + 1) * half, gw, lane, gtid, acc, []() { return true; });
+    direct_mainloop<BM, BN, BKS, WM, WN, STAGES, 0>(p, p.B, smem + g * STAGES * STAGE, m0, n0, g * half,
+                                                    (g + 1) * half, gw, lane, gtid, acc, []() { return true; });
 
     // second half -> LDS in each lane's accumulator order, first half adds it
-    float* xs = reinterpret_cast<float*>(smem) + (int64_t)gw * (FM * FN * 16 * 64);
-    lds_barrier();
-    if (g == 1) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
+    float* xs = reinterpret_cast<float*>(smem);
+    static_for<(NB + PB - 1) / PB>([&](auto pc) {
+        constexpr int b0 = decltype(pc)::value * PB;
+        lds_barrier();
+        if (g == 1) {
+            static_for<(NB - b0 < PB ? NB - b0 : PB)>([&](auto qc) {
+                constexpr int q = b0 + decltype(qc)::value, i = q / FN, j = q % FN;
+                float* dst = xs + ((int64_t)(q - b0) * (WM * WN) + gw) * (16 * 64);
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    *reinterpret_cast<f32x4*>(xs + ((i * FN + j) * 4 + c) * 256 + lane * 4) =
+                    *reinterpret_cast<f32x4*>(dst + c * 256 + lane * 4) =
                         f32x4{acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
-    }
-    lds_barrier();
-    if (g == 0) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
+            });
+        }
+        lds_barrier();
+        if (g == 0) {
+            static_for<(NB - b0 < PB ? NB - b0 : PB)>([&](auto qc) {
+                constexpr int q = b0 + decltype(qc)::value, i = q / FN, j = q % FN;
+                const float* src = xs + ((int64_t)(q - b0) * (WM * WN) + gw) * (16 * 64);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    const f32x4 v = *reinterpret_cast<const f32x4*>(xs + ((i * FN + j) * 4 + c) * 256 + lane * 4);
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(src + c * 256 + lane * 4);
                     acc[i][j][4 * c] += v[0];
                     acc[i][j][4 * c + 1] += v[1];
                     acc[i][j][4 * c + 2] += v[2];
                     acc[i][j][4 * c + 3] += v[3];
                 }
-    }
+            });
+        }
+    });
     staged_epilogue<EPI_STORE_BF16, BM, BN, WM, WN, FM, FN, NT, SMEM_ELEMS * 2>(
         p, acc, reinterpret_cast<uint8_t*>(smem), m0, n0, wm, wn, lane, tid, 0, nullptr, p.C, g == 0);
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES>
+template <int BM, int BN, int WM, int WN, int STAGES, int BKS = BK>
 hipError_t launch_slicedk(const KParams& kp, hipStream_t stream) {
     KParams q = kp;
     q.tiles_m = (kp.M + BM - 1) / BM;
     q.tiles_n = (kp.N + BN - 1) / BN;
     q.dual_tiles_n = 0;
-    hipLaunchKernelGGL((gemm_slicedk_kernel<BM, BN, WM, WN, STAGES>), dim3((unsigned)(q.tiles_m * q.tiles_n)),
+    hipLaunchKernelGGL((gemm_slicedk_kernel<BM, BN, WM, WN, STAGES, BKS>), dim3((unsigned)(q.tiles_m * q.tiles_n)),
                        dim3(2 * WM * WN * 64), 0, stream, q);
     return hipGetLastError();
 }
