@@ -761,7 +761,11 @@ __device__ __forceinline__ void staged_epilogue(const KParams& p, const f32x16 (
             } else if constexpr (EPI == EPI_STORE_BF16 || EPI == EPI_SCALE_BF16) {
                 uint16_t* C = reinterpret_cast<uint16_t*>(Cb);
                 if (full) {
-                    *reinterpret_cast<u32x4*>(C + off) = w;
+                    // Non-temporal: the output does not displace operands
+                    // (this GEMM's or the next one's) from the L2s and the
+                    // Infinity Cache. MLP step 586.5 -> 571.9 us, Q/O 39.0 ->
+                    // 37.8 us, down 185.7 -> 184.1 us in an interleaved A/B.
+                    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(C + off));
                 } else {
                     const uint32_t e4[4] = {w.x, w.y, w.z, w.w};
                     for (int e = 0; e < 8 && n + e < N; ++e) C[off + e] = (uint16_t)(e4[e >> 1] >> ((e & 1) * 16));
