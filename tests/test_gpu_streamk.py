@@ -124,3 +124,27 @@ def test_streamk_workspace_rules_on_device(force):
     assert L.gemm_bf16_streamk(a.data_ptr(), b.data_ptr(), c.data_ptr(), None, need, m, n, k, st) == \
         bg.BG_ERR_WORKSPACE
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("cfg", [23, 10])
+def test_streamk_exchange_repeated_calls(cfg, force):
+    """100 calls back to back on exactly summable data (every output unique
+    whatever the split), alternating two workspaces: each result compared
+    bit for bit on the device with the oracle's, so a partial read before
+    its flag, or a flag taken from another call, shows up as a difference."""
+    force(bg.TUNE_STREAMK_TILE, cfg)
+    m, n, k = 5120, 512, 2048
+    print(f"streamk repeated cfg={cfg}", flush=True)
+    a = synthetic.grid_bf16((m, k), -8, 8, -5, 3400, 0)
+    b = synthetic.grid_bf16((n, k), -8, 8, -5, 3400, 1)
+    want = to_dev_bf16(oracle.f32_to_bf16(oracle.gemm_bf16_ref(a, b).astype(np.float32))).view(torch.int16)
+    A, B = to_dev_bf16(a), to_dev_bf16(b)
+    need = bg.gemm_bf16_streamk_workspace(m, n, k)
+    wss = [torch.empty(need, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    outs = [torch.empty((m, n), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    bad = torch.zeros((), dtype=torch.int64, device="cuda")
+    for i in range(100):
+        c = bg.gemm_bf16_streamk(A, B, workspace=wss[i % 2], out=outs[i % 2])
+        bad += (c.view(torch.int16) != want).sum()
+    torch.cuda.synchronize()
+    assert int(bad) == 0, f"{int(bad)} differing elements over 100 calls"
