@@ -176,7 +176,22 @@ splitk_reduce_kernel(const float* __restrict__ ws, uint16_t* __restrict__ C, int
     if (e0 >= count) return;
     if (vec && e0 + 3 < count) {
         f32x4 s = *reinterpret_cast<const f32x4*>(ws + e0);
-        for (int p = 1; p < splits; ++p) {
+        // four planes' loads in flight before their adds (same ascending
+        // order): 128 x 4096 x 7168 FP4 decode at k_splits 12, 25.9 -> 25.1 us
+        int p = 1;
+        for (; p + 3 < splits; p += 4) {
+            f32x4 v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const f32x4*>(ws + (int64_t)(p + q) * count + e0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                s.x = __fadd_rn(s.x, v[q].x);
+                s.y = __fadd_rn(s.y, v[q].y);
+                s.z = __fadd_rn(s.z, v[q].z);
+                s.w = __fadd_rn(s.w, v[q].w);
+            }
+        }
+        for (; p < splits; ++p) {
             const f32x4 v = *reinterpret_cast<const f32x4*>(ws + (int64_t)p * count + e0);
             s.x = __fadd_rn(s.x, v.x);
             s.y = __fadd_rn(s.y, v.y);
