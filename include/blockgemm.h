@@ -205,10 +205,11 @@ bg_status gemm_bf16_splitk_noalloc(const uint16_t* A, const uint16_t* B, uint16_
  *             overlapping A, B or C. It needs no initialization: the call
  *             marks each partial it publishes with a number unique to the
  *             call. Calls that may run concurrently need separate workspaces.
- *  K == 0, K not a multiple of 8, or K >= 2^31 / 640 (beyond the kernel's
- *  32-bit operand offsets): the data-parallel kernel of gemm_bf16 computes C
- *  (the same bits gemm_bf16 returns) and the workspace is unused (it may be
- *  NULL); otherwise a NULL workspace is BG_ERR_WORKSPACE.
+ *  K == 0, K not a multiple of 8, K >= 2^31 / 640 (beyond the kernel's
+ *  32-bit operand offsets), or 2^30 or more 128 x 128 tiles or (tile, K step)
+ *  pairs per XCD (beyond its 32-bit step ids): the data-parallel kernel of
+ *  gemm_bf16 computes C (the same bits gemm_bf16 returns) and the workspace
+ *  is unused (it may be NULL); otherwise a NULL workspace is BG_ERR_WORKSPACE.
  *  Other rules as gemm_bf16. The tile configuration is chosen from the shape
  *  (bg_tune_set(BG_TUNE_STREAMK_TILE, ...) overrides it); the workspace size
  *  depends on it, so query the size after any override.
