@@ -1673,6 +1673,9 @@ constexpr TileChoice kTileChoices[] = {
     {9, 160, 128, 2, 884.0, 819.0},
     {6, 128, 128, 2, 808.0, 671.0},
     {23, 128, 128, 1, 763.0, 763.0},   // three stages: 5120 x 512, 160 tiles
+    // 160 x 128 with three stages (one block per CU): 5120 x 1024 x 2048 is one
+    // round of 256 tiles, 23.9 us against 28.7 us for the two-block 160 x 128
+    {17, 160, 128, 1, 880.0, 900.0},
     // sliced K, 64 x 128 (two K halves per tile, rates counted on the whole
     // K): deep-K problems with few tiles, e.g. 1024 x 1024 x 8192 33.5 us
     // against 50.0 us for the 128 x 128 tile. BF16 store of one problem
