@@ -1493,12 +1493,20 @@ gemm_slicedk_kernel(KParams p) {
 
     int tm, tn;
     tile_of_block(p.tiles_m, p.tiles_n, tm, tn);
+    // the second problem of a dual launch (uniform per workgroup)
+    const uint16_t* Bop = p.B;
+    void* Cop = p.C;
+    if (p.dual_tiles_n > 0 && tn >= p.dual_tiles_n) {
+        tn -= p.dual_tiles_n;
+        Bop = p.B1;
+        Cop = p.C1;
+    }
     const int m0 = tm * BM, n0 = tn * BN;
     const int half = p.K / 2;
 
     f32x16 acc[FM][FN];
     zero_acc(acc);
-    direct_mainloop<BM, BN, BKS, WM, WN, STAGES, 0>(p, p.B, smem + g * STAGES * STAGE, m0, n0, g * half,
+    direct_mainloop<BM, BN, BKS, WM, WN, STAGES, 0>(p, Bop, smem + g * STAGES * STAGE, m0, n0, g * half,
                                                     (g + 1) * half, gw, lane, gtid, acc, []() { return true; });
 
     // second half -> LDS in each lane's accumulator order, first half adds it
@@ -1533,7 +1541,7 @@ gemm_slicedk_kernel(KParams p) {
         }
     });
     staged_epilogue<EPI_STORE_BF16, BM, BN, WM, WN, FM, FN, NT, SMEM_ELEMS * 2>(
-        p, acc, reinterpret_cast<uint8_t*>(smem), m0, n0, wm, wn, lane, tid, 0, nullptr, p.C, g == 0);
+        p, acc, reinterpret_cast<uint8_t*>(smem), m0, n0, wm, wn, lane, tid, 0, nullptr, Cop, g == 0);
 }
 
 template <int BM, int BN, int WM, int WN, int STAGES, int BKS = BK>
@@ -1542,6 +1550,10 @@ hipError_t launch_slicedk(const KParams& kp, hipStream_t stream) {
     q.tiles_m = (kp.M + BM - 1) / BM;
     q.tiles_n = (kp.N + BN - 1) / BN;
     q.dual_tiles_n = 0;
+    if (kp.dual) {   // dual launch: the second product's tiles follow the first's
+        q.dual_tiles_n = q.tiles_n;
+        q.tiles_n *= 2;
+    }
     hipLaunchKernelGGL((gemm_slicedk_kernel<BM, BN, WM, WN, STAGES, BKS>), dim3((unsigned)(q.tiles_m * q.tiles_n)),
                        dim3(2 * WM * WN * 64), 0, stream, q);
     return hipGetLastError();
@@ -1633,10 +1645,11 @@ hipError_t launch_tile_cfg(const KParams& kp, int splits, int cfg, hipStream_t s
         case 23: return launch_direct<128, 128, 64, 2, 2, 3, EPI>(kp, splits, stream);
         case 27:
         case 28:
-            // sliced K (two K halves per tile): BF16 store of one problem with
-            // K % 128 == 0; anything else takes the 128 x 128 three-stage tile
+            // sliced K (two K halves per tile): BF16 stores (one problem or a
+            // dual launch) with K % 128 == 0; anything else takes the 128 x 128
+            // three-stage tile
             if constexpr (EPI == EPI_STORE_BF16) {
-                if (splits == 1 && !kp.dual && kp.k_chunk == kp.K && kp.K % 128 == 0) {
+                if (splits == 1 && kp.k_chunk == kp.K && kp.K % 128 == 0) {
                     if (cfg == 27) return launch_slicedk<128, 128, 2, 2, 2>(kp, stream);
                     return launch_slicedk<64, 128, 2, 2, 3>(kp, stream);
                 }
@@ -1880,6 +1893,10 @@ hipError_t launch_dense_dual(const DenseProblem& p, const uint16_t* B1, uint16_t
     if (cfg < 0) {
         if (p.K <= 128) {
             cfg = 9;
+        } else if (choose_schedule(kp.M, kp.N, kp.K, 1, kp.cus, EPI_STORE_BF16).cfg == kSlicedCfg) {
+            // gemm_bf16 sums these outputs in two K halves; so must the dual
+            // launch, whose outputs equal gemm_bf16's bit for bit
+            cfg = kSlicedCfg;
         } else {
             double t;
             cfg = best_single(kp.M, 2 * kp.N, kp.K, 1, kp.cus, &t)->cfg;

@@ -1,7 +1,7 @@
 // Work plan of the stream-K GEMM: which K steps of which output tiles each
 // workgroup computes, who stores each tile, and whose partial sums it adds.
 // Host and device share this code: the kernel calls it with blockIdx.x, and
-// the library's bg_streamk_segments export runs the very same functions on
+// the library's bg_streamk_plan export runs the very same functions on
 // the host, so tests can check on the CPU that the plan covers every K step
 // of every tile exactly once and that every wait is on a workgroup that
 // publishes without waiting.

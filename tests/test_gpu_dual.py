@@ -16,8 +16,10 @@ from gpu_util import assert_bits_equal, bits_of, check_close, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
+# the last three take gemm_bf16's sliced-K tile (deep K, few tiles): the dual
+# launch must then sum each output in the same two K halves
 SHAPES = [(1, 1, 8), (7, 129, 65), (65, 257, 136), (300, 200, 1000), (257, 255, 2000), (129, 520, 64),
-          (513, 384, 72), (33, 70, 9), (260, 300, 127)]
+          (513, 384, 72), (33, 70, 9), (260, 300, 127), (128, 256, 512), (300, 200, 2048), (512, 1024, 4096)]
 
 
 def _inputs(m, n, k, seed):
@@ -50,10 +52,10 @@ def test_dual_matches_oracle_and_single_calls(m, n, k):
 # every direct tile configuration of the dense table, forced through the
 # tuning hook (0 is the register-staged tile: the dual call then runs two
 # ordinary launches)
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 6, 8, 9, 10, 12, 14, 23])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 6, 8, 9, 10, 12, 14, 17, 23, 27, 28])
 def test_dual_every_tile_config(cfg, force):
     force(bg.TUNE_TILE, cfg)
-    for m, n, k in [(65, 257, 136), (257, 300, 520), (33, 70, 64)]:
+    for m, n, k in [(65, 257, 136), (257, 300, 520), (33, 70, 64), (130, 260, 512)]:
         _check(*_inputs(m, n, k, 5000 + cfg), f"cfg {cfg} dual {m}x{n}x{k}")
 
 
