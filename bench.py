@@ -33,10 +33,11 @@ sys.path.insert(0, ROOT)
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense BF16 MFMA, published
 FP4_PEAK_TFLOPS = 10100.0     # MI355X dense FP4 MFMA, published
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, published
-# FP32 vector ALU without FMA and without packed-FP32 ops: 256 CUs x 4 SIMDs x
-# 16 lanes x 2.4 GHz = 39.3 T FP32 operations/s; a multiply plus an add per
-# multiply-accumulate makes this 39.3 TFLOP/s of GEMM flops.
-VALU_NOFMA_PEAK_TFLOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# FP32 vector ALU without FMA: the published 157.3 TFLOP/s counts two flops
+# per FMA lane, i.e. 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz FP32 operations;
+# a plain multiply or add issues at the same lane rate, so a multiply plus an
+# add per multiply-accumulate peaks at 78.6 TFLOP/s of GEMM flops.
+VALU_NOFMA_PEAK_TFLOPS = 256 * 4 * 32 * 2.4e9 / 1e12
 
 M, HID, INTER = 5120, 2048, 11008
 

@@ -10,11 +10,14 @@
 // product and sum goes through __fmul_rn / __fadd_rn, so no multiply-add can
 // be fused. FP32 denormals are kept (the library is built without flushing).
 //
-// Design (CDNA4): a workgroup of 16x16 threads owns a (16*RM) x (16*RN)
-// output tile; each thread keeps an RM x RN block of accumulators. K is
-// walked in steps of KT; each step stages A and B rows as FP32 into LDS,
-// row-major with a padded pitch. The per-output k order is untouched by the
-// tiling: tiles are visited in ascending k and, inside a tile, k ascends.
+// Design (CDNA4), two forms. Tile form: a workgroup of 16x16 threads owns a
+// (16*RM) x (16*RN) output tile; each thread keeps an RM x RN block of
+// accumulators. K is walked in steps of KT; each step stages A and B rows as
+// FP32 into LDS, row-major with a padded pitch. Scalar-A form (K % 8 == 0):
+// only B goes through LDS; A's values come through scalar loads into SGPRs,
+// which every lane of a wave reads as a broadcast operand. In both the
+// per-output k order is untouched by the tiling: steps are visited in
+// ascending k and, inside a step, k ascends.
 #include <cmath>
 
 #include "bg_internal.hpp"
@@ -148,6 +151,110 @@ gemm_ordered_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__
     }
 }
 
+// Second form, for K % 8 == 0: A's rows through the scalar unit. A wave owns
+// RM output rows and 64 columns (one per lane); the four waves of a
+// workgroup take 4*RM consecutive rows and share one 64-column B block staged
+// in LDS as above. A's values arrive by scalar loads and are widened in
+// scalar registers, so the 64 lanes multiply one SGPR operand (a broadcast
+// that costs no LDS bandwidth): per four k a lane reads one 16-byte B vector
+// from LDS, where the tile form reads RM + RN. The order per output is the
+// same strict ascending k.
+//
+// Measured on MI355X against the tile form's best block (same bits):
+// 4510 x 256 x 2048 142 -> 120 us, 2255 x 256 x 2048 104 -> 78 us with RM = 3.
+// Two columns per lane (half the scalar widening per multiply), 16-wide K
+// steps with RM = 4..6, and a pipelined form (B in two LDS buffers, the next
+// step's operands loaded during this step's arithmetic) were all slower; RM =
+// 4 runs out of SGPRs (spills to VGPR lanes).
+template <int RM, bool F32_OUT>
+__global__ void __launch_bounds__(256)
+gemm_ordered_sa_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* C,
+                       int M, int N, int K, int tiles_n) {
+    constexpr int TN = 64;
+    constexpr int LDK = KT + 4;
+    constexpr int W = KT / 2;   // 32-bit words of one A row per step
+    __shared__ __attribute__((aligned(16))) float sB[TN * LDK];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int tm, tn;
+    tile_of<ORDER_ROWS>((int)blockIdx.x, (int)gridDim.x / tiles_n, tiles_n, tm, tn);
+    const int r0 = tm * 4 * RM + wave * RM, n0 = tn * TN;
+
+    // rows past M read row M - 1 (in bounds) and are not stored
+    const uint32_t* arow[RM];
+#pragma unroll
+    for (int i = 0; i < RM; ++i)
+        arow[i] = reinterpret_cast<const uint32_t*>(A + (int64_t)min(r0 + i, M - 1) * K);
+
+    float acc[RM];
+#pragma unroll
+    for (int i = 0; i < RM; ++i) acc[i] = 0.0f;
+
+    for (int k0 = 0; k0 < K; k0 += KT) {
+        // this step's A words (two k each), zero past K; issued before the
+        // barrier so they arrive while B is staged
+        uint32_t aw[RM][W];
+        const int kw = k0 >> 1;
+        if (k0 + KT <= K) {
+#pragma unroll
+            for (int i = 0; i < RM; ++i)
+#pragma unroll
+                for (int j = 0; j < W; ++j) aw[i][j] = arow[i][kw + j];
+        } else {
+            const int nw = (K - k0) >> 1;
+#pragma unroll
+            for (int i = 0; i < RM; ++i)
+#pragma unroll
+                for (int j = 0; j < W; ++j) aw[i][j] = j < nw ? arow[i][kw + j] : 0u;
+        }
+        __syncthreads();
+        stage<TN, 256, LDK>(sB, B, n0, N, K, k0, true, tid);
+        __syncthreads();
+        // past K both operands are zero: the products are +0 and leave every
+        // accumulator unchanged
+#pragma unroll
+        for (int kc = 0; kc < KT; kc += 4) {
+            const f32x4 b = *reinterpret_cast<const f32x4*>(&sB[lane * LDK + kc]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int i = 0; i < RM; ++i) {
+                    const uint32_t w = aw[i][(kc + q) >> 1];
+                    const float a = __builtin_bit_cast(float, ((kc + q) & 1) ? (w & 0xFFFF0000u) : (w << 16));
+                    acc[i] = __fadd_rn(acc[i], __fmul_rn(a, b[q]));
+                }
+        }
+    }
+
+    const int n = n0 + lane;
+    if (n >= N) return;
+#pragma unroll
+    for (int i = 0; i < RM; ++i) {
+        const int m = r0 + i;
+        if (m >= M) break;
+        if constexpr (F32_OUT)
+            reinterpret_cast<float*>(C)[(int64_t)m * N + n] = acc[i];
+        else
+            reinterpret_cast<uint16_t*>(C)[(int64_t)m * N + n] = f32_to_bf16_rne(acc[i]);
+    }
+}
+
+template <int RM>
+hipError_t launch_ordered_sa(const uint16_t* A, const uint16_t* B, void* C, bool f32_out, int M, int N,
+                             int K, hipStream_t stream) {
+    const int tiles_m = (M + 4 * RM - 1) / (4 * RM);
+    const int tiles_n = (N + 63) / 64;
+    dim3 grid((unsigned)(tiles_m * tiles_n));
+    if (f32_out)
+        hipLaunchKernelGGL((gemm_ordered_sa_kernel<RM, true>), grid, dim3(256), 0, stream, A, B, C, M, N,
+                           K, tiles_n);
+    else
+        hipLaunchKernelGGL((gemm_ordered_sa_kernel<RM, false>), grid, dim3(256), 0, stream, A, B, C, M, N,
+                           K, tiles_n);
+    return hipGetLastError();
+}
+
 template <int RM, int RN>
 hipError_t launch_ordered_cfg(const uint16_t* A, const uint16_t* B, void* C, bool f32_out, int M,
                               int N, int K, hipStream_t stream) {
@@ -241,19 +348,22 @@ scaled_add_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ delta
 
 }  // namespace
 
-// Register-block choice, fitted to MI355X measurements of this kernel: the
-// VALU loop needs four to five waves per SIMD to hide LDS and dependency
-// latency (one wave per SIMD runs at roughly half speed), single-column
-// blocks amortize their A reads worst, and a larger block reuses its
-// operands better. Score = min(waves per SIMD, 4.5) x column factor x
-// (outputs per thread)^(1/4); the highest score wins. Measured: 4510 x 256 x
-// 2048 picks 2x2 (152 us), 2255 x 256 x 2048 picks 2x1 (111 us).
+// Variant choice. With K % 8 == 0 the scalar-A form runs, with the most rows
+// per wave (up to 3) that still gives every SIMD two waves: 4510 x 256 x 2048
+// and 2255 x 256 x 2048 both take 3 (120 and 78 us). Otherwise the tile form
+// runs with a register block fitted to MI355X measurements: the VALU loop
+// needs four to five waves per SIMD to hide LDS and dependency latency (one
+// wave per SIMD runs at roughly half speed), single-column blocks amortize
+// their A reads worst, and a larger block reuses its operands better. Score =
+// min(waves per SIMD, 4.5) x column factor x (outputs per thread)^(1/4); the
+// highest score wins (those two shapes picked 2x2, 142 us, and 2x1, 104 us).
 namespace {
+// rn == 0: the scalar-A form with rm rows per wave (K % 8 == 0 only)
 struct OrdChoice {
     int rm, rn;
 };
-constexpr OrdChoice kOrdChoices[] = {{4, 4}, {2, 2}, {2, 4}, {6, 2}, {5, 2}, {4, 2}, {3, 2},
-                                     {9, 1}, {6, 1}, {4, 1}, {2, 1}, {1, 1}};
+constexpr OrdChoice kOrdChoices[] = {{4, 4}, {2, 2}, {2, 4}, {6, 2}, {5, 2}, {4, 2}, {3, 2}, {9, 1},
+                                     {6, 1}, {4, 1}, {2, 1}, {1, 1}, {1, 0}, {2, 0}, {3, 0}};
 
 template <int RM, int RN>
 hipError_t run_ordered(const uint16_t* A, const uint16_t* B, void* C, bool f32_out, int M, int N,
@@ -266,10 +376,23 @@ hipError_t launch_ordered(const uint16_t* A, const uint16_t* B, void* C, bool f3
                           uint32_t N, uint32_t K, uint32_t cus, hipStream_t stream) {
     const int simds = 4 * (cus > 0 ? (int)cus : 256);
     int pick = tune(BG_TUNE_ORDERED);   // forced register-block variant, or -1
-    if (pick < 0 || pick >= (int)(sizeof(kOrdChoices) / sizeof(kOrdChoices[0]))) {
+    constexpr int kChoices = (int)(sizeof(kOrdChoices) / sizeof(kOrdChoices[0]));
+    if ((pick < 0 || pick >= kChoices) && K % 8 == 0) {
+        pick = 12;   // scalar-A form, one row per wave
+        for (int c = kChoices - 1; c >= 12; --c) {
+            const int rm = kOrdChoices[c].rm;
+            const double waves = 4.0 * ((M + 4 * rm - 1) / (4 * rm)) * (double)((N + 63) / 64);
+            if (waves >= 2.0 * simds) {
+                pick = c;
+                break;
+            }
+        }
+    }
+    if (pick < 0 || pick >= kChoices) {
         double best = -1.0;
-        for (int c = 0; c < (int)(sizeof(kOrdChoices) / sizeof(kOrdChoices[0])); ++c) {
+        for (int c = 0; c < kChoices; ++c) {
             const int rm = kOrdChoices[c].rm, rn = kOrdChoices[c].rn;
+            if (rn == 0) continue;
             const double waves = 4.0 * ((M + 16 * rm - 1) / (16 * rm)) * (double)((N + 16 * rn - 1) / (16 * rn));
             const double per_simd = waves / simds;
             const double col = rn == 2 ? 1.0 : (rn == 4 ? 0.9 : 0.85);
@@ -281,6 +404,7 @@ hipError_t launch_ordered(const uint16_t* A, const uint16_t* B, void* C, bool f3
         }
     }
     const int m = (int)M, n = (int)N, k = (int)K;
+    if (kOrdChoices[pick].rn == 0 && k % 8 != 0) pick = 10;   // the scalar-A form needs K % 8 == 0
     switch (pick) {
         case 0: return run_ordered<4, 4>(A, B, C, f32_out, m, n, k, stream);
         case 1: return run_ordered<2, 2>(A, B, C, f32_out, m, n, k, stream);
@@ -293,7 +417,10 @@ hipError_t launch_ordered(const uint16_t* A, const uint16_t* B, void* C, bool f3
         case 8: return run_ordered<6, 1>(A, B, C, f32_out, m, n, k, stream);
         case 9: return run_ordered<4, 1>(A, B, C, f32_out, m, n, k, stream);
         case 10: return run_ordered<2, 1>(A, B, C, f32_out, m, n, k, stream);
-        default: return run_ordered<1, 1>(A, B, C, f32_out, m, n, k, stream);
+        case 11: return run_ordered<1, 1>(A, B, C, f32_out, m, n, k, stream);
+        case 12: return launch_ordered_sa<1>(A, B, C, f32_out, m, n, k, stream);
+        case 13: return launch_ordered_sa<2>(A, B, C, f32_out, m, n, k, stream);
+        default: return launch_ordered_sa<3>(A, B, C, f32_out, m, n, k, stream);
     }
 }
 

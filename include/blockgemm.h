@@ -418,7 +418,10 @@ const char* bg_status_string(bg_status status);
  *                      points built on it: dual, strided, scaled_acc,
  *                      split-K planes), an index into the library's tile table
  *  BG_TUNE_COLSPLIT:   0 turns the column split of gemm_bf16 off
- *  BG_TUNE_ORDERED:    register-block variant of gemm_bf16_ordered
+ *  BG_TUNE_ORDERED:    variant of gemm_bf16_ordered (0-11 register blocks of
+ *                      the tile form, 12-14 the scalar-A form with 1-3 rows
+ *                      per wave, which needs K % 8 == 0: other K take the
+ *                      tile form's 2 x 1 block)
  *  BG_TUNE_FP4_TILE:   tile of gemm_fp4_blockscaled(_batched)
  *  BG_TUNE_FP4_SPLITK_TILE: tile of gemm_fp4_blockscaled_splitk's planes
  *  BG_TUNE_W4A16_TILE: tile of gemm_w4a16

@@ -208,11 +208,16 @@ def test_ordered_worked_cases_on_gpu():
     assert int(d32.cpu().numpy().view(np.uint32)[0, 0]) == 3
 
 
-@pytest.mark.parametrize("choice", list(range(12)))
+@pytest.mark.parametrize("choice", list(range(15)))
 def test_every_ordered_register_block_bit_exact(choice, force):
-    """Each register-block variant (the BG_TUNE_ORDERED override) keeps the strict order."""
+    """Each register-block variant (the BG_TUNE_ORDERED override) keeps the strict order.
+    Choices 12-14 are the scalar-A form with 1-3 rows per wave (K % 8 == 0;
+    other K run the tile form): the shapes with K % 8 == 0 cover a ragged last
+    K step (264, 40, 8), rows that do not fill a workgroup's row block, and
+    N % 64 != 0."""
     force(bg.TUNE_ORDERED, choice)
-    for m, n, k in [(1, 1, 1), (37, 70, 300), (150, 33, 65), (145, 256, 2048)]:
+    for m, n, k in [(1, 1, 1), (37, 70, 300), (150, 33, 65), (145, 256, 2048), (37, 70, 264), (150, 33, 40),
+                    (5, 200, 8), (1, 65, 96)]:
         x = synthetic.normal_bf16((m, k), 1.0, 90 + choice, 0)
         w = synthetic.normal_bf16((n, k), 0.5, 90 + choice, 1)
         dx, dw = to_dev_bf16(x), to_dev_bf16(w)
