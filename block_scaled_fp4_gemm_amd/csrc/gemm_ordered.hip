@@ -153,19 +153,22 @@ gemm_ordered_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__
 
 // Second form, for K % 8 == 0: A's rows through the scalar unit. A wave owns
 // RM output rows and 64 columns (one per lane); the four waves of a
-// workgroup take 4*RM consecutive rows and share one 64-column B block staged
-// in LDS as above. A's values arrive by scalar loads and are widened in
-// scalar registers, so the 64 lanes multiply one SGPR operand (a broadcast
-// that costs no LDS bandwidth): per four k a lane reads one 16-byte B vector
-// from LDS, where the tile form reads RM + RN. The order per output is the
-// same strict ascending k.
+// workgroup take 4*RM consecutive rows and share one 64-column B block in LDS
+// (FP32, the same padded pitch as above). A's values arrive by scalar loads
+// and are widened in scalar registers, so the 64 lanes multiply one SGPR
+// operand (a broadcast that costs no LDS bandwidth): per four k a lane reads
+// one 16-byte B vector from LDS, where the tile form reads RM + RN. Each
+// thread loads its 8-element B unit one step ahead into registers and writes
+// it to LDS at the start of the next step, so that load's latency is covered
+// by a step of arithmetic. The order per output is the same strict ascending
+// k.
 //
-// Measured on MI355X against the tile form's best block (same bits):
-// 4510 x 256 x 2048 142 -> 120 us, 2255 x 256 x 2048 104 -> 78 us with RM = 3.
-// Two columns per lane (half the scalar widening per multiply), 16-wide K
-// steps with RM = 4..6, and a pipelined form (B in two LDS buffers, the next
-// step's operands loaded during this step's arithmetic) were all slower; RM =
-// 4 runs out of SGPRs (spills to VGPR lanes).
+// Measured on MI355X against the tile form's best block (same bits), RM = 3:
+// 4510 x 256 x 2048 142 -> 118 us, 2255 x 256 x 2048 104 -> 71 us (loading
+// B at the start of its own step instead: 126 and 79 us). Two columns per
+// lane (half the scalar widening per multiply), 16-wide K steps with RM =
+// 4..6, and a form with B in two LDS buffers and A prefetched as well were
+// all slower; RM = 4 runs out of SGPRs (spills to VGPR lanes).
 template <int RM, bool F32_OUT>
 __global__ void __launch_bounds__(256)
 gemm_ordered_sa_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* C,
@@ -191,9 +194,19 @@ gemm_ordered_sa_kernel(const uint16_t* __restrict__ A, const uint16_t* __restric
 #pragma unroll
     for (int i = 0; i < RM; ++i) acc[i] = 0.0f;
 
+    // this thread's B unit: k0 + 8*bc .. k0 + 8*bc + 7 of column n0 + brow,
+    // zero past N or K (K % 8 == 0: a unit lies wholly inside or past K)
+    const int brow = tid % TN, bc = tid / TN;
+    const int bn = n0 + brow;
+    const uint16_t* bsrc = B + (int64_t)min(bn, N - 1) * K + bc * 8;
+    auto load_b = [&](int kk) -> u32x4 {
+        if (bn < N && kk + bc * 8 < K) return *reinterpret_cast<const u32x4*>(bsrc + kk);
+        return u32x4{0u, 0u, 0u, 0u};
+    };
+    u32x4 bw = load_b(0);
     for (int k0 = 0; k0 < K; k0 += KT) {
         // this step's A words (two k each), zero past K; issued before the
-        // barrier so they arrive while B is staged
+        // barrier so they arrive while B is written to LDS
         uint32_t aw[RM][W];
         const int kw = k0 >> 1;
         if (k0 + KT <= K) {
@@ -209,8 +222,15 @@ gemm_ordered_sa_kernel(const uint16_t* __restrict__ A, const uint16_t* __restric
                 for (int j = 0; j < W; ++j) aw[i][j] = j < nw ? arow[i][kw + j] : 0u;
         }
         __syncthreads();
-        stage<TN, 256, LDK>(sB, B, n0, N, K, k0, true, tid);
+        {
+            float* dst = &sB[brow * LDK + bc * 8];
+            *reinterpret_cast<f32x4*>(dst) = f32x4{bf16_bits_to_f32(bw.x & 0xFFFFu), bf16_bits_to_f32(bw.x >> 16),
+                                                   bf16_bits_to_f32(bw.y & 0xFFFFu), bf16_bits_to_f32(bw.y >> 16)};
+            *reinterpret_cast<f32x4*>(dst + 4) = f32x4{bf16_bits_to_f32(bw.z & 0xFFFFu), bf16_bits_to_f32(bw.z >> 16),
+                                                       bf16_bits_to_f32(bw.w & 0xFFFFu), bf16_bits_to_f32(bw.w >> 16)};
+        }
         __syncthreads();
+        if (k0 + KT < K) bw = load_b(k0 + KT);
         // past K both operands are zero: the products are +0 and leave every
         // accumulator unchanged
 #pragma unroll
