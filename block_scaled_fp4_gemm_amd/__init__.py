@@ -139,7 +139,8 @@ def _dims(t: torch.Tensor, n: int, what: str):
 
 
 def _on_device(*ts) -> None:
-    """Every tensor (None skipped) is contiguous and on the current HIP device."""
+    """Every tensor (None skipped) is on the current HIP device (contiguity is
+    checked where its pointer is taken, in _ptr)."""
     ts = [t for t in ts if t is not None]
     for t in ts:
         if t.device.type != "cuda":

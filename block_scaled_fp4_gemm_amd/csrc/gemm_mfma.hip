@@ -1013,6 +1013,274 @@ gemm_mfma_kernel(KParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Kernel 1b: FP4 x FP4 for few rows (decode shapes), K % 64 == 0, one
+// problem. A 128 x 256 tile, four waves of 128 x 64 (every wave covers all
+// the rows, so each weight column belongs to one wave).
+//
+// What bounds the register-staged kernel at these shapes is the number of
+// L1-to-L2 requests, not bytes: each 64-wide step fetches 32 bytes of packed
+// data and 4 scale bytes from every one of the tile's 384 rows, about 770
+// requests per step against a per-CU ceiling of about 64 in flight at ~300
+// cycles each. Here the packed bytes and scales of four steps (one 128-byte
+// line of data per row) go straight to LDS rings with direct loads whose 64
+// lanes cover 8 whole rows: about 190 requests per step.
+//
+//   raw rings (two groups of 4 steps): A 128 x 128 B, B 256 x 128 B, their
+//     scales 16 B per row; the lane that lands in slot c of a row fetches the
+//     row's logical 16-byte chunk chunk_slot<8>(row, c)
+//   A: each thread dequantizes one 32-element unit per step from the raw ring
+//     into an FP16 stage (two stages), read as MFMA fragments as elsewhere
+//   B: each lane reads its column's 16 bytes and 2 scale bytes of the step
+//     from the ring and dequantizes them into its MFMA operand registers
+//
+// K order inside a step: at sub-step kk, lane half h holds k = 32h + 8kk ..
+// 32h + 8kk + 7 in both operands, so a lane's four sub-steps of B are one
+// 16-byte read. The MFMA sums the same products over the step, in its own
+// order, as with the natural order.
+// ---------------------------------------------------------------------------
+template <int EPI>
+__global__ void __launch_bounds__(256)
+gemm_fp4_dec_kernel(KParams p) {
+    constexpr int BM = 128, BN = 256, WN = 4, NT = 256;
+    constexpr int TN = BN / WN;                   // 64 columns per wave
+    constexpr int FM = BM / 32, FN = TN / 32;     // 4 x 2 MFMA blocks
+    constexpr int G = 4;                          // steps per raw group (one 128-byte line per row)
+    constexpr int R = 2 * G;                      // steps per loop round (both raw buffers)
+    // LDS map (bytes)
+    constexpr int RAW_B = 0;                              // [2][256][128]
+    constexpr int RAW_A = RAW_B + 2 * BN * 128;           // [2][128][128]
+    constexpr int SC_B = RAW_A + 2 * BM * 128;            // [2][256][16]
+    constexpr int SC_A = SC_B + 2 * BN * 16;              // [2][128][16]
+    constexpr int F16_A = SC_A + 2 * BM * 16;             // [2][128][64] FP16
+    constexpr int LDS_BYTES = F16_A + 2 * BM * BK * 2;    // 143360
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+    int tm, tn;
+    tile_of_block(p.tiles_m, p.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int split = blockIdx.y;
+    const int kb = (int)min((int64_t)p.K, (int64_t)split * p.k_chunk);
+    const int ke = (int)min((int64_t)p.K, (int64_t)kb + p.k_chunk);
+    const int nsteps = (ke - kb) / BK;            // whole steps: K and the chunk are multiples of 64
+
+    f32x16 acc[FM][FN];
+    zero_acc(acc);
+
+    if (nsteps > 0) {
+        const int kh = p.K >> 1, ks = p.K >> 4;   // bytes per row: packed data, scales
+        // Buffer resources from the tile's first row to the end of each
+        // matrix: a lane reading past the end (a group that runs past K on
+        // the last row) gets zeros. Rows past M or N are clamped.
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            uniform_ptr(p.Aq + (int64_t)m0 * kh), (short)0, (p.M - m0) * kh, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            uniform_ptr(p.Bq + (int64_t)n0 * kh), (short)0, (p.N - n0) * kh, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+            uniform_ptr(p.SFA + (int64_t)m0 * ks), (short)0, (p.M - m0) * ks, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+            uniform_ptr(p.SFB + (int64_t)n0 * ks), (short)0, (p.N - n0) * ks, 0x00020000);
+        const uint32_t zero = __builtin_amdgcn_readfirstlane(0u);
+
+        // Per-lane row offsets of this wave's direct loads: data segments of
+        // 8 rows (B: wave*8 + j, j < 8; A: wave*4 + j, j < 4), scale
+        // segments of 64 rows (B: segment `wave`; A: segment wave & 1, waves
+        // 0 and 1 only)
+        uint32_t vb[8], va[4];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int row = (wave * 8 + j) * 8 + lane / 8;
+            const int lrow = min(n0 + row, p.N - 1) - n0;
+            vb[j] = (uint32_t)(lrow * kh + chunk_slot<8>(row, lane % 8) * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = (wave * 4 + j) * 8 + lane / 8;
+            const int lrow = min(m0 + row, p.M - 1) - m0;
+            va[j] = (uint32_t)(lrow * kh + chunk_slot<8>(row, lane % 8) * 16);
+        }
+        const uint32_t vsb = (uint32_t)((min(n0 + wave * 64 + lane, p.N - 1) - n0) * ks);
+        const uint32_t vsa = (uint32_t)((min(m0 + (wave & 1) * 64 + lane, p.M - 1) - m0) * ks);
+
+        // group g (steps 4g .. 4g+3 of this split) into raw buffer g % 2
+        auto load_group = [&](int g) {
+            const int k = kb + g * G * BK;
+            const uint32_t kd = (uint32_t)(k >> 1), kss = (uint32_t)(k >> 4);
+            const int buf = g & 1;
+            // Inline assembly: the compiler's wait insertion cannot tell the
+            // ring buffers apart; completion is waited for explicitly (vmcnt)
+            // before the barrier that publishes the group.
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t l = (uint32_t)(uintptr_t)(
+                    (__attribute__((address_space(3))) uint8_t*)(lds + RAW_B + buf * BN * 128 + (wave * 8 + j) * 1024));
+                asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(vb[j] + kd), "s"(rb), "s"(zero),
+                             "{m0}"(l));
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t l = (uint32_t)(uintptr_t)(
+                    (__attribute__((address_space(3))) uint8_t*)(lds + RAW_A + buf * BM * 128 + (wave * 4 + j) * 1024));
+                asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(va[j] + kd), "s"(ra), "s"(zero),
+                             "{m0}"(l));
+            }
+            {
+                const uint32_t l = (uint32_t)(uintptr_t)(
+                    (__attribute__((address_space(3))) uint8_t*)(lds + SC_B + buf * BN * 16 + wave * 1024));
+                asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(vsb + kss), "s"(rsb), "s"(zero),
+                             "{m0}"(l));
+            }
+            if (wave < 2) {
+                const uint32_t l = (uint32_t)(uintptr_t)(
+                    (__attribute__((address_space(3))) uint8_t*)(lds + SC_A + buf * BM * 16 + wave * 1024));
+                asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(vsa + kss), "s"(rsa), "s"(zero),
+                             "{m0}"(l));
+            }
+        };
+
+        // B: this lane's column of each column block, its step-s chunk (2s + h)
+        const int brow0 = wave * TN + (lane & 31);
+        uint32_t boff[FN][G], bsoff[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int row = brow0 + j * 32;
+#pragma unroll
+            for (int st = 0; st < G; ++st) boff[j][st] = (uint32_t)(row * 128 + chunk_slot<8>(row, 2 * st + h) * 16);
+            bsoff[j] = (uint32_t)(row * 16 + 2 * h);
+        }
+        auto read_b = [&](int buf, int st, u32x4 (&w)[FN], uint32_t (&sc)[FN]) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                w[j] = *reinterpret_cast<const u32x4*>(lds + RAW_B + buf * BN * 128 + boff[j][st]);
+                sc[j] = *reinterpret_cast<const uint16_t*>(lds + SC_B + buf * BN * 16 + bsoff[j] + 4 * st);
+            }
+        };
+        using Deq = Fp4Stager<BM, NT, true, 32>;
+        auto deq_b = [&](const u32x4 (&w)[FN], const uint32_t (&sc)[FN], int kk, bf16x8 (&fb)[FN]) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const f16x2 s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[j], 1.0f, false);
+                const f16x2 s16 = kk < 2 ? f16x2{s2.x, s2.x} : f16x2{s2.y, s2.y};
+                fb[j] = __builtin_bit_cast(bf16x8, Deq::deq8(w[j][kk], s16, 0.0f));
+            }
+        };
+
+        // A: thread tid's unit is row tid / 2, elements 32u .. 32u + 31 (u = tid % 2)
+        const int arow = tid >> 1, au = tid & 1;
+        uint32_t aroff[G];
+#pragma unroll
+        for (int st = 0; st < G; ++st) aroff[st] = (uint32_t)(arow * 128 + chunk_slot<8>(arow, 2 * st + au) * 16);
+        const uint32_t asoff = (uint32_t)(arow * 16 + 2 * au);
+        uint32_t adst[4];   // FP16 stage byte offsets of the unit's four 8-element chunks
+#pragma unroll
+        for (int c = 0; c < 4; ++c) adst[c] = (uint32_t)(arow * 128 + chunk_slot<8>(arow, 4 * au + c) * 16);
+        auto read_a = [&](int buf, int st, u32x4& w, uint32_t& sc) {
+            w = *reinterpret_cast<const u32x4*>(lds + RAW_A + buf * BM * 128 + aroff[st]);
+            sc = *reinterpret_cast<const uint16_t*>(lds + SC_A + buf * BM * 16 + asoff + 4 * st);
+        };
+        auto store_a = [&](int stage, const u32x4& w, uint32_t sc) {
+            const f16x2 s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, false);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const f16x2 s16 = c < 2 ? f16x2{s2.x, s2.x} : f16x2{s2.y, s2.y};
+                *reinterpret_cast<u32x4*>(lds + F16_A + stage * BM * BK * 2 + adst[c]) = Deq::deq8(w[c], s16, 0.0f);
+            }
+        };
+
+        // A fragment byte offsets within an FP16 stage: row-block i, sub-step
+        // kk reads chunk 4h + kk of row 32i + (lane & 31); the swizzle of row
+        // 32i + r is that of r with bit 2 flipped for odd i
+        uint32_t aoff[2][4];
+        {
+            const int r = lane & 31;
+#pragma unroll
+            for (int par = 0; par < 2; ++par)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    aoff[par][kk] = (uint32_t)((32 * par + r) * 128 + chunk_slot<8>(32 * par + r, 4 * h + kk) * 16);
+        }
+        auto load_fa = [&](int stage, int kk, bf16x8 (&fa)[FM]) {
+            const uint8_t* base = lds + F16_A + stage * BM * BK * 2;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                fa[i] = *reinterpret_cast<const bf16x8*>(base + aoff[i & 1][kk] + 4096 * (i & ~1));
+        };
+
+        // prologue: group 0 in raw buffer 0, step 0's A in FP16 stage 0 and
+        // its B in registers
+        load_group(0);
+        wait_vmcnt<0>();
+        lds_barrier();
+        u32x4 bw[2][FN], aw;
+        uint32_t bsc[2][FN], asc;
+        read_a(0, 0, aw, asc);
+        store_a(0, aw, asc);
+        read_b(0, 0, bw[0], bsc[0]);
+        lds_barrier();
+        bf16x8 fa[2][FM], fb[2][FN];
+        load_fa(0, 0, fa[0]);
+        deq_b(bw[0], bsc[0], 0, fb[0]);
+
+        // step t = round start + r: raw buffer (r / G), step-in-group r % G,
+        // FP16 stage t % 2, B registers r % 2 (the next step's in (r+1) % 2).
+        // Each sub-step fetches the next one's A fragments and dequantizes
+        // its B operands while its own 8 MFMAs (8 accumulators) run; a
+        // scheduling boundary after each sub-step keeps the MFMAs on one
+        // accumulator 8 apart.
+        // One barrier per step, after sub-step 2: it publishes step t+1's
+        // FP16 stage (written in sub-step 2), so sub-step 3 fetches that
+        // step's first fragments under its own MFMAs. Stage (t+1) % 2 was last
+        // read in sub-step 2 of step t-1, before that step's barrier; a raw
+        // buffer is last read two barriers before its next group is loaded.
+        auto step = [&](int t, auto rc) {
+            constexpr int r = decltype(rc)::value;
+            constexpr int st = r % G, cur = r % 2, nx = (r + 1) % 2;
+            constexpr int nbuf = ((r + 1) % R) / G, nst = (r + 1) % G;   // where step t+1 lives
+            if constexpr (st == 0) load_group(t / G + 1);   // the next group, 4 steps ahead
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<4>([&](auto kc) {
+                constexpr int kk = decltype(kc)::value;
+                if constexpr (kk == 0) read_a(nbuf, nst, aw, asc);           // step t+1's A unit
+                if constexpr (kk == 1) read_b(nbuf, nst, bw[nx], bsc[nx]);   // step t+1's B
+                if constexpr (kk == 2) store_a(nx, aw, asc);
+                if constexpr (kk + 1 < 4) {
+                    load_fa(cur, kk + 1, fa[(kk + 1) & 1]);
+                    deq_b(bw[cur], bsc[cur], kk + 1, fb[(kk + 1) & 1]);
+                } else {
+                    load_fa(nx, 0, fa[0]);                  // sub-step 0 of step t+1
+                    deq_b(bw[nx], bsc[nx], 0, fb[0]);
+                }
+                mfma_block<FM, FN, true>(fa[kk & 1], fb[kk & 1], acc);
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (kk == 2) {
+                    // the next group's loads are complete for this wave
+                    // before the barrier that precedes the first read of that
+                    // group (sub-step 0 of the group's last step)
+                    if constexpr (st == G - 2) wait_vmcnt<0>();
+                    lds_barrier();
+                }
+            });
+        };
+        // whole rounds of R steps, then the remaining steps one by one (no
+        // work past the last step)
+        int t = 0;
+        for (; t + R <= nsteps; t += R)
+            static_for<R>([&](auto rc) { step(t + decltype(rc)::value, rc); });
+        if (t < nsteps)
+            static_for<R - 1>([&](auto rc) {
+                if (t + decltype(rc)::value < nsteps) step(t + decltype(rc)::value, rc);
+            });
+        // direct loads still in flight (a group past the last step) must land
+        // before the epilogue reuses LDS
+        wait_vmcnt<0>();
+    }
+
+    staged_epilogue<EPI, BM, BN, 1, WN, FM, FN, NT, 65536>(p, acc, lds, m0, n0, 0, wave, lane, tid, split);
+}
+
+// ---------------------------------------------------------------------------
 // Kernel 2: BF16 operands with K % 8 == 0. Whole BKS steps are loaded straight
 // into LDS (no VGPR round trip, no LDS write instructions) through a ring of
 // STAGES buffers: the loads for step t + STAGES - 1 are issued while step t
@@ -1938,12 +2206,31 @@ int choose_w4a16(int M, int N, int cus) {
 
 // FP4 tile choices (the BG_TUNE_FP4_TILE and BG_TUNE_FP4_SPLITK_TILE
 // overrides force one when `tuned`).
+template <int EPI>
+hipError_t launch_fp4_dec(const KParams& kp, int splits, hipStream_t stream) {
+    KParams q = kp;
+    q.tiles_m = (kp.M + 127) / 128;
+    q.tiles_n = (kp.N + 255) / 256;
+    dim3 grid((unsigned)(q.tiles_m * q.tiles_n), (unsigned)splits, 1u);
+    hipLaunchKernelGGL((gemm_fp4_dec_kernel<EPI>), grid, dim3(256), 0, stream, q);
+    return hipGetLastError();
+}
+
 template <int SRC>
 hipError_t launch_fp4_src(const KParams& kp, int M, int splits, int batch, bool tuned, hipStream_t stream) {
+    // the decode kernel: one problem, K and the split chunk whole 64-wide steps
+    // (buffer records: each operand's packed bytes below 2^31)
+    const bool dec_ok = SRC == SRC_FP4W && batch == 1 && kp.K % 64 == 0 && kp.k_chunk % 64 == 0 &&
+                        (int64_t)kp.M * (kp.K / 2) < (int64_t(1) << 31) &&
+                        (int64_t)kp.N * (kp.K / 2) < (int64_t(1) << 31);
     // FP32 planes (split-K) for the small-M decode shapes
     if (splits > 1) {
         int sk = tuned ? tune(BG_TUNE_FP4_SPLITK_TILE) : -1;
-        if (sk < 0) sk = M <= 192 ? 3 : 2;
+        // the decode kernel where each split runs at least 12 steps (measured
+        // on MI355X: 128 x 7168 x 16384 at k_splits 8, 32 steps, 47.0 against
+        // 50.7 us; at 9-10 steps the register-staged 128 x 256 tile is ahead)
+        if (sk < 0) sk = dec_ok && M <= 128 && kp.k_chunk >= 12 * BK ? 7 : M <= 192 ? 3 : 2;
+        if (dec_ok && sk == 7) return launch_fp4_dec<EPI_STORE_F32>(kp, splits, stream);
         if constexpr (SRC == SRC_FP4W) {
             switch (sk) {
                 case 0: return launch_cfg<128, 128, 2, 2, EPI_STORE_F32, SRC, 2>(kp, splits, stream);
@@ -1961,6 +2248,7 @@ hipError_t launch_fp4_src(const KParams& kp, int M, int splits, int batch, bool 
     // 256 x 256 tiles with two register sets where the 32-element units
     // leave room for them (3% ahead of one set on 4096 x 4096 x 8192)
     if (cfg < 0) cfg = M <= 192 ? 2 : SRC == SRC_FP4W ? 1 : 0;
+    if (dec_ok && cfg == 10) return launch_fp4_dec<EPI_STORE_BF16>(kp, 1, stream);
     if constexpr (SRC == SRC_FP4W) {
         switch (cfg) {
             case 1: return launch_cfg<256, 256, 2, 4, EPI_STORE_BF16, SRC, 2>(kp, 1, stream, batch);

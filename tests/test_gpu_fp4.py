@@ -75,11 +75,14 @@ FP4_TILE_SHAPES = [(1, 1, 16), (65, 129, 48), (257, 255, 1040), (300, 520, 208),
                    (1, 1, 32), (65, 129, 96), (257, 255, 1056), (300, 520, 224)]
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 5, 6, 7, 8, 9])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 5, 6, 7, 8, 9, 10])
 def test_every_fp4_tile_config(cfg, force):
-    """Each FP4 tile variant (the BG_TUNE_FP4_TILE override) on ragged shapes."""
+    """Each FP4 tile variant (the BG_TUNE_FP4_TILE override) on ragged shapes.
+    10 is the decode kernel (raw FP4 rings in LDS, weights dequantized in
+    registers), which takes K % 64 == 0 (the last four shapes); other K fall
+    back to the default tiles."""
     force(bg.TUNE_FP4_TILE, cfg)
-    for m, n, k in FP4_TILE_SHAPES:
+    for m, n, k in FP4_TILE_SHAPES + [(1, 1, 64), (65, 129, 128), (129, 300, 1024), (128, 520, 320)]:
         a, b = synthetic.fp4_packed(m, k, 70 + cfg, 0), synthetic.fp4_packed(n, k, 70 + cfg, 1)
         sfa = synthetic.e4m3_uniform(m, k // 16, 2 ** -4, 2 ** 4, 70, 4)
         sfb = synthetic.e4m3_uniform(n, k // 16, 2 ** -4, 2 ** 4, 70, 5)
@@ -206,12 +209,17 @@ def test_gemm_on_imported_scales_equals_plain_scales():
     assert_bits_equal(bits_of(c1), bits_of(c2), "imported vs plain scales")
 
 
-@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6, 7])
 def test_every_fp4_splitk_tile(tile, force):
     """Each FP4 split-K tile (the BG_TUNE_FP4_SPLITK_TILE override): planes
-    summed in order equal the exact result on power-of-two scales."""
+    summed in order equal the exact result on power-of-two scales. 7 is the
+    decode kernel (K % 64 == 0 only: 1040 and 1056 fall back); its shapes
+    cover splits of 1-4 steps (a partial last ring round), chunks that start
+    mid-line (448 / 6 = 128-element chunks of a 448-long K), an empty last
+    split and rows past 128."""
     force(bg.TUNE_FP4_SPLITK_TILE, tile)
-    for m, n, k, ks in [(128, 384, 4096, 8), (65, 129, 1040, 3), (300, 520, 2048, 5), (65, 129, 1056, 3)]:
+    for m, n, k, ks in [(128, 384, 4096, 8), (65, 129, 1040, 3), (300, 520, 2048, 5), (65, 129, 1056, 3),
+                        (1, 1, 64, 2), (33, 257, 640, 4), (128, 300, 1280, 3), (100, 70, 448, 6)]:
         a, b = synthetic.fp4_packed(m, k, 150 + tile, 0), synthetic.fp4_packed(n, k, 150 + tile, 1)
         sfa = synthetic.e4m3_choice(m, k // 16, [0x38, 0x40], 150, 4)
         sfb = synthetic.e4m3_choice(n, k // 16, [0x38, 0x40], 150, 5)
