@@ -1014,8 +1014,11 @@ gemm_mfma_kernel(KParams p) {
 
 // ---------------------------------------------------------------------------
 // Kernel 1b: FP4 x FP4 for few rows (decode shapes), K % 64 == 0, one
-// problem. A 128 x 256 tile, four waves of 128 x 64 (every wave covers all
-// the rows, so each weight column belongs to one wave).
+// problem. A 128 x 256 tile, four waves of 128 x 64 (WM = 1: every wave
+// covers all the rows, so each weight column belongs to one wave) or eight
+// waves of 64 x 64 (WM = 2: the two row halves each dequantize the weight
+// columns they share, so that a second wave per SIMD overlaps one wave's
+// dequantization with the other's MFMAs; the default).
 //
 // What bounds the register-staged kernel at these shapes is the number of
 // L1-to-L2 requests, not bytes: each 64-wide step fetches 32 bytes of packed
@@ -1028,8 +1031,9 @@ gemm_mfma_kernel(KParams p) {
 //   raw rings (two groups of 4 steps): A 128 x 128 B, B 256 x 128 B, their
 //     scales 16 B per row; the lane that lands in slot c of a row fetches the
 //     row's logical 16-byte chunk chunk_slot<8>(row, c)
-//   A: each thread dequantizes one 32-element unit per step from the raw ring
-//     into an FP16 stage (two stages), read as MFMA fragments as elsewhere
+//   A: each thread dequantizes one 32-element (WM = 1) or 16-element unit per
+//     step from the raw ring into an FP16 stage (two stages), read as MFMA
+//     fragments as elsewhere
 //   B: each lane reads its column's 16 bytes and 2 scale bytes of the step
 //     from the ring and dequantizes them into its MFMA operand registers
 //
@@ -1038,12 +1042,13 @@ gemm_mfma_kernel(KParams p) {
 // 16-byte read. The MFMA sums the same products over the step, in its own
 // order, as with the natural order.
 // ---------------------------------------------------------------------------
-template <int EPI>
-__global__ void __launch_bounds__(256)
+template <int EPI, int WM>
+__global__ void __launch_bounds__(256 * WM)
 gemm_fp4_dec_kernel(KParams p) {
-    constexpr int BM = 128, BN = 256, WN = 4, NT = 256;
-    constexpr int TN = BN / WN;                   // 64 columns per wave
-    constexpr int FM = BM / 32, FN = TN / 32;     // 4 x 2 MFMA blocks
+    constexpr int BM = 128, BN = 256, WN = 4, NW = WM * WN, NT = 64 * NW;
+    constexpr int TM = BM / WM, TN = BN / WN;     // 128 (or 64) x 64 per wave
+    constexpr int FM = TM / 32, FN = TN / 32;     // 4 (or 2) x 2 MFMA blocks
+    static_assert(WM == 1 || WM == 2, "one or two row halves");
     constexpr int G = 4;                          // steps per raw group (one 128-byte line per row)
     constexpr int R = 2 * G;                      // steps per loop round (both raw buffers)
     // LDS map (bytes)
@@ -1058,6 +1063,7 @@ gemm_fp4_dec_kernel(KParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+    const int wm = wave / WN, wn = wave % WN;
     int tm, tn;
     tile_of_block(p.tiles_m, p.tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
@@ -1085,24 +1091,26 @@ gemm_fp4_dec_kernel(KParams p) {
         const uint32_t zero = __builtin_amdgcn_readfirstlane(0u);
 
         // Per-lane row offsets of this wave's direct loads: data segments of
-        // 8 rows (B: wave*8 + j, j < 8; A: wave*4 + j, j < 4), scale
-        // segments of 64 rows (B: segment `wave`; A: segment wave & 1, waves
-        // 0 and 1 only)
-        uint32_t vb[8], va[4];
+        // 8 rows (B: 32 segments, A: 16, dealt out evenly), scale segments of
+        // 64 rows (B: segment `wave` of waves 0-3; A: segments 0 and 1, from
+        // waves 0-1 with four waves, 4-5 with eight)
+        constexpr int SB = 32 / NW, SA = 16 / NW;   // data segments per wave
+        const int asw = NW == 8 ? wave - 4 : wave;   // A-scale segment of this wave (0 or 1 loads)
+        uint32_t vb[SB], va[SA];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int row = (wave * 8 + j) * 8 + lane / 8;
+        for (int j = 0; j < SB; ++j) {
+            const int row = (wave * SB + j) * 8 + lane / 8;
             const int lrow = min(n0 + row, p.N - 1) - n0;
             vb[j] = (uint32_t)(lrow * kh + chunk_slot<8>(row, lane % 8) * 16);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = (wave * 4 + j) * 8 + lane / 8;
+        for (int j = 0; j < SA; ++j) {
+            const int row = (wave * SA + j) * 8 + lane / 8;
             const int lrow = min(m0 + row, p.M - 1) - m0;
             va[j] = (uint32_t)(lrow * kh + chunk_slot<8>(row, lane % 8) * 16);
         }
-        const uint32_t vsb = (uint32_t)((min(n0 + wave * 64 + lane, p.N - 1) - n0) * ks);
-        const uint32_t vsa = (uint32_t)((min(m0 + (wave & 1) * 64 + lane, p.M - 1) - m0) * ks);
+        const uint32_t vsb = (uint32_t)((min(n0 + (wave & 3) * 64 + lane, p.N - 1) - n0) * ks);
+        const uint32_t vsa = (uint32_t)((min(m0 + (asw & 1) * 64 + lane, p.M - 1) - m0) * ks);
 
         // group g (steps 4g .. 4g+3 of this split) into raw buffer g % 2
         auto load_group = [&](int g) {
@@ -1113,35 +1121,35 @@ gemm_fp4_dec_kernel(KParams p) {
             // ring buffers apart; completion is waited for explicitly (vmcnt)
             // before the barrier that publishes the group.
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < SB; ++j) {
                 const uint32_t l = (uint32_t)(uintptr_t)(
-                    (__attribute__((address_space(3))) uint8_t*)(lds + RAW_B + buf * BN * 128 + (wave * 8 + j) * 1024));
+                    (__attribute__((address_space(3))) uint8_t*)(lds + RAW_B + buf * BN * 128 + (wave * SB + j) * 1024));
                 asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(vb[j] + kd), "s"(rb), "s"(zero),
                              "{m0}"(l));
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < SA; ++j) {
                 const uint32_t l = (uint32_t)(uintptr_t)(
-                    (__attribute__((address_space(3))) uint8_t*)(lds + RAW_A + buf * BM * 128 + (wave * 4 + j) * 1024));
+                    (__attribute__((address_space(3))) uint8_t*)(lds + RAW_A + buf * BM * 128 + (wave * SA + j) * 1024));
                 asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(va[j] + kd), "s"(ra), "s"(zero),
                              "{m0}"(l));
             }
-            {
+            if (wave < 4) {
                 const uint32_t l = (uint32_t)(uintptr_t)(
                     (__attribute__((address_space(3))) uint8_t*)(lds + SC_B + buf * BN * 16 + wave * 1024));
                 asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(vsb + kss), "s"(rsb), "s"(zero),
                              "{m0}"(l));
             }
-            if (wave < 2) {
+            if (asw >= 0 && asw < 2) {
                 const uint32_t l = (uint32_t)(uintptr_t)(
-                    (__attribute__((address_space(3))) uint8_t*)(lds + SC_A + buf * BM * 16 + wave * 1024));
+                    (__attribute__((address_space(3))) uint8_t*)(lds + SC_A + buf * BM * 16 + asw * 1024));
                 asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(vsa + kss), "s"(rsa), "s"(zero),
                              "{m0}"(l));
             }
         };
 
         // B: this lane's column of each column block, its step-s chunk (2s + h)
-        const int brow0 = wave * TN + (lane & 31);
+        const int brow0 = wn * TN + (lane & 31);
         uint32_t boff[FN][G], bsoff[FN];
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
@@ -1157,7 +1165,7 @@ gemm_fp4_dec_kernel(KParams p) {
                 sc[j] = *reinterpret_cast<const uint16_t*>(lds + SC_B + buf * BN * 16 + bsoff[j] + 4 * st);
             }
         };
-        using Deq = Fp4Stager<BM, NT, true, 32>;
+        using Deq = Fp4Stager<BM, 256, true, 32>;
         auto deq_b = [&](const u32x4 (&w)[FN], const uint32_t (&sc)[FN], int kk, bf16x8 (&fb)[FN]) {
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
@@ -1167,23 +1175,32 @@ gemm_fp4_dec_kernel(KParams p) {
             }
         };
 
-        // A: thread tid's unit is row tid / 2, elements 32u .. 32u + 31 (u = tid % 2)
-        const int arow = tid >> 1, au = tid & 1;
+        // A: thread tid's unit is row tid / UPR, elements UE*u .. UE*u + UE - 1
+        // (u = tid % UPR): 32 elements with four waves, 16 with eight
+        constexpr int UE = 32 / WM, UPR = BK / UE;
+        const int arow = tid / UPR, au = tid % UPR;
         uint32_t aroff[G];
 #pragma unroll
-        for (int st = 0; st < G; ++st) aroff[st] = (uint32_t)(arow * 128 + chunk_slot<8>(arow, 2 * st + au) * 16);
-        const uint32_t asoff = (uint32_t)(arow * 16 + 2 * au);
-        uint32_t adst[4];   // FP16 stage byte offsets of the unit's four 8-element chunks
+        for (int st = 0; st < G; ++st)
+            // step st's packed bytes of the row start at 32 st; the unit's at
+            // 32 st + UE*au/2: 16-byte chunk 2 st + UE*au/32, byte (UE*au/2) % 16
+            aroff[st] = (uint32_t)(arow * 128 + chunk_slot<8>(arow, 2 * st + (UE * au) / 32) * 16 + ((UE * au) / 2) % 16);
+        const uint32_t asoff = (uint32_t)(arow * 16 + (UE * au) / 16);
+        uint32_t adst[UE / 8];   // FP16 stage byte offsets of the unit's 8-element chunks
 #pragma unroll
-        for (int c = 0; c < 4; ++c) adst[c] = (uint32_t)(arow * 128 + chunk_slot<8>(arow, 4 * au + c) * 16);
-        auto read_a = [&](int buf, int st, u32x4& w, uint32_t& sc) {
-            w = *reinterpret_cast<const u32x4*>(lds + RAW_A + buf * BM * 128 + aroff[st]);
-            sc = *reinterpret_cast<const uint16_t*>(lds + SC_A + buf * BM * 16 + asoff + 4 * st);
+        for (int c = 0; c < UE / 8; ++c) adst[c] = (uint32_t)(arow * 128 + chunk_slot<8>(arow, (UE / 8) * au + c) * 16);
+        typedef uint32_t AWords __attribute__((ext_vector_type(UE / 8)));
+        auto read_a = [&](int buf, int st, AWords& w, uint32_t& sc) {
+            w = *reinterpret_cast<const AWords*>(lds + RAW_A + buf * BM * 128 + aroff[st]);
+            if constexpr (UE == 32)
+                sc = *reinterpret_cast<const uint16_t*>(lds + SC_A + buf * BM * 16 + asoff + 4 * st);
+            else
+                sc = *(lds + SC_A + buf * BM * 16 + asoff + 4 * st);
         };
-        auto store_a = [&](int stage, const u32x4& w, uint32_t sc) {
+        auto store_a = [&](int stage, const AWords& w, uint32_t sc) {
             const f16x2 s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, false);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
+            for (int c = 0; c < UE / 8; ++c) {
                 const f16x2 s16 = c < 2 ? f16x2{s2.x, s2.x} : f16x2{s2.y, s2.y};
                 *reinterpret_cast<u32x4*>(lds + F16_A + stage * BM * BK * 2 + adst[c]) = Deq::deq8(w[c], s16, 0.0f);
             }
@@ -1202,7 +1219,7 @@ gemm_fp4_dec_kernel(KParams p) {
                     aoff[par][kk] = (uint32_t)((32 * par + r) * 128 + chunk_slot<8>(32 * par + r, 4 * h + kk) * 16);
         }
         auto load_fa = [&](int stage, int kk, bf16x8 (&fa)[FM]) {
-            const uint8_t* base = lds + F16_A + stage * BM * BK * 2;
+            const uint8_t* base = lds + F16_A + stage * BM * BK * 2 + 4096 * FM * wm;
 #pragma unroll
             for (int i = 0; i < FM; ++i)
                 fa[i] = *reinterpret_cast<const bf16x8*>(base + aoff[i & 1][kk] + 4096 * (i & ~1));
@@ -1213,7 +1230,8 @@ gemm_fp4_dec_kernel(KParams p) {
         load_group(0);
         wait_vmcnt<0>();
         lds_barrier();
-        u32x4 bw[2][FN], aw;
+        u32x4 bw[2][FN];
+        AWords aw;
         uint32_t bsc[2][FN], asc;
         read_a(0, 0, aw, asc);
         store_a(0, aw, asc);
@@ -1277,7 +1295,7 @@ gemm_fp4_dec_kernel(KParams p) {
         wait_vmcnt<0>();
     }
 
-    staged_epilogue<EPI, BM, BN, 1, WN, FM, FN, NT, 65536>(p, acc, lds, m0, n0, 0, wave, lane, tid, split);
+    staged_epilogue<EPI, BM, BN, WM, WN, FM, FN, NT, 65536>(p, acc, lds, m0, n0, wm, wn, lane, tid, split);
 }
 
 // ---------------------------------------------------------------------------
@@ -2206,13 +2224,13 @@ int choose_w4a16(int M, int N, int cus) {
 
 // FP4 tile choices (the BG_TUNE_FP4_TILE and BG_TUNE_FP4_SPLITK_TILE
 // overrides force one when `tuned`).
-template <int EPI>
+template <int EPI, int WM = 1>
 hipError_t launch_fp4_dec(const KParams& kp, int splits, hipStream_t stream) {
     KParams q = kp;
     q.tiles_m = (kp.M + 127) / 128;
     q.tiles_n = (kp.N + 255) / 256;
     dim3 grid((unsigned)(q.tiles_m * q.tiles_n), (unsigned)splits, 1u);
-    hipLaunchKernelGGL((gemm_fp4_dec_kernel<EPI>), grid, dim3(256), 0, stream, q);
+    hipLaunchKernelGGL((gemm_fp4_dec_kernel<EPI, WM>), grid, dim3(256 * WM), 0, stream, q);
     return hipGetLastError();
 }
 
@@ -2226,11 +2244,13 @@ hipError_t launch_fp4_src(const KParams& kp, int M, int splits, int batch, bool 
     // FP32 planes (split-K) for the small-M decode shapes
     if (splits > 1) {
         int sk = tuned ? tune(BG_TUNE_FP4_SPLITK_TILE) : -1;
-        // the decode kernel where each split runs at least 12 steps (measured
-        // on MI355X: 128 x 7168 x 16384 at k_splits 8, 32 steps, 47.0 against
-        // 50.7 us; at 9-10 steps the register-staged 128 x 256 tile is ahead)
-        if (sk < 0) sk = dec_ok && M <= 128 && kp.k_chunk >= 12 * BK ? 7 : M <= 192 ? 3 : 2;
+        // the decode kernel with eight waves for M <= 128 (measured on MI355X,
+        // interleaved, against the register-staged 128 x 256 tile: 128 x 7168 x
+        // 16384 at k_splits 8 43.8 against 49.5 us, 128 x 4096 x 7168 at 12
+        // 25.6 against 26.7 us; ahead at every k_splits from 4 to 16)
+        if (sk < 0) sk = dec_ok && M <= 128 ? 8 : M <= 192 ? 3 : 2;
         if (dec_ok && sk == 7) return launch_fp4_dec<EPI_STORE_F32>(kp, splits, stream);
+        if (dec_ok && sk == 8) return launch_fp4_dec<EPI_STORE_F32, 2>(kp, splits, stream);
         if constexpr (SRC == SRC_FP4W) {
             switch (sk) {
                 case 0: return launch_cfg<128, 128, 2, 2, EPI_STORE_F32, SRC, 2>(kp, splits, stream);
@@ -2249,6 +2269,7 @@ hipError_t launch_fp4_src(const KParams& kp, int M, int splits, int batch, bool 
     // leave room for them (3% ahead of one set on 4096 x 4096 x 8192)
     if (cfg < 0) cfg = M <= 192 ? 2 : SRC == SRC_FP4W ? 1 : 0;
     if (dec_ok && cfg == 10) return launch_fp4_dec<EPI_STORE_BF16>(kp, 1, stream);
+    if (dec_ok && cfg == 11) return launch_fp4_dec<EPI_STORE_BF16, 2>(kp, 1, stream);
     if constexpr (SRC == SRC_FP4W) {
         switch (cfg) {
             case 1: return launch_cfg<256, 256, 2, 4, EPI_STORE_BF16, SRC, 2>(kp, 1, stream, batch);

@@ -422,10 +422,11 @@ const char* bg_status_string(bg_status status);
  *                      the tile form, 12-14 the scalar-A form with 1-3 rows
  *                      per wave, which needs K % 8 == 0: other K take the
  *                      tile form's 2 x 1 block)
- *  BG_TUNE_FP4_TILE:   tile of gemm_fp4_blockscaled(_batched) (10: the decode
- *                      kernel, one problem with K % 64 == 0)
- *  BG_TUNE_FP4_SPLITK_TILE: tile of gemm_fp4_blockscaled_splitk's planes (7:
- *                      the decode kernel, K % 64 == 0)
+ *  BG_TUNE_FP4_TILE:   tile of gemm_fp4_blockscaled(_batched) (10, 11: the
+ *                      decode kernel with four or eight waves, one problem
+ *                      with K % 64 == 0)
+ *  BG_TUNE_FP4_SPLITK_TILE: tile of gemm_fp4_blockscaled_splitk's planes (7, 8:
+ *                      the decode kernel with four or eight waves, K % 64 == 0)
  *  BG_TUNE_W4A16_TILE: tile of gemm_w4a16
  *  BG_TUNE_STREAMK_TILE: tile of gemm_bf16_streamk (23: 128 x 128, 10: 256 x 128;
  *                      other values select 128 x 128)

@@ -75,12 +75,12 @@ FP4_TILE_SHAPES = [(1, 1, 16), (65, 129, 48), (257, 255, 1040), (300, 520, 208),
                    (1, 1, 32), (65, 129, 96), (257, 255, 1056), (300, 520, 224)]
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 5, 6, 7, 8, 9, 10])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 5, 6, 7, 8, 9, 10, 11])
 def test_every_fp4_tile_config(cfg, force):
     """Each FP4 tile variant (the BG_TUNE_FP4_TILE override) on ragged shapes.
-    10 is the decode kernel (raw FP4 rings in LDS, weights dequantized in
-    registers), which takes K % 64 == 0 (the last four shapes); other K fall
-    back to the default tiles."""
+    10 and 11 are the decode kernel with four or eight waves (raw FP4 rings in
+    LDS, weights dequantized in registers), which takes K % 64 == 0 (the last
+    four shapes); other K fall back to the default tiles."""
     force(bg.TUNE_FP4_TILE, cfg)
     for m, n, k in FP4_TILE_SHAPES + [(1, 1, 64), (65, 129, 128), (129, 300, 1024), (128, 520, 320)]:
         a, b = synthetic.fp4_packed(m, k, 70 + cfg, 0), synthetic.fp4_packed(n, k, 70 + cfg, 1)
@@ -209,11 +209,12 @@ def test_gemm_on_imported_scales_equals_plain_scales():
     assert_bits_equal(bits_of(c1), bits_of(c2), "imported vs plain scales")
 
 
-@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6, 7, 8])
 def test_every_fp4_splitk_tile(tile, force):
     """Each FP4 split-K tile (the BG_TUNE_FP4_SPLITK_TILE override): planes
-    summed in order equal the exact result on power-of-two scales. 7 is the
-    decode kernel (K % 64 == 0 only: 1040 and 1056 fall back); its shapes
+    summed in order equal the exact result on power-of-two scales. 7 and 8
+    are the decode kernel with four or eight waves (K % 64 == 0 only: 1040
+    and 1056 fall back); its shapes
     cover splits of 1-4 steps (a partial last ring round), chunks that start
     mid-line (448 / 6 = 128-element chunks of a 448-long K), an empty last
     split and rows past 128."""
