@@ -209,6 +209,39 @@ def test_gemm_on_imported_scales_equals_plain_scales():
     assert_bits_equal(bits_of(c1), bits_of(c2), "imported vs plain scales")
 
 
+def _decode_sweep_cases():
+    """Seeded (M, N, K, k_splits) draws for the decode kernel: M up to 128
+    (one row tile) and a few past it, N around the 256-column tile, K a
+    multiple of 64 (1 to 40 steps), splits from 1 to 9 (short, partial-group
+    and empty splits)."""
+    rng = np.random.default_rng(2024)
+    cases = []
+    for _ in range(24):
+        m = int(rng.choice([1, 2, 31, 32, 33, 64, 95, 127, 128, 129, 200]))
+        n = int(rng.choice([1, 16, 63, 200, 255, 256, 257, 511, 700]))
+        k = 64 * int(rng.integers(1, 41))
+        ks = int(rng.integers(1, 10))
+        cases.append((m, n, k, ks))
+    return cases
+
+
+@pytest.mark.parametrize("tile", [7, 8])
+def test_decode_kernel_shape_sweep_bit_exact(tile, force):
+    """The decode kernel (split-K tiles 7 and 8, forced) over 24 seeded shapes,
+    on power-of-two scales (every product and sum exact in FP32): each output
+    bit-identical to the oracle's."""
+    force(bg.TUNE_FP4_SPLITK_TILE, tile)
+    for i, (m, n, k, ks) in enumerate(_decode_sweep_cases()):
+        print(f"decode sweep tile={tile} m={m} n={n} k={k} ks={ks}", flush=True)
+        a, b = synthetic.fp4_packed(m, k, 1700 + i, 0), synthetic.fp4_packed(n, k, 1700 + i, 1)
+        sfa = synthetic.e4m3_choice(m, k // 16, [0x30, 0x38, 0x40], 1700 + i, 4)
+        sfb = synthetic.e4m3_choice(n, k // 16, [0x30, 0x38, 0x40], 1700 + i, 5)
+        c = bg.gemm_fp4_blockscaled_splitk(to_dev_u8(a), to_dev_u8(sfa), to_dev_u8(b), to_dev_u8(sfb), ks)
+        torch.cuda.synchronize()
+        want = oracle.f32_to_bf16(oracle.gemm_fp4_ref(a, sfa, b, sfb).astype(np.float32))
+        assert_bits_equal(bits_of(c), want, f"decode sweep tile {tile} {m}x{n}x{k} ks={ks}")
+
+
 @pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6, 7, 8])
 def test_every_fp4_splitk_tile(tile, force):
     """Each FP4 split-K tile (the BG_TUNE_FP4_SPLITK_TILE override): planes
