@@ -229,6 +229,28 @@ def test_every_ordered_register_block_bit_exact(choice, force):
         assert_bits_equal(bits_of(c16), oracle.f32_to_bf16(want), f"ord bf16 {choice} {m}x{n}x{k}")
 
 
+@pytest.mark.parametrize("choice", [-1, 12, 13, 14])
+def test_ordered_scalar_a_shape_sweep(choice, force):
+    """The scalar-A form (forced, and the automatic choice) over 16 seeded
+    shapes with K % 8 == 0: rows that do not fill a workgroup's 4*RM rows,
+    N % 64 != 0, and ragged last K steps (K % 32 in 8, 16, 24); FP32 sums
+    bit-identical to the strict-order oracle."""
+    if choice >= 0:
+        force(bg.TUNE_ORDERED, choice)
+    rng = np.random.default_rng(77)
+    for i in range(16):
+        m = int(rng.integers(1, 300))
+        n = int(rng.integers(1, 200))
+        k = 8 * int(rng.integers(1, 90))
+        x = synthetic.normal_bf16((m, k), 1.0, 400 + i, 0)
+        w = synthetic.normal_bf16((n, k), 0.5, 400 + i, 1)
+        c32 = bg.gemm_bf16_ordered_f32(to_dev_bf16(x), to_dev_bf16(w))
+        torch.cuda.synchronize()
+        want = oracle.gemm_ordered_f32(x, w)
+        assert_bits_equal(c32.cpu().numpy().view(np.uint32), want.view(np.uint32),
+                          f"ordered sweep {choice} {m}x{n}x{k}")
+
+
 @pytest.mark.parametrize("count", [1, 7, 8, 9, 1000, 4099])
 def test_bf16_scaled_add_matches_epilogue_definition(count):
     out = synthetic.normal_bf16((count,), 1.0, 11, 2)
