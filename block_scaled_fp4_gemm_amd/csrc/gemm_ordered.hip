@@ -160,15 +160,17 @@ gemm_ordered_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__
 // one 16-byte B vector from LDS, where the tile form reads RM + RN. Each
 // thread loads its 8-element B unit one step ahead into registers and writes
 // it to LDS at the start of the next step, so that load's latency is covered
-// by a step of arithmetic. The order per output is the same strict ascending
-// k.
+// by a step of arithmetic; the B block alternates between two LDS buffers, so
+// each step needs one barrier. The order per output is the same strict
+// ascending k.
 //
 // Measured on MI355X against the tile form's best block (same bits), RM = 3:
-// 4510 x 256 x 2048 142 -> 118 us, 2255 x 256 x 2048 104 -> 71 us (loading
-// B at the start of its own step instead: 126 and 79 us). Two columns per
-// lane (half the scalar widening per multiply), 16-wide K steps with RM =
-// 4..6, and a form with B in two LDS buffers and A prefetched as well were
-// all slower; RM = 4 runs out of SGPRs (spills to VGPR lanes).
+// 4510 x 256 x 2048 142 -> 116 us, 2255 x 256 x 2048 104 -> 68 us (one B
+// buffer and two barriers per step: 121 and 73 us; B loaded at the start of
+// its own step as well: 126 and 79 us). Two columns per lane (half the
+// scalar widening per multiply), 16-wide K steps with RM = 4..6, and a form
+// that also prefetched A's words a step ahead were all slower; RM = 4 runs
+// out of SGPRs (spills to VGPR lanes).
 template <int RM, bool F32_OUT>
 __global__ void __launch_bounds__(256)
 gemm_ordered_sa_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* C,
@@ -176,7 +178,7 @@ gemm_ordered_sa_kernel(const uint16_t* __restrict__ A, const uint16_t* __restric
     constexpr int TN = 64;
     constexpr int LDK = KT + 4;
     constexpr int W = KT / 2;   // 32-bit words of one A row per step
-    __shared__ __attribute__((aligned(16))) float sB[TN * LDK];
+    __shared__ __attribute__((aligned(16))) float sBuf[2 * TN * LDK];   // two B buffers: one barrier per step
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -204,7 +206,11 @@ gemm_ordered_sa_kernel(const uint16_t* __restrict__ A, const uint16_t* __restric
         return u32x4{0u, 0u, 0u, 0u};
     };
     u32x4 bw = load_b(0);
-    for (int k0 = 0; k0 < K; k0 += KT) {
+    int buf = 0;
+    for (int k0 = 0; k0 < K; k0 += KT, buf ^= 1) {
+        // buffer `buf` was last read in the step before the previous one,
+        // which every wave finished before the previous step's barrier
+        float* sB = sBuf + buf * TN * LDK;
         // this step's A words (two k each), zero past K; issued before the
         // barrier so they arrive while B is written to LDS
         uint32_t aw[RM][W];
@@ -221,7 +227,6 @@ gemm_ordered_sa_kernel(const uint16_t* __restrict__ A, const uint16_t* __restric
 #pragma unroll
                 for (int j = 0; j < W; ++j) aw[i][j] = j < nw ? arow[i][kw + j] : 0u;
         }
-        __syncthreads();
         {
             float* dst = &sB[brow * LDK + bc * 8];
             *reinterpret_cast<f32x4*>(dst) = f32x4{bf16_bits_to_f32(bw.x & 0xFFFFu), bf16_bits_to_f32(bw.x >> 16),
