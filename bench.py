@@ -530,33 +530,48 @@ def measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream, oracle_seconds
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     spread = {}
 
-    def timed(fn, reps=50):
-        """Median per-call time in us over `reps` calls, warm and cold
-        (p20/p80 kept in `spread`), after 5 untimed calls. Calls are
-        enqueued back to back (no host synchronisation between them), each
-        inside its own pair of events on the stream; cold calls are preceded
-        by a 1 GiB write that evicts the L2s and the 256 MB Infinity Cache."""
+    def timed(fn, reps=50, batch=10, batches=8):
+        """Per-call time in us, warm and cold (p20/p80 kept in `spread`),
+        after 5 untimed calls, with calls enqueued back to back (no host
+        synchronisation between them). Warm: `batches` pairs of events on the
+        stream, each around `batch` consecutive calls; the median per-call
+        time of the batches. An event pair around every single call adds about
+        2 us to each call (measured on 16-40 us calls), which a batch spreads
+        over its calls; the step itself is timed the same way. Cold: `reps`
+        calls, each preceded by a 1 GiB write that evicts the L2s and the
+        256 MB Infinity Cache and inside its own pair of events; the median."""
         for _ in range(5):
             fn()
         torch.cuda.synchronize()
         res = {}
         gc.collect()
         gc.disable()
-        for mode in ("warm", "cold"):
-            pairs = []
-            for _ in range(reps):
-                if mode == "cold":
-                    flush.zero_()
-                s = torch.cuda.Event(enable_timing=True)
-                e = torch.cuda.Event(enable_timing=True)
-                s.record(stream)
+        pairs = []
+        for _ in range(batches):
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            for _ in range(batch):
                 fn()
-                e.record(stream)
-                pairs.append((s, e))
-            torch.cuda.synchronize()
-            us = [a.elapsed_time(b) * 1e3 for a, b in pairs]
-            res[mode] = float(np.median(us))
-            spread[mode] = [round(float(np.percentile(us, 20)), 2), round(float(np.percentile(us, 80)), 2)]
+            e.record(stream)
+            pairs.append((s, e))
+        torch.cuda.synchronize()
+        us = [a.elapsed_time(b) * 1e3 / batch for a, b in pairs]
+        res["warm"] = float(np.median(us))
+        spread["warm"] = [round(float(np.percentile(us, 20)), 2), round(float(np.percentile(us, 80)), 2)]
+        pairs = []
+        for _ in range(reps):
+            flush.zero_()
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            fn()
+            e.record(stream)
+            pairs.append((s, e))
+        torch.cuda.synchronize()
+        us = [a.elapsed_time(b) * 1e3 for a, b in pairs]
+        res["cold"] = float(np.median(us))
+        spread["cold"] = [round(float(np.percentile(us, 20)), 2), round(float(np.percentile(us, 80)), 2)]
         gc.enable()
         return res["warm"], res["cold"]
 

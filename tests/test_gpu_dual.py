@@ -52,7 +52,7 @@ def test_dual_matches_oracle_and_single_calls(m, n, k):
 # every direct tile configuration of the dense table, forced through the
 # tuning hook (0 is the register-staged tile: the dual call then runs two
 # ordinary launches)
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 6, 8, 9, 10, 12, 14, 17, 23, 27, 28])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 6, 8, 9, 10, 12, 14, 17, 23, 24, 27, 28])
 def test_dual_every_tile_config(cfg, force):
     force(bg.TUNE_TILE, cfg)
     for m, n, k in [(65, 257, 136), (257, 300, 520), (33, 70, 64), (130, 260, 512)]:

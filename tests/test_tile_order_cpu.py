@@ -18,7 +18,8 @@ GRIDS = sorted(set([
     tiles(5120, 11008, 256, 256, dual=True),     # gate+up dual call: 20 x 86
     tiles(5120, 9472, 256, 256), tiles(5120, 1536, 256, 128),   # gate/up column split
     tiles(5120, 2048, 160, 256),                 # down and Q/O
-    tiles(5120, 512, 128, 128),                  # K/V
+    tiles(5120, 512, 96, 128),                   # K/V
+    tiles(5120, 512, 128, 128),                  # K/V, the previous tile
     tiles(2048, 17408, 64, 128),                 # LoRA fold
     tiles(4096, 4096, 256, 256),                 # FP4
     tiles(128, 7168, 128, 256), tiles(128, 4096, 128, 256),   # FP4 decode
