@@ -495,9 +495,9 @@ def profile_rows(bg, synthetic, torch, up16, u8, dev):
     calls.append(("fp4_decode_k8", lambda: bg.gemm_fp4_blockscaled_splitk(DA, DSA, DB, DSB, 8, workspace=WS)))
     ea, esa, eb, esb = synthetic.fp4_decode(m=128, n=4096, k=7168)
     EA, ESA, EB, ESB = u8(ea), u8(esa), u8(eb), u8(esb)
-    WS2 = torch.empty(12 * 128 * 4096, dtype=torch.float32, device=dev)
-    calls.append(("fp4_decode_4096_k12",
-                  lambda: bg.gemm_fp4_blockscaled_splitk(EA, ESA, EB, ESB, 12, workspace=WS2)))
+    WS2 = torch.empty(8 * 128 * 4096, dtype=torch.float32, device=dev)
+    calls.append(("fp4_decode_4096_k8",
+                  lambda: bg.gemm_fp4_blockscaled_splitk(EA, ESA, EB, ESB, 8, workspace=WS2)))
     wa, wb, wsb, s2 = synthetic.w4a16_gemm()
     WA, WB, WSB = up16(wa), u8(wb), u8(wsb)
     calls.append(("w4a16", lambda: bg.gemm_w4a16(WA, WB, WSB, s2)))
@@ -701,7 +701,7 @@ def measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream, oracle_seconds
     del A4, SA, B4, SB, C
 
     # the kernelbot page's decode shapes (M = 128) through FP4 split-K, best
-    # k_splits of 4/8/12/16. Bounds: the 16-bit MFMA rate (exact dequantization)
+    # k_splits of 4/6/7/8/12/16. Bounds: the 16-bit MFMA rate (exact dequantization)
     # and HBM for the algorithmic bytes (A, B, scales read once, C written once).
     for m, n, k in ((128, 7168, 16384), (128, 4096, 7168)):
         ad, sad, bd, sbd = synthetic.fp4_decode(m=m, n=n, k=k)
@@ -709,7 +709,7 @@ def measure_rows(bg, synthetic, torch, np, up16, u8, dev, stream, oracle_seconds
         C = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         WS = torch.empty((16, m, n), dtype=torch.float32, device=dev)
         best = None
-        for ks in (4, 8, 12, 16):
+        for ks in (4, 6, 7, 8, 12, 16):
             w, c = timed(lambda: bg.gemm_fp4_blockscaled_splitk(AD, SAD, BD, SBD, ks, workspace=WS[:ks], out=C))
             if best is None or w < best[1]:
                 best = (ks, w, c, dict(spread))

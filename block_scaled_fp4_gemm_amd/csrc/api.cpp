@@ -381,8 +381,9 @@ bg_status gemm_fp4_blockscaled_batched(const uint8_t* A, const uint8_t* SFA, con
     if (M == 0 || N == 0 || L == 0) return BG_OK;
     bg_status s = check_fp4(A, SFA, B, SFB, C, (uint64_t)M * N * 2, M, N, K, L);
     if (s != BG_OK) return s;
-    if ((s = check_device()) != BG_OK) return s;
-    bg::Fp4Problem p{A, SFA, B, SFB, C, M, N, K, K, 1, L};
+    uint32_t cus = 0;
+    if ((s = check_device(&cus)) != BG_OK) return s;
+    bg::Fp4Problem p{A, SFA, B, SFB, C, M, N, K, K, 1, L, cus};
     return launched(bg::launch_fp4(p, (hipStream_t)stream));
 }
 
@@ -395,9 +396,10 @@ bg_status gemm_fp4_blockscaled_splitk(const uint8_t* A, const uint8_t* SFA, cons
     if (M == 0 || N == 0) return BG_OK;
     bg_status s = check_fp4(A, SFA, B, SFB, C, (uint64_t)M * N * 2, M, N, K, 1);
     if (s != BG_OK) return s;
+    uint32_t cus = 0;
     if (k_splits == 1) {
-        if ((s = check_device()) != BG_OK) return s;
-        bg::Fp4Problem p{A, SFA, B, SFB, C, M, N, K, K, 1, 1};
+        if ((s = check_device(&cus)) != BG_OK) return s;
+        bg::Fp4Problem p{A, SFA, B, SFB, C, M, N, K, K, 1, 1, cus};
         return launched(bg::launch_fp4(p, (hipStream_t)stream));
     }
     const uint64_t per = ((uint64_t)K + k_splits - 1) / k_splits;
@@ -410,9 +412,9 @@ bg_status gemm_fp4_blockscaled_splitk(const uint8_t* A, const uint8_t* SFA, cons
         overlap(rw, range_of(B, (uint64_t)N * (K / 2))) || overlap(rw, range_of(SFB, (uint64_t)N * (K / 16))) ||
         overlap(rw, range_of(C, (uint64_t)M * N * 2)))
         return BG_ERR_ALIAS;
-    if ((s = check_device()) != BG_OK) return s;
+    if ((s = check_device(&cus)) != BG_OK) return s;
     const hipStream_t st = (hipStream_t)stream;
-    bg::Fp4Problem p{A, SFA, B, SFB, workspace, M, N, K, chunk, k_splits, 1};
+    bg::Fp4Problem p{A, SFA, B, SFB, workspace, M, N, K, chunk, k_splits, 1, cus};
     hipError_t e = bg::launch_fp4(p, st);
     if (e != hipSuccess) return BG_ERR_LAUNCH;
     return launched(bg::launch_splitk_reduce(workspace, C, M, N, k_splits, st));

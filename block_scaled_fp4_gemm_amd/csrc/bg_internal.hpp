@@ -41,6 +41,7 @@ struct Fp4Problem {
     uint32_t k_chunk;    // K elements per split (multiple of 64, or K)
     uint32_t splits;     // > 1: FP32 planes (batch must be 1)
     uint32_t batch;
+    uint32_t cus;        // compute units of the device (0: 256)
 };
 
 struct W4a16Problem {

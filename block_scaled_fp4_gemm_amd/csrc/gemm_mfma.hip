@@ -1018,7 +1018,9 @@ gemm_mfma_kernel(KParams p) {
 // covers all the rows, so each weight column belongs to one wave) or eight
 // waves of 64 x 64 (WM = 2: the two row halves each dequantize the weight
 // columns they share, so that a second wave per SIMD overlaps one wave's
-// dequantization with the other's MFMAs; the default).
+// dequantization with the other's MFMAs; the default). BN = 128 halves the
+// tile's columns (eight waves of 64 x 32), for split counts that leave CUs
+// idle with 256 columns.
 //
 // The register-staged kernel at these shapes sends about 770 L1-to-L2
 // requests per 64-wide step (32 bytes of packed data and 4 scale bytes from
@@ -1043,10 +1045,10 @@ gemm_mfma_kernel(KParams p) {
 // 16-byte read. The MFMA sums the same products over the step, in its own
 // order, as with the natural order.
 // ---------------------------------------------------------------------------
-template <int EPI, int WM>
+template <int EPI, int WM, int BN = 256>
 __global__ void __launch_bounds__(256 * WM)
 gemm_fp4_dec_kernel(KParams p) {
-    constexpr int BM = 128, BN = 256, WN = 4, NW = WM * WN, NT = 64 * NW;
+    constexpr int BM = 128, WN = 4, NW = WM * WN, NT = 64 * NW;
     constexpr int TM = BM / WM, TN = BN / WN;     // 128 (or 64) x 64 per wave
     constexpr int FM = TM / 32, FN = TN / 32;     // 4 (or 2) x 2 MFMA blocks
     static_assert(WM == 1 || WM == 2, "one or two row halves");
@@ -1095,7 +1097,7 @@ gemm_fp4_dec_kernel(KParams p) {
         // 8 rows (B: 32 segments, A: 16, dealt out evenly), scale segments of
         // 64 rows (B: segment `wave` of waves 0-3; A: segments 0 and 1, from
         // waves 0-1 with four waves, 4-5 with eight)
-        constexpr int SB = 32 / NW, SA = 16 / NW;   // data segments per wave
+        constexpr int SB = BN / 8 / NW, SA = 16 / NW;   // data segments per wave
         const int asw = NW == 8 ? wave - 4 : wave;   // A-scale segment of this wave (0 or 1 loads)
         uint32_t vb[SB], va[SA];
 #pragma unroll
@@ -1135,7 +1137,7 @@ gemm_fp4_dec_kernel(KParams p) {
                 asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(va[j] + kd), "s"(ra), "s"(zero),
                              "{m0}"(l));
             }
-            if (wave < 4) {
+            if (wave < BN / 64) {
                 const uint32_t l = (uint32_t)(uintptr_t)(
                     (__attribute__((address_space(3))) uint8_t*)(lds + SC_B + buf * BN * 16 + wave * 1024));
                 asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(vsb + kss), "s"(rsb), "s"(zero),
@@ -2229,13 +2231,13 @@ int choose_w4a16(int M, int N, int cus) {
 
 // FP4 tile choices (the BG_TUNE_FP4_TILE and BG_TUNE_FP4_SPLITK_TILE
 // overrides force one when `tuned`).
-template <int EPI, int WM = 1>
+template <int EPI, int WM = 1, int BN = 256>
 hipError_t launch_fp4_dec(const KParams& kp, int splits, hipStream_t stream) {
     KParams q = kp;
     q.tiles_m = (kp.M + 127) / 128;
-    q.tiles_n = (kp.N + 255) / 256;
+    q.tiles_n = (kp.N + BN - 1) / BN;
     dim3 grid((unsigned)(q.tiles_m * q.tiles_n), (unsigned)splits, 1u);
-    hipLaunchKernelGGL((gemm_fp4_dec_kernel<EPI, WM>), grid, dim3(256 * WM), 0, stream, q);
+    hipLaunchKernelGGL((gemm_fp4_dec_kernel<EPI, WM, BN>), grid, dim3(256 * WM), 0, stream, q);
     return hipGetLastError();
 }
 
@@ -2252,10 +2254,18 @@ hipError_t launch_fp4_src(const KParams& kp, int M, int splits, int batch, bool 
         // the decode kernel with eight waves for M <= 128 (measured on MI355X,
         // interleaved, against the register-staged 128 x 256 tile: 128 x 7168 x
         // 16384 at k_splits 8 43.8 against 49.5 us, 128 x 4096 x 7168 at 12
-        // 25.6 against 26.7 us; ahead at every k_splits from 4 to 16)
-        if (sk < 0) sk = dec_ok && M <= 128 ? 8 : M <= 192 ? 3 : 2;
+        // 25.6 against 26.7 us; ahead at every k_splits from 4 to 16), with
+        // 128-column tiles when twice as many tiles still fit one round: 128 x
+        // 4096 x 7168 20.7-21.3 us at k_splits 6-8 against 22.8-22.9 us for the
+        // best 256-column split (12-14), 128 x 7168 x 16384 a tie (44.5 at 4
+        // against 44.0 us at 8)
+        if (sk < 0) {
+            const int64_t t128 = (int64_t)((M + 127) / 128) * ((kp.N + 127) / 128) * splits;
+            sk = dec_ok && M <= 128 ? (t128 <= kp.cus ? 9 : 8) : M <= 192 ? 3 : 2;
+        }
         if (dec_ok && sk == 7) return launch_fp4_dec<EPI_STORE_F32>(kp, splits, stream);
         if (dec_ok && sk == 8) return launch_fp4_dec<EPI_STORE_F32, 2>(kp, splits, stream);
+        if (dec_ok && sk == 9) return launch_fp4_dec<EPI_STORE_F32, 2, 128>(kp, splits, stream);
         if constexpr (SRC == SRC_FP4W) {
             switch (sk) {
                 case 0: return launch_cfg<128, 128, 2, 2, EPI_STORE_F32, SRC, 2>(kp, splits, stream);
@@ -2304,6 +2314,7 @@ hipError_t launch_fp4(const Fp4Problem& p, hipStream_t stream) {
     kp.lda = kp.ldb = (int)p.K;
     kp.ldc = (int)p.N;
     kp.k_chunk = (int)p.k_chunk;
+    kp.cus = p.cus > 0 ? (int)p.cus : 256;
     const int splits = (int)p.splits, batch = (int)p.batch;
     if (batch > 1) {
         kp.bs_a = (int64_t)p.M * (p.K / 2);

@@ -426,7 +426,8 @@ const char* bg_status_string(bg_status status);
  *                      decode kernel with four or eight waves, one problem
  *                      with K % 64 == 0)
  *  BG_TUNE_FP4_SPLITK_TILE: tile of gemm_fp4_blockscaled_splitk's planes (7, 8:
- *                      the decode kernel with four or eight waves, K % 64 == 0)
+ *                      the decode kernel with four or eight waves and 256
+ *                      columns, 9: eight waves and 128 columns; K % 64 == 0)
  *  BG_TUNE_W4A16_TILE: tile of gemm_w4a16
  *  BG_TUNE_STREAMK_TILE: tile of gemm_bf16_streamk (23: 128 x 128, 10: 256 x 128;
  *                      other values select 128 x 128)

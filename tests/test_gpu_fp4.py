@@ -211,23 +211,23 @@ def test_gemm_on_imported_scales_equals_plain_scales():
 
 def _decode_sweep_cases():
     """Seeded (M, N, K, k_splits) draws for the decode kernel: M up to 128
-    (one row tile) and a few past it, N around the 256-column tile, K a
+    (one row tile) and a few past it, N around the 128- and 256-column tiles, K a
     multiple of 64 (1 to 40 steps), splits from 1 to 9 (short, partial-group
     and empty splits)."""
     rng = np.random.default_rng(2024)
     cases = []
     for _ in range(24):
         m = int(rng.choice([1, 2, 31, 32, 33, 64, 95, 127, 128, 129, 200]))
-        n = int(rng.choice([1, 16, 63, 200, 255, 256, 257, 511, 700]))
+        n = int(rng.choice([1, 16, 63, 127, 128, 129, 200, 255, 256, 257, 511, 700]))
         k = 64 * int(rng.integers(1, 41))
         ks = int(rng.integers(1, 10))
         cases.append((m, n, k, ks))
     return cases
 
 
-@pytest.mark.parametrize("tile", [7, 8])
+@pytest.mark.parametrize("tile", [7, 8, 9])
 def test_decode_kernel_shape_sweep_bit_exact(tile, force):
-    """The decode kernel (split-K tiles 7 and 8, forced) over 24 seeded shapes,
+    """The decode kernel (split-K tiles 7, 8 and 9, forced) over 24 seeded shapes,
     on power-of-two scales (every product and sum exact in FP32): each output
     bit-identical to the oracle's."""
     force(bg.TUNE_FP4_SPLITK_TILE, tile)
@@ -242,12 +242,12 @@ def test_decode_kernel_shape_sweep_bit_exact(tile, force):
         assert_bits_equal(bits_of(c), want, f"decode sweep tile {tile} {m}x{n}x{k} ks={ks}")
 
 
-@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6, 7, 8, 9])
 def test_every_fp4_splitk_tile(tile, force):
     """Each FP4 split-K tile (the BG_TUNE_FP4_SPLITK_TILE override): planes
     summed in order equal the exact result on power-of-two scales. 7 and 8
-    are the decode kernel with four or eight waves (K % 64 == 0 only: 1040
-    and 1056 fall back); its shapes
+    are the decode kernel with four or eight waves, 9 with eight waves and
+    128 columns (K % 64 == 0 only: 1040 and 1056 fall back); its shapes
     cover splits of 1-4 steps (a partial last ring round), chunks that start
     mid-line (448 / 6 = 128-element chunks of a 448-long K), an empty last
     split and rows past 128."""

@@ -65,7 +65,7 @@ def test_every_scale_byte_and_code_fp4(cfg, force):
     assert_values_equal(bits_of(c), want, "fp4 special codes")
 
 
-@pytest.mark.parametrize("ks,tile", [(2, -1), (4, -1), (4, 0), (2, 1), (4, 7), (3, 7), (3, 8)])
+@pytest.mark.parametrize("ks,tile", [(2, -1), (4, -1), (4, 0), (2, 1), (4, 7), (3, 7), (3, 8), (3, 9)])
 def test_every_scale_byte_and_code_fp4_splitk(ks, tile, force):
     if tile >= 0:
         force(bg.TUNE_FP4_SPLITK_TILE, tile)
